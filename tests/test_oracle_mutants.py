@@ -1,0 +1,116 @@
+"""Planted mistakes in the oracle, on the CPU: each mutant must fail at least one
+of the pins in test_oracle.py, which shows those pins constrain the oracle."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import mita_oracle as mo
+import test_oracle as pins
+
+
+def _patch(monkeypatch, name, fn):
+    monkeypatch.setattr(mo, name, fn)
+    if hasattr(oracle, name):
+        monkeypatch.setattr(oracle, name, fn)
+
+
+def _fails(*tests):
+    for t in tests:
+        try:
+            t()
+        except AssertionError:
+            return True
+    return False
+
+
+def attend_scaled(scale_fn=None, drop_landmarks=False, landmark_values_from_v=False):
+    def attend(Q, K, V, Qt, Vt, I, E, queries=None):
+        Q, K, V, Qt, Vt = (np.asarray(x, np.float64) for x in (Q, K, V, Qt, Vt))
+        N, d = Q.shape
+        qs = range(N) if queries is None else list(queries)
+        O = np.empty((len(qs), d))
+        for row, q in enumerate(qs):
+            keys = ([] if drop_landmarks else [Qt]) + [K[I[e]] for e in E[q]]
+            lv = V[: Qt.shape[0]] if landmark_values_from_v else Vt
+            vals = ([] if drop_landmarks else [lv]) + [V[I[e]] for e in E[q]]
+            Ks, Vs = np.concatenate(keys), np.concatenate(vals)
+            lg = (Ks @ Q[q]) * (scale_fn(d) if scale_fn else 1 / math.sqrt(d))
+            w = np.exp(lg - lg.max())
+            O[row] = (w / w.sum()) @ Vs
+        return O
+    return attend
+
+
+OUTPUT_PINS = (pins.test_hand_worked_example,
+               pins.test_k_equals_n_s_equals_1_is_full_attention_over_landmarks_and_keys,
+               pins.test_k_equals_n_s_equals_m_adds_ln_m_to_key_logits)
+
+
+def test_mutant_wrong_scale(monkeypatch):
+    _patch(monkeypatch, "attend", attend_scaled(scale_fn=lambda d: 1.0 / d))
+    assert _fails(*OUTPUT_PINS)
+
+
+def test_mutant_missing_shared_expert(monkeypatch):
+    _patch(monkeypatch, "attend", attend_scaled(drop_landmarks=True))
+    assert _fails(*OUTPUT_PINS)
+
+
+def test_mutant_landmark_values_not_shared_expert(monkeypatch):
+    _patch(monkeypatch, "attend", attend_scaled(landmark_values_from_v=True))
+    assert _fails(*OUTPUT_PINS)
+
+
+def test_mutant_topk_ties_to_higher_index(monkeypatch):
+    def topk(S, k):
+        order = np.argsort(-S[:, ::-1], axis=1, kind="stable")
+        return np.sort(S.shape[1] - 1 - order[:, :k], axis=1)
+    _patch(monkeypatch, "topk_experts", topk)
+    assert _fails(pins.test_topk_brute_force_with_ties)
+
+
+def test_mutant_topk_smallest_scores(monkeypatch):
+    _patch(monkeypatch, "topk_experts", lambda S, k: np.sort(np.argsort(S, axis=1, kind="stable")[:, :k], axis=1))
+    assert _fails(pins.test_topk_matches_torch_topk_without_ties)
+
+
+def test_mutant_scores_from_values(monkeypatch):
+    orig_forward = mo.forward
+
+    def forward(Q, K, V, *a, **kw):
+        return orig_forward(Q, V, V, *a, **kw)   # transposed role: V used as keys
+    monkeypatch.setattr(oracle, "forward", forward)
+    assert _fails(pins.test_hand_worked_example, pins.test_single_landmark_is_mean_query,
+                  pins.test_k_equals_n_s_equals_1_is_full_attention_over_landmarks_and_keys)
+
+
+def test_mutant_pool_floor_windows(monkeypatch):
+    _patch(monkeypatch, "adaptive_windows", lambda L, M: [((i * L) // M, ((i + 1) * L) // M) for i in range(M)])
+    assert _fails(lambda: pins.test_pool_matches_torch_adaptive_avg_pool1d(100, 7),
+                  pins.test_pool_windows_overlap_when_not_divisible)
+
+
+def test_mutant_pool_column_major_landmarks(monkeypatch):
+    orig = mo.pool
+
+    def pool(Q, gh, gw, ph, pw):
+        out = orig(Q, gh, gw, ph, pw)
+        return out.reshape(ph, pw, -1).transpose(1, 0, 2).reshape(ph * pw, -1)
+    _patch(monkeypatch, "pool", pool)
+    assert _fails(lambda: pins.test_pool_matches_torch_adaptive_avg_pool2d(9, 13, 4, 5))
+
+
+def test_mutant_route_ascending(monkeypatch):
+    _patch(monkeypatch, "route", lambda Q, Qt, s, R=None: np.argsort(mo.route_scores(Q, Qt), axis=1, kind="stable")[:, :s])
+    assert _fails(pins.test_route_brute_force_and_order, pins.test_hand_worked_example)
+
+
+def test_mutant_shared_expert_unscaled(monkeypatch):
+    def shared_expert(Qt, K, V):
+        S = mo.scores(Qt, K)
+        W = np.exp(S - S.max(axis=1, keepdims=True))
+        return (W / W.sum(axis=1, keepdims=True)) @ V
+    _patch(monkeypatch, "shared_expert", shared_expert)
+    assert _fails(lambda: pins.test_shared_expert_matches_torch_sdpa(16, 1024, 64))

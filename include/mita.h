@@ -1,0 +1,124 @@
+/* MiTA (Mixture of Top-k Activations) attention forward pass on one AMD Instinct
+ * MI355X (gfx950): C ABI.
+ *
+ * The operation is the one described on the three gist.science summaries of
+ * "MiTA Attention: Efficient Fast-Weight Scaling via a Mixture of Top-k
+ * Activations" (Arabic, Dutch and Hindi pages). Per (batch, head) slice, with
+ * Q, K, V of shape [N, d] and no mask:
+ *   1. landmark queries Q~ [m, d]: adaptive average pooling of Q
+ *      (Arabic/Hindi section 2, "mechanism details"; Dutch "Kernconcepten" 1);
+ *   2. shared expert V~ = softmax(Q~ K^T / sqrt d) V, Q~ also being its keys
+ *      (Arabic/Hindi section 2; Dutch "Kernconcepten" 2, "Wiskundige Formulering");
+ *   3. deformable experts I_i = the k tokens n with the largest q~_i . K_n
+ *      (Arabic/Hindi section 2; Dutch "Kernconcepten" 3);
+ *   4. routing: query q goes to the s landmarks with the largest q . q~_i
+ *      (the pages leave the rule open; this dot-product top-s is the reading taken);
+ *   5. output: softmax(q K*^T / sqrt d) V* with K* = [Q~, K_{I_e1}, .., K_{I_es}],
+ *      V* = [V~, V_{I_e1}, .., V_{I_es}] (Dutch "Wiskundige Formulering").
+ *      A token present in two of a query's experts is counted twice.
+ * Ties in steps 3 and 4 go to the lower index.
+ *
+ * Conventions for every entry point
+ *   - Tensors are device pointers, row-major and contiguous: Q, K, V and out are
+ *     [B, H, N, d] with d fastest, all of the dtype named in the shape (bf16 as
+ *     raw 16-bit patterns, or fp32). The caller allocates and owns every buffer;
+ *     the library keeps no pointer after a call returns and allocates nothing.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *     asynchronously; the call returns without synchronising. Device faults show
+ *     up at the caller's next synchronisation.
+ *   - Arguments are checked before anything is enqueued. A failed check returns
+ *     a negative status and enqueues nothing; mita_last_error() then describes it.
+ *     No C++ exception crosses this interface.
+ *   - Calls that share a workspace must not overlap in time.
+ */
+#ifndef MITA_H
+#define MITA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MITA_OK = 0,
+  MITA_ERR_INVALID_ARG = -1, /* a size, pointer or shape field is out of range   */
+  MITA_ERR_UNSUPPORTED = -2, /* valid request this build does not implement      */
+  MITA_ERR_WORKSPACE = -3,   /* workspace missing, misaligned or too small      */
+  MITA_ERR_HIP = -4          /* a HIP runtime call failed; see mita_last_error() */
+} mita_status;
+
+typedef enum { MITA_F32 = 0, MITA_BF16 = 1 } mita_dtype;
+
+/* Problem shape. Tokens lie on a row-major grid_h x grid_w grid (grid_h = 1 for a
+ * 1D sequence) and are pooled separably to a row-major pool_h x pool_w grid of
+ * landmarks, so m = pool_h * pool_w. Pooling window i of an axis of length L
+ * pooled to M cells is [floor(i L / M), ceil((i + 1) L / M)).
+ * Supported: d in {64, 128}; 1 <= pool_h <= grid_h; 1 <= pool_w <= grid_w;
+ * grid_h * grid_w = N; m <= 4096; B * H * N * max(d, s) < 2^31. */
+typedef struct {
+  int32_t B, H, N, d;
+  int32_t grid_h, grid_w;
+  int32_t pool_h, pool_w;
+  int32_t dtype; /* mita_dtype */
+} mita_shape;
+
+/* Bytes of device workspace that mita_forward and the step entry points need for
+ * this shape and (m, k, s); 0 if the arguments are invalid. The workspace holds
+ * every intermediate (landmarks, the m x N score rows, expert sets, routing,
+ * buckets and partial outputs) and must be 256-byte aligned. */
+size_t mita_workspace_bytes(const mita_shape* shape, int m, int k, int s);
+
+/* Whole forward pass, steps 1-5: out = MiTA(Q, K, V) with m landmarks, experts of
+ * k tokens and s routed experts per query. Requires 1 <= m <= N, 1 <= k <= N,
+ * 1 <= s <= m. `out` has the input dtype ([B, H, N, d]); bf16 results are
+ * rounded to nearest even. Equivalent to calling mita_pool, mita_landmark,
+ * mita_topk, mita_route and mita_gather in that order on the same workspace. */
+mita_status mita_forward(const void* Q, const void* K, const void* V, int m, int k, int s, void* out,
+                         const mita_shape* shape, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Step entry points, for per-step checks and timing. They run the steps of
+ * mita_forward one at a time: each reads what the earlier steps left in the
+ * workspace, so they must be called in this order with the same shape, (m, k, s)
+ * and workspace. Each may also copy its result out for inspection; every
+ * `*_out` pointer may be NULL. */
+
+/* Step 1 (pooling). Qt_out: fp64 [B, H, m, d], the landmark queries. */
+mita_status mita_pool(const void* Q, int m, int k, int s, const mita_shape* shape, void* workspace,
+                      size_t workspace_bytes, double* Qt_out, void* stream);
+
+/* Step 2 (shared expert and score rows). Vt_out: fp32 [B, H, m, d], the shared
+ * expert V~. S_out: fp32 [B, H, m, N], the unscaled scores q~_i . K_n as computed
+ * on the GPU (fp32 accumulation, used to rank tokens before exact refinement). */
+mita_status mita_landmark(const void* K, const void* V, int m, int k, int s, const mita_shape* shape,
+                          void* workspace, size_t workspace_bytes, float* Vt_out, float* S_out, void* stream);
+
+/* Step 3 (deformable experts). I_out: int32 [B, H, m, k], each row the k token
+ * ids of expert i in ascending order. Selection is exact: candidates whose fp32
+ * score lies within a proven error bound of the k-th largest are re-scored in
+ * fp64 before the cut. */
+mita_status mita_topk(const void* K, int m, int k, int s, const mita_shape* shape, void* workspace,
+                      size_t workspace_bytes, int32_t* I_out, void* stream);
+
+/* Step 4 (routing). E_out: int32 [B, H, N, s], the routed landmarks of each
+ * query, ordered by decreasing score. The set is exact in the same sense as
+ * step 3; the order among the s entries follows the fp32 scores. */
+mita_status mita_route(const void* Q, int m, int k, int s, const mita_shape* shape, void* workspace,
+                       size_t workspace_bytes, int32_t* E_out, void* stream);
+
+/* Step 5 (output): buckets the (query, expert) pairs by expert, runs attention of
+ * each bucket over its expert's gathered keys and the shared expert, and merges
+ * the s + 1 partial softmaxes of each query into out. */
+mita_status mita_gather(const void* Q, const void* K, const void* V, int m, int k, int s, void* out,
+                        const mita_shape* shape, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Short description of a status code (static storage). */
+const char* mita_status_string(int status);
+/* Message of the last failed call on this thread ("" if none). */
+const char* mita_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MITA_H */

@@ -1,0 +1,179 @@
+// Wave-level pieces of flash-style attention on gfx950 MFMA, shared by the
+// shared-expert, gather and combine kernels.
+//
+// A workgroup is 4 waves; each wave owns 16 queries. Keys arrive in blocks of
+// 64 staged in LDS. Scores are computed transposed, S^T = K Q^T, with the
+// 16x16 MFMA tiles, so lane l holds the scores of query l%16 against keys
+// 4*(l/16) + j (+16 per tile). Those four consecutive keys are exactly what the
+// lane must feed as the B operand of the P.V product when V^T is the A operand,
+// so the probabilities never leave registers: bf16 needs V^T in LDS (written
+// transposed while staging), fp32 reads V rows directly.
+#pragma once
+#include "common.h"
+#include "plan.h"
+
+namespace mita {
+
+template <typename T, int D>
+struct Tiles {
+  static constexpr bool BF = sizeof(T) == 2;
+  static constexpr int KSTR = D + (BF ? 8 : 4);                 // key tile row stride (elements)
+  static constexpr int VSTR = BF ? (kKeyBlock + 8) : (D + 4);   // bf16: V^T rows of 64 keys; fp32: V rows
+  static constexpr int KTILE = kKeyBlock * KSTR;                // elements per key tile
+  static constexpr int VTILE = BF ? D * VSTR : kKeyBlock * VSTR;
+  static constexpr int EPC = 16 / sizeof(T);                    // elements per 16-byte chunk
+};
+
+// Copy 64 rows into a key tile: row r comes from rowptr(r) (D contiguous
+// elements, 16-byte aligned); rows r >= nvalid are zero.
+template <typename T, int D, typename RowFn>
+__device__ __forceinline__ void stage_rows(T* dst, int stride, RowFn rowptr, int nvalid, int tid) {
+  constexpr int EPC = Tiles<T, D>::EPC, CPR = D / EPC, TOTAL = kKeyBlock * CPR;
+#pragma unroll
+  for (int c = tid; c < TOTAL; c += 256) {
+    const int r = c / CPR, cc = (c % CPR) * EPC;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < nvalid) v = *(const uint4*)(rowptr(r) + cc);
+    *(uint4*)(dst + r * stride + cc) = v;
+  }
+}
+
+// Copy 64 bf16 rows into V^T [D][64 + pad]; rows r >= nvalid are zero.
+template <int D, typename RowFn>
+__device__ __forceinline__ void stage_vt_bf16(uint16_t* Vt, RowFn rowptr, int nvalid, int tid) {
+  constexpr int VSTR = Tiles<uint16_t, D>::VSTR, CPR = D / 8, TOTAL = (kKeyBlock / 4) * CPR;
+#pragma unroll
+  for (int c = tid; c < TOTAL; c += 256) {
+    const int kg = c / CPR, cc = (c % CPR) * 8;
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = kg * 4 + u;
+      v[u] = r < nvalid ? *(const uint4*)(rowptr(r) + cc) : make_uint4(0, 0, 0, 0);
+    }
+    const uint32_t* w0 = (const uint32_t*)&v[0];
+    const uint32_t* w1 = (const uint32_t*)&v[1];
+    const uint32_t* w2 = (const uint32_t*)&v[2];
+    const uint32_t* w3 = (const uint32_t*)&v[3];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int sh = (e & 1) * 16, q = e >> 1;
+      uint2 out;
+      out.x = ((w0[q] >> sh) & 0xFFFFu) | (((w1[q] >> sh) & 0xFFFFu) << 16);
+      out.y = ((w2[q] >> sh) & 0xFFFFu) | (((w3[q] >> sh) & 0xFFFFu) << 16);
+      *(uint2*)(Vt + (cc + e) * VSTR + kg * 4) = out;
+    }
+  }
+}
+
+// S^T block (64 keys x 16 queries) for bf16. Query side: QP parts in registers
+// (qf[p][ks] is lane's 8 elements 32*ks + 8*(lane/16) of query lane%16). Key
+// side: one tile, or two (hi, lo) when KP == 2.
+template <int D, int KP, int QP>
+__device__ __forceinline__ void qk_bf16(const uint16_t* Ks0, const uint16_t* Ks1, const uint4 (&qf)[QP][D / 32],
+                                        f32x4 (&acc)[4], int lane) {
+  constexpr int KSTR = Tiles<uint16_t, D>::KSTR;
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int off = (16 * kt + r) * KSTR + 32 * ks + 8 * g;
+      const uint4 a0 = *(const uint4*)(Ks0 + off);
+#pragma unroll
+      for (int p = 0; p < QP; ++p) acc[kt] = mma_bf16(a0, qf[p][ks], acc[kt]);
+      if constexpr (KP == 2) {
+        const uint4 a1 = *(const uint4*)(Ks1 + off);
+        acc[kt] = mma_bf16(a1, qf[0][ks], acc[kt]);
+      }
+    }
+  }
+}
+
+// S^T block for fp32 (qf[ks] is element 4*ks + lane/16 of query lane%16).
+template <int D>
+__device__ __forceinline__ void qk_f32(const float* Ks, const float (&qf)[D / 4], f32x4 (&acc)[4], int lane) {
+  constexpr int KSTR = Tiles<float, D>::KSTR;
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < D / 4; ++ks) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) acc[kt] = mma_f32(Ks[(16 * kt + r) * KSTR + 4 * ks + g], qf[ks], acc[kt]);
+  }
+}
+
+// Online softmax over one block. x holds log2-domain logits (masked keys are
+// -inf; every block has at least one live key). On return x holds the
+// unnormalised probabilities, and the returned factor rescales earlier sums.
+__device__ __forceinline__ float online_softmax(f32x4 (&x)[4], float& mrun, float& lrun) {
+  float bm = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bm = fmaxf(bm, x[kt][j]);
+  bm = quad_max(bm);
+  const float mnew = fmaxf(mrun, bm);
+  const float alpha = exp2f(mrun - mnew);
+  float sum = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float p = exp2f(x[kt][j] - mnew);
+      x[kt][j] = p;
+      sum += p;
+    }
+  lrun = lrun * alpha + sum;
+  mrun = mnew;
+  return alpha;
+}
+
+template <int D>
+__device__ __forceinline__ void rescale(f32x4 (&o)[D / 16], float alpha) {
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[dt][j] *= alpha;
+}
+
+// O^T += V^T P^T for bf16: o[dt] holds O^T[16*dt + 4*(lane/16) + j][lane%16].
+template <int D>
+__device__ __forceinline__ void pv_bf16(const uint16_t* Vt, const f32x4 (&p)[4], f32x4 (&o)[D / 16], int lane) {
+  constexpr int VSTR = Tiles<uint16_t, D>::VSTR;
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint4 b;
+    b.x = pack_bf16x2(p[2 * h][0], p[2 * h][1]);
+    b.y = pack_bf16x2(p[2 * h][2], p[2 * h][3]);
+    b.z = pack_bf16x2(p[2 * h + 1][0], p[2 * h + 1][1]);
+    b.w = pack_bf16x2(p[2 * h + 1][2], p[2 * h + 1][3]);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const uint16_t* row = Vt + (16 * dt + r) * VSTR + 32 * h + 4 * g;
+      const uint2 lo = *(const uint2*)row, hi = *(const uint2*)(row + 16);
+      o[dt] = mma_bf16(make_uint4(lo.x, lo.y, hi.x, hi.y), b, o[dt]);
+    }
+  }
+}
+
+// Same for fp32, V rows read directly from the row-major V tile.
+template <int D>
+__device__ __forceinline__ void pv_f32(const float* Vs, const f32x4 (&p)[4], f32x4 (&o)[D / 16], int lane) {
+  constexpr int VSTR = Tiles<float, D>::VSTR;
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float* row = Vs + (16 * kt + 4 * g + j) * VSTR + r;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) o[dt] = mma_f32(row[16 * dt], p[kt][j], o[dt]);
+    }
+}
+
+}  // namespace mita

@@ -1,0 +1,117 @@
+// Device helpers shared by the gfx950 kernels of the MiTA forward pass.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mita {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVE = 64;
+
+// ---------------------------------------------------------------- bf16 bits
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float -> bf16 bits, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// double -> bf16 bits, round to nearest even, without a detour through float
+// (a double rounding could move the value by more than half a bf16 ulp).
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+  // Round the double to 8 significant bits: split with a power-of-two shifter.
+  if (x == 0.0) return (uint16_t)(__double_as_longlong(x) >> 48);
+  int e;
+  frexp(x, &e);                       // |x| in [2^(e-1), 2^e)
+  double sh = ldexp(1.0, e - 8 + 52); // adding and removing sh keeps 8 significant bits (RNE)
+  double r = (x > 0) ? ((x + sh) - sh) : ((x - sh) + sh);
+  float f = (float)r;                 // exact: r has 8 significant bits
+  return (uint16_t)(__float_as_uint(f) >> 16);
+}
+
+// ---------------------------------------------------------------- order keys
+// Monotone map of float32 onto uint32: a < b (as floats) iff key(a) < key(b).
+__device__ __forceinline__ uint32_t f32_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_f32(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+// Same map for float64 onto uint64.
+__device__ __forceinline__ uint64_t f64_key(double x) {
+  uint64_t u = (uint64_t)__double_as_longlong(x);
+  return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// ---------------------------------------------------------------- wave reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+// Reduce over the four lanes l, l^16, l^32, l^48 (one column of an MFMA 16x16 tile).
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16, WAVE));
+  return fmaxf(v, __shfl_xor(v, 32, WAVE));
+}
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __shfl_xor(v, 16, WAVE);
+  return v + __shfl_xor(v, 32, WAVE);
+}
+
+// Inclusive prefix sum over the 256 threads of a block, in thread order.
+__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wtot, uint32_t& total) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = __shfl_up(v, o, WAVE);
+    if (lane >= o) v += t;
+  }
+  if (lane == 63) wtot[w] = v;
+  __syncthreads();
+  uint32_t off = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) off += (i < w) ? wtot[i] : 0u;
+  total = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+  __syncthreads();
+  return v + off;
+}
+
+// ---------------------------------------------------------------- MFMA wrappers
+// 16x16 output tiles: lane l holds C[4*(l/16) + j][l%16], j = 0..3.
+// bf16, K = 32: lane l supplies A[l%16][8*(l/16) .. +8] and B[8*(l/16) .. +8][l%16].
+__device__ __forceinline__ f32x4 mma_bf16(const uint4& a, const uint4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+// f32, K = 4: lane l supplies A[l%16][l/16] and B[l/16][l%16].
+__device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+}  // namespace mita

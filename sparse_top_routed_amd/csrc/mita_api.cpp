@@ -1,0 +1,257 @@
+// C ABI of the MiTA forward pass: argument checks, workspace carving and the
+// launch sequence of the five steps on one HIP stream.
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "plan.h"
+
+namespace mita {
+
+static thread_local char g_last_error[512] = "";
+
+static void set_error(const char* msg) {
+  snprintf(g_last_error, sizeof g_last_error, "%s", msg ? msg : "");
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+mita_status make_plan(const mita_shape* shape, int m, int k, int s, Plan* p, const char** err) {
+  *err = "";
+  if (!shape) { *err = "shape is NULL"; return MITA_ERR_INVALID_ARG; }
+  const mita_shape& sh = *shape;
+  if (sh.B < 1 || sh.H < 1 || sh.N < 1 || sh.d < 1) { *err = "B, H, N and d must be >= 1"; return MITA_ERR_INVALID_ARG; }
+  if (sh.dtype != MITA_F32 && sh.dtype != MITA_BF16) { *err = "dtype must be MITA_F32 or MITA_BF16"; return MITA_ERR_INVALID_ARG; }
+  if (sh.grid_h < 1 || sh.grid_w < 1 || (int64_t)sh.grid_h * sh.grid_w != sh.N) {
+    *err = "grid_h * grid_w must equal N"; return MITA_ERR_INVALID_ARG;
+  }
+  if (sh.pool_h < 1 || sh.pool_w < 1 || sh.pool_h > sh.grid_h || sh.pool_w > sh.grid_w) {
+    *err = "need 1 <= pool_h <= grid_h and 1 <= pool_w <= grid_w"; return MITA_ERR_INVALID_ARG;
+  }
+  if ((int64_t)sh.pool_h * sh.pool_w != m) { *err = "pool_h * pool_w must equal m"; return MITA_ERR_INVALID_ARG; }
+  if (m < 1 || m > sh.N) { *err = "need 1 <= m <= N"; return MITA_ERR_INVALID_ARG; }
+  if (k < 1 || k > sh.N) { *err = "need 1 <= k <= N"; return MITA_ERR_INVALID_ARG; }
+  if (s < 1 || s > m) { *err = "need 1 <= s <= m"; return MITA_ERR_INVALID_ARG; }
+  if (sh.d != 64 && sh.d != 128) { *err = "d must be 64 or 128"; return MITA_ERR_UNSUPPORTED; }
+  if (m > kMaxLandmarks) { *err = "m above 4096 is not supported"; return MITA_ERR_UNSUPPORTED; }
+  const int64_t BH = (int64_t)sh.B * sh.H;
+  const int64_t lim = (int64_t)1 << 31;
+  if (BH * sh.N * std::max(sh.d, s) >= lim || BH * m * (int64_t)std::max(k, sh.d) >= lim) {
+    *err = "tensor too large for 32-bit element indexing"; return MITA_ERR_UNSUPPORTED;
+  }
+
+  Plan& P = *p;
+  P.B = sh.B; P.H = sh.H; P.N = sh.N; P.d = sh.d; P.m = m; P.k = k; P.s = s;
+  P.grid_h = sh.grid_h; P.grid_w = sh.grid_w; P.pool_h = sh.pool_h; P.pool_w = sh.pool_w;
+  P.dtype = sh.dtype;
+  P.esize = sh.dtype == MITA_BF16 ? 2 : 4;
+  P.BH = (int)BH;
+
+  // Shared-expert kernel: enough key chunks that the grid holds ~2048 workgroups.
+  P.lm_tiles = (m + kLandmarkTile - 1) / kLandmarkTile;
+  const int64_t base = BH * P.lm_tiles;
+  int64_t want = std::max<int64_t>(1, (2048 + base - 1) / base);
+  int64_t chunk = (sh.N + want - 1) / want;
+  chunk = std::max<int64_t>(chunk, 4 * kKeyBlock);
+  chunk = (chunk + kKeyBlock - 1) / kKeyBlock * kKeyBlock;
+  P.lchunk = (int)chunk;
+  P.nsplit = (int)((sh.N + chunk - 1) / chunk);
+
+  // Top-k select: segments of at most kTopkSegMax scores, multiples of 1024.
+  P.G = (sh.N + kTopkSegMax - 1) / kTopkSegMax;
+  int seg = (sh.N + P.G - 1) / P.G;
+  P.seg = (seg + 1023) / 1024 * 1024;
+  P.G = (sh.N + P.seg - 1) / P.seg;
+
+  P.qtiles = (sh.N + kQueryTile - 1) / kQueryTile;
+  P.max_tiles = (int)(((int64_t)sh.N * s + kQueryTile - 1) / kQueryTile + m);
+
+  // Error bound of an approximate score relative to |q~|_2 |k|_2 (a factor 2 of slack):
+  // bf16: Q~ split in two bf16 parts (representation error 2^-16) and 2d products
+  // accumulated in fp32; fp32: Q~ rounded to fp32 and d products accumulated in fp32.
+  const double u = 1.0 / (1 << 23);
+  if (sh.dtype == MITA_BF16)
+    P.gamma_qk = 2.0 * (1.0 / 65536.0 + 1.02 * (2.0 * sh.d + 4.0) * u);
+  else
+    P.gamma_qk = 2.0 * (u + 1.02 * (sh.d + 4.0) * u);
+
+  // Workspace carving.
+  Layout& L = P.ws;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+  const size_t bh = (size_t)BH, N = sh.N, d = sh.d;
+  L.qt64 = take(bh * m * d * 8);
+  L.qtop = take(bh * m * d * 4);
+  L.qtnorm = take(bh * m * 4);
+  L.lpart = take(bh * m * P.nsplit * (d + 2) * 4);
+  L.kmax = take(bh * P.nsplit * 4);
+  L.vt32 = take(bh * m * d * 4);
+  L.vt16 = take(bh * m * d * 2);
+  L.S = take(bh * m * N * 4);
+  L.cand_key = take(bh * m * N * 4);
+  L.cand_idx = take(bh * m * N * 4);
+  L.cand_cnt = take(bh * m * P.G * 4);
+  L.I = take(bh * m * (size_t)k * 4);
+  L.E = take(bh * N * s * 4);
+  // counters: everything from here to `perm` is cleared before routing
+  L.counters = take(256);
+  L.bcount = take(bh * m * 4);
+  L.bcursor = take(bh * m * 4);
+  L.counters_bytes = off - L.counters;
+  L.rflag = take(bh * N * 4);
+  L.boff = take(bh * (m + 1) * 4);
+  L.toff = take(bh * (m + 1) * 4);
+  L.perm = take(bh * N * s * 4);
+  if (s > 1) {
+    L.pacc = take(bh * N * s * d * 4);
+    L.pml = take(bh * N * s * 2 * 4);
+  } else {
+    L.pacc = L.pml = 0;
+  }
+  L.total = off;
+  return MITA_OK;
+}
+
+}  // namespace mita
+
+using namespace mita;
+
+namespace {
+
+mita_status check_common(const mita_shape* shape, int m, int k, int s, void* ws, size_t ws_bytes, Plan* P) {
+  const char* err = "";
+  mita_status st = make_plan(shape, m, k, s, P, &err);
+  if (st != MITA_OK) { set_error(err); return st; }
+  if (!ws) { set_error("workspace is NULL"); return MITA_ERR_WORKSPACE; }
+  if (((uintptr_t)ws & 255) != 0) { set_error("workspace must be 256-byte aligned"); return MITA_ERR_WORKSPACE; }
+  if (ws_bytes < P->ws.total) { set_error("workspace smaller than mita_workspace_bytes()"); return MITA_ERR_WORKSPACE; }
+  return MITA_OK;
+}
+
+mita_status check_ptr(const void* p, const char* name) {
+  static thread_local char buf[128];
+  if (!p) { snprintf(buf, sizeof buf, "%s is NULL", name); set_error(buf); return MITA_ERR_INVALID_ARG; }
+  if (((uintptr_t)p & 15) != 0) { snprintf(buf, sizeof buf, "%s must be 16-byte aligned", name); set_error(buf); return MITA_ERR_INVALID_ARG; }
+  return MITA_OK;
+}
+
+mita_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return MITA_OK;
+  char buf[400];
+  snprintf(buf, sizeof buf, "%s: %s", where, hipGetErrorString(e));
+  set_error(buf);
+  return MITA_ERR_HIP;
+}
+
+mita_status copy_out(void* dst, const void* src, size_t bytes, hipStream_t st, const char* what) {
+  if (!dst) return MITA_OK;
+  if (((uintptr_t)dst & 7) != 0) { set_error("output pointer must be 8-byte aligned"); return MITA_ERR_INVALID_ARG; }
+  return hip_status(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st), what);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mita_workspace_bytes(const mita_shape* shape, int m, int k, int s) {
+  Plan P;
+  const char* err;
+  if (make_plan(shape, m, k, s, &P, &err) != MITA_OK) { set_error(err); return 0; }
+  return P.ws.total;
+}
+
+const char* mita_status_string(int status) {
+  switch (status) {
+    case MITA_OK: return "MITA_OK";
+    case MITA_ERR_INVALID_ARG: return "MITA_ERR_INVALID_ARG: invalid argument";
+    case MITA_ERR_UNSUPPORTED: return "MITA_ERR_UNSUPPORTED: not supported by this build";
+    case MITA_ERR_WORKSPACE: return "MITA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case MITA_ERR_HIP: return "MITA_ERR_HIP: HIP runtime error";
+    default: return "unknown mita_status";
+  }
+}
+
+const char* mita_last_error(void) { return g_last_error; }
+
+mita_status mita_pool(const void* Q, int m, int k, int s, const mita_shape* shape, void* workspace,
+                      size_t workspace_bytes, double* Qt_out, void* stream) {
+  Plan P;
+  mita_status st = check_common(shape, m, k, s, workspace, workspace_bytes, &P);
+  if (st != MITA_OK) return st;
+  if ((st = check_ptr(Q, "Q")) != MITA_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  if ((st = hip_status(launch_pool(P, Q, ws, hs), "pool")) != MITA_OK) return st;
+  return copy_out(Qt_out, ws + P.ws.qt64, (size_t)P.BH * m * P.d * 8, hs, "pool copy-out");
+}
+
+mita_status mita_landmark(const void* K, const void* V, int m, int k, int s, const mita_shape* shape,
+                          void* workspace, size_t workspace_bytes, float* Vt_out, float* S_out, void* stream) {
+  Plan P;
+  mita_status st = check_common(shape, m, k, s, workspace, workspace_bytes, &P);
+  if (st != MITA_OK) return st;
+  if ((st = check_ptr(K, "K")) != MITA_OK || (st = check_ptr(V, "V")) != MITA_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  if ((st = hip_status(launch_landmark(P, K, V, ws, hs), "landmark")) != MITA_OK) return st;
+  if ((st = copy_out(Vt_out, ws + P.ws.vt32, (size_t)P.BH * m * P.d * 4, hs, "landmark copy-out")) != MITA_OK) return st;
+  return copy_out(S_out, ws + P.ws.S, (size_t)P.BH * m * P.N * 4, hs, "score copy-out");
+}
+
+mita_status mita_topk(const void* K, int m, int k, int s, const mita_shape* shape, void* workspace,
+                      size_t workspace_bytes, int32_t* I_out, void* stream) {
+  Plan P;
+  mita_status st = check_common(shape, m, k, s, workspace, workspace_bytes, &P);
+  if (st != MITA_OK) return st;
+  if ((st = check_ptr(K, "K")) != MITA_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  if ((st = hip_status(launch_topk(P, K, ws, hs), "topk")) != MITA_OK) return st;
+  return copy_out(I_out, ws + P.ws.I, (size_t)P.BH * m * k * 4, hs, "topk copy-out");
+}
+
+mita_status mita_route(const void* Q, int m, int k, int s, const mita_shape* shape, void* workspace,
+                       size_t workspace_bytes, int32_t* E_out, void* stream) {
+  Plan P;
+  mita_status st = check_common(shape, m, k, s, workspace, workspace_bytes, &P);
+  if (st != MITA_OK) return st;
+  if ((st = check_ptr(Q, "Q")) != MITA_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  if ((st = hip_status(launch_clear(P, ws, hs), "clear")) != MITA_OK) return st;
+  if ((st = hip_status(launch_route(P, Q, ws, hs), "route")) != MITA_OK) return st;
+  return copy_out(E_out, ws + P.ws.E, (size_t)P.BH * P.N * s * 4, hs, "route copy-out");
+}
+
+mita_status mita_gather(const void* Q, const void* K, const void* V, int m, int k, int s, void* out,
+                        const mita_shape* shape, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan P;
+  mita_status st = check_common(shape, m, k, s, workspace, workspace_bytes, &P);
+  if (st != MITA_OK) return st;
+  if ((st = check_ptr(Q, "Q")) != MITA_OK || (st = check_ptr(K, "K")) != MITA_OK ||
+      (st = check_ptr(V, "V")) != MITA_OK || (st = check_ptr(out, "out")) != MITA_OK)
+    return st;
+  return hip_status(launch_gather(P, Q, K, V, out, (char*)workspace, (hipStream_t)stream), "gather");
+}
+
+mita_status mita_forward(const void* Q, const void* K, const void* V, int m, int k, int s, void* out,
+                         const mita_shape* shape, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan P;
+  mita_status st = check_common(shape, m, k, s, workspace, workspace_bytes, &P);
+  if (st != MITA_OK) return st;
+  if ((st = check_ptr(Q, "Q")) != MITA_OK || (st = check_ptr(K, "K")) != MITA_OK ||
+      (st = check_ptr(V, "V")) != MITA_OK || (st = check_ptr(out, "out")) != MITA_OK)
+    return st;
+  hipStream_t hs = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  if ((st = hip_status(launch_pool(P, Q, ws, hs), "pool")) != MITA_OK) return st;
+  if ((st = hip_status(launch_landmark(P, K, V, ws, hs), "landmark")) != MITA_OK) return st;
+  if ((st = hip_status(launch_topk(P, K, ws, hs), "topk")) != MITA_OK) return st;
+  if ((st = hip_status(launch_clear(P, ws, hs), "clear")) != MITA_OK) return st;
+  if ((st = hip_status(launch_route(P, Q, ws, hs), "route")) != MITA_OK) return st;
+  return hip_status(launch_gather(P, Q, K, V, out, ws, hs), "gather");
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// Host-side plan of one MiTA forward call: validated sizes, launch shapes and the
+// carving of the caller's workspace into the intermediates of the five steps.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/mita.h"
+
+namespace mita {
+
+constexpr int kMaxLandmarks = 4096;
+constexpr int kLandmarkTile = 64;     // landmarks per workgroup in the shared-expert kernel
+constexpr int kKeyBlock = 64;         // keys per LDS block in the attention kernels
+constexpr int kQueryTile = 64;        // queries per workgroup in the router, gather and combine kernels
+constexpr int kTopkSegMax = 8192;     // scores per workgroup in the segment select kernel
+constexpr int kRouteFastMaxS = 6;     // the router keeps per-lane top lists up to this s
+
+// Workspace offsets (bytes) of every intermediate buffer.
+struct Layout {
+  size_t qt64;      // f64 [BH, m, d]     landmark queries
+  size_t qtop;      // bf16 [BH, 2, m, d] hi/lo split of Q~ (bf16 path) or f32 [BH, m, d]
+  size_t qtnorm;    // f32 [BH, m]        upper bound of |q~_i|_2
+  size_t lpart;     // f32 [BH, m, nsplit, d + 2]  per-chunk (max, sum, acc) of the shared expert
+  size_t kmax;      // f32 [BH, nsplit]   upper bound of max_n |K_n|_2 per key chunk
+  size_t vt32;      // f32 [BH, m, d]     shared expert V~
+  size_t vt16;      // bf16 [BH, m, d]    V~ rounded to bf16 (MFMA operand)
+  size_t S;         // f32 [BH, m, N]     approximate scores q~_i . K_n
+  size_t cand_key;  // u32 [BH * m, N]    per-segment candidates of the top-k select (order keys)
+  size_t cand_idx;  // u32 [BH * m, N]    ... and their token ids
+  size_t cand_cnt;  // u32 [BH * m, G]    candidates per segment
+  size_t I;         // i32 [BH, m, k]     expert token sets, ascending
+  size_t E;         // i32 [BH, N, s]     routed experts per query
+  size_t counters;  // u32 block cleared at the start of routing (below)
+  size_t rflag;     // u32 [BH * N]       queries whose routing needs the exact fp64 pass
+  size_t bcount;    // u32 [BH, m]        queries routed to each expert
+  size_t bcursor;   // u32 [BH, m]        scatter cursors
+  size_t boff;      // u32 [BH, m + 1]    bucket offsets
+  size_t toff;      // u32 [BH, m + 1]    tile offsets (query tiles of kQueryTile per bucket)
+  size_t perm;      // i32 [BH, N * s]    (query * s + slot) grouped by expert
+  size_t pacc;      // f32 [BH, N, s, d]  per-slot partial outputs (s > 1)
+  size_t pml;       // f32 [BH, N, s, 2]  per-slot (max, sum)
+  size_t total;
+  size_t counters_bytes;
+};
+
+struct Plan {
+  int B, H, N, d, m, k, s;
+  int grid_h, grid_w, pool_h, pool_w;
+  int dtype;        // mita_dtype
+  int esize;        // bytes per input element
+  int BH;
+  // shared-expert kernel
+  int lm_tiles;     // ceil(m / kLandmarkTile)
+  int lchunk;       // keys per workgroup (multiple of kKeyBlock)
+  int nsplit;       // ceil(N / lchunk)
+  // top-k select
+  int seg;          // scores per segment workgroup
+  int G;            // segments per row
+  // router and output
+  int qtiles;       // ceil(N / kQueryTile)
+  int max_tiles;    // upper bound of query tiles over all buckets of one slice
+  double gamma_qk;  // relative error bound of an approximate score, in units of |q~| |k|
+  Layout ws;
+};
+
+// Validate arguments and build the plan. Returns MITA_OK or a negative status and
+// fills `err` (static storage) with the reason.
+mita_status make_plan(const mita_shape* shape, int m, int k, int s, Plan* p, const char** err);
+
+// Kernel launchers (one per step; each returns the first HIP error it meets).
+hipError_t launch_clear(const Plan& p, char* ws, hipStream_t st);
+hipError_t launch_pool(const Plan& p, const void* Q, char* ws, hipStream_t st);
+hipError_t launch_landmark(const Plan& p, const void* K, const void* V, char* ws, hipStream_t st);
+hipError_t launch_topk(const Plan& p, const void* K, char* ws, hipStream_t st);
+hipError_t launch_route(const Plan& p, const void* Q, char* ws, hipStream_t st);
+hipError_t launch_gather(const Plan& p, const void* Q, const void* K, const void* V, void* out, char* ws,
+                         hipStream_t st);
+
+}  // namespace mita

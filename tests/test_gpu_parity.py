@@ -1,0 +1,137 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the same
+seeded input bits. Index sets must be exact except on near-ties (relative
+k-th/(k+1)-th gap below 1e-6); outputs within max-abs 2e-2 (bf16) or 1e-4 (fp32)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from helpers import check_slice, run_gpu_steps, say, to_device, out_to_f64
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+
+def small(name, **kw):
+    return W["tiny"].with_(name=name, **kw)
+
+
+# Several tiles and ragged tails: N not a multiple of 64 (or of 4), 2D grids with
+# overlapping windows, both head sizes, both dtypes, every router path (fast
+# lists of 4, 6 and 8 entries, and the exact kernel for s > 6).
+SMALL = [
+    W["tiny"],
+    small("ragged_bf16", B=2, H=2, N=1000, grid_w=1000, pool_w=10, k=37, s=3, dtype="bf16"),
+    small("ragged_f32_d128", B=1, H=3, N=777, d=128, grid_w=777, pool_w=13, k=100, s=2),
+    small("grid2d_overlap", B=1, H=2, N=30 * 33, grid_h=30, grid_w=33, pool_h=4, pool_w=5, k=50, s=1, dtype="bf16"),
+    small("d128_s5", B=1, H=2, N=2048, d=128, grid_w=2048, pool_w=32, k=64, s=5, dtype="bf16", ncl=8),
+    small("exact_router_s7", B=1, H=1, N=1536, grid_w=1536, pool_w=24, k=40, s=7, dtype="bf16"),
+    small("multi_segment", B=1, H=1, N=20000, grid_w=20000, pool_w=40, k=300, s=2, dtype="bf16", needle_frac=0.01),
+    small("odd_n", B=1, H=1, N=1001, grid_w=1001, pool_w=7, k=1001, s=7, dtype="bf16"),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_small_workloads_all_slices(w, lib):
+    say(f"[parity] {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} m={w.m} k={w.k} s={w.s} {w.dtype}")
+    Q, K, V = synth.make_inputs(w)
+    gpu = run_gpu_steps(w, Q, K, V, lib)
+    for z in range(w.slices):
+        st = check_slice(w, Q, K, V, gpu, z)
+        say(f"  slice {z}: {st}")
+
+
+def test_forward_equals_steps_and_is_deterministic(lib):
+    w = SMALL[1]
+    Q, K, V = synth.make_inputs(w)
+    Qd, Kd, Vd = (to_device(x, w.dtype) for x in (Q, K, V))
+    call = lib.Mita.create(Qd, w.m, w.k, w.s, pool=(w.pool_h, w.pool_w))
+    a = call.forward(Qd, Kd, Vd).clone()
+    b = call.forward(Qd, Kd, Vd).clone()
+    call.pool(Qd)
+    call.landmark(Kd, Vd)
+    call.topk(Kd)
+    call.route(Qd)
+    c = call.gather(Qd, Kd, Vd)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
+def test_full_attention_reduction(lib):
+    # k = N: every expert holds every token; s = m adds ln m to every key logit
+    import oracle
+    for s in (1, 4):
+        w = small("kN", N=256, grid_w=256, pool_w=4, k=256, s=s)
+        Q, K, V = synth.make_inputs(w)
+        gpu = run_gpu_steps(w, Q, K, V, lib)
+        check_slice(w, Q, K, V, gpu, 0)
+        assert (np.sort(gpu["I"][0, 0], axis=1) == np.arange(256)).all()
+
+
+def test_degenerate_ties(lib):
+    # all-zero keys: every score ties, so experts are the k lowest token ids;
+    # all-zero queries: every router score ties, so queries go to experts 0..s-1
+    w = small("ties", N=4096, grid_w=4096, pool_w=16, k=100, s=2, dtype="bf16")
+    Q, K, V = synth.make_inputs(w)
+    K[:] = 0
+    Q[..., :2048, :] = 0
+    gpu = run_gpu_steps(w, Q, K, V, lib)
+    assert (gpu["I"][0, 0] == np.arange(100)[None, :]).all()
+    assert (gpu["E"][0, 0, :2048] == np.array([0, 1])[None, :]).all()
+    check_slice(w, Q, K, V, gpu, 0)
+
+
+def test_single_landmark_and_identity_pool(lib):
+    for pw, k, s in ((1, 20, 1), (128, 5, 3)):
+        w = small(f"pool{pw}", N=128, grid_w=128, pool_w=pw, k=k, s=s, dtype="bf16")
+        Q, K, V = synth.make_inputs(w)
+        gpu = run_gpu_steps(w, Q, K, V, lib)
+        check_slice(w, Q, K, V, gpu, 0)
+
+
+def test_invalid_arguments_raise(lib):
+    w = W["tiny"]
+    Q = torch.zeros((1, 1, 1024, 64), device="cuda")
+    with pytest.raises(ValueError):
+        lib.Mita.create(Q, 16, 2000, 1)           # k > N
+    with pytest.raises(ValueError):
+        lib.Mita.create(Q, 16, 64, 17)            # s > m
+    with pytest.raises(ValueError):
+        lib.Mita.create(torch.zeros((1, 1, 64, 96), device="cuda"), 4, 8, 1)   # d = 96 unsupported
+
+
+FULL = ["vit_b", "seg", "long", "very_long"]
+FULL_SLICES = {"vit_b": [0, 383], "seg": [0, 95], "long": [31], "very_long": [5]}
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name, lib):
+    """Whole workload through mita_forward (the launch configuration the benchmark
+    times), checked on sampled slices and queries."""
+    w = W[name]
+    say(f"[parity-full] {name}: generating")
+    Q, K, V = synth.make_inputs(w)
+    Qd, Kd, Vd = (to_device(x, w.dtype) for x in (Q, K, V))
+    call = lib.Mita.create(Qd, w.m, w.k, w.s, grid=(w.grid_h, w.grid_w), pool=(w.pool_h, w.pool_w))
+    say(f"[parity-full] {name}: forward")
+    O = call.forward(Qd, Kd, Vd)
+    torch.cuda.synchronize()
+    say(f"[parity-full] {name}: steps")
+    Qt = call.pool(Qd, want=True)
+    Vt, _ = call.landmark(Kd, Vd, want_vt=True)
+    I = call.topk(Kd, want=True)
+    E = call.route(Qd, want=True)
+    O2 = call.gather(Qd, Kd, Vd)
+    torch.cuda.synchronize()
+    assert torch.equal(O.view(torch.int16), O2.view(torch.int16))
+    gpu = {"Qt": Qt.cpu().numpy(), "Vt": Vt.cpu().numpy().astype(np.float64), "I": I.cpu().numpy(),
+           "E": E.cpu().numpy(), "O": out_to_f64(O)}
+    del Qd, Kd, Vd, call
+    rng = np.random.default_rng(1)
+    for z in FULL_SLICES[name]:
+        queries = np.sort(rng.choice(w.N, size=min(w.N, 192), replace=False))
+        say(f"[parity-full] {name}: oracle on slice {z}")
+        st = check_slice(w, Q, K, V, gpu, z, queries=queries, check_s=False)
+        say(f"  slice {z}: {st}")

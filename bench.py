@@ -1,0 +1,155 @@
+"""MiTA attention forward throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload vit_b]
+
+Prints one JSON line: query-tokens/s of the whole forward pass (B*H*N per call)
+on seeded synthetic inputs resident in HBM, the roofline position of the
+dominant kernel (timed live with HIP events on the library's stream) and the
+fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MiTA fwd query-tokens/sec (B·H·N/s) + % bf16 MFMA peak, % HBM BW"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def step_bytes(w) -> dict:
+    """Algorithmic HBM bytes per forward call, by step (each input or
+    intermediate counted once per step that must read or write it)."""
+    e = 2 if w.dtype == "bf16" else 4
+    BH, N, d, m, k, s = w.slices, w.N, w.d, w.m, w.k, w.s
+    tok = BH * N * d * e
+    return {
+        "pool": tok + BH * m * d * (8 + 4 + 4),
+        # K and V read once, score rows written once (fp32), shared-expert partials
+        "landmark": 2 * tok + BH * m * N * 4,
+        # score rows read once, expert lists written
+        "topk": BH * m * N * 4 + BH * m * k * 4,
+        "route": tok + BH * N * s * 4,
+        # Q read, each expert's k gathered K/V rows once, output written (+ partials when s > 1)
+        "gather": 2 * tok + BH * m * k * d * e * 2 + (BH * N * s * (d + 2) * 4 * 2 if s > 1 else 0),
+    }
+
+
+def cpu_baseline(w, Q, K, V, budget_s: float = 12.0) -> dict:
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    import synth
+
+    done, t0 = 0, time.perf_counter()
+    with threadpool_limits(limits=1):
+        for z in range(w.slices):
+            q64, k64, v64 = (synth.to_f64(x.reshape(-1, w.N, w.d)[z], w.dtype) for x in (Q, K, V))
+            oracle.forward(q64, k64, v64, w.grid_h, w.grid_w, w.pool_h, w.pool_w, w.k, w.s)
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    el = time.perf_counter() - t0
+    return {"value": done * w.N / el, "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {w.slices} (batch, head) slices of {w.name}, all {w.N} queries each, "
+                      f"fp64 numpy, BLAS limited to 1 thread, {el:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="vit_b")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--breakdown", action="store_true", help="print per-step times to stderr")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the MiTA forward here runs on a single MI355X "
+              "(no sharding, no collectives); run it with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    from sparse_top_routed_amd import mita
+
+    w = synth.WORKLOADS[a.workload]
+    Q, K, V = synth.make_inputs(w)
+
+    def dev(x):
+        if w.dtype == "bf16":
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(x).cuda()
+
+    Qd, Kd, Vd = dev(Q), dev(K), dev(V)
+    call = mita.Mita.create(Qd, w.m, w.k, w.s, grid=(w.grid_h, w.grid_w), pool=(w.pool_h, w.pool_w))
+    out = torch.empty_like(Qd)
+    for _ in range(a.warmup):
+        call.forward(Qd, Kd, Vd, out)
+    torch.cuda.synchronize()
+
+    st = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(st)
+    for _ in range(a.steps):
+        call.forward(Qd, Kd, Vd, out)
+    t1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1) / a.steps
+    tokens = w.slices * w.N
+
+    # per-step times: the same launches as forward, one step entry point at a time,
+    # bracketed by events on the stream the kernels run on
+    names = ["pool", "landmark", "topk", "route", "gather"]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    acc = dict.fromkeys(names, 0.0)
+    for _ in range(a.steps):
+        ev[0].record(st)
+        call.pool(Qd); ev[1].record(st)
+        call.landmark(Kd, Vd); ev[2].record(st)
+        call.topk(Kd); ev[3].record(st)
+        call.route(Qd); ev[4].record(st)
+        call.gather(Qd, Kd, Vd, out); ev[5].record(st)
+        torch.cuda.synchronize()
+        for i, n in enumerate(names):
+            acc[n] += ev[i].elapsed_time(ev[i + 1])
+    per = {n: acc[n] / a.steps for n in names}
+    nbytes = step_bytes(w)
+    dom = max(per, key=per.get)
+    achieved = nbytes[dom] / (per[dom] * 1e-3) / 1e9
+    if a.breakdown:
+        for n in names:
+            print(f"{n:9s} {per[n] * 1e3:9.1f} us  {nbytes[n] / (per[n] * 1e-3) / 1e9:8.1f} GB/s (algorithmic)",
+                  file=sys.stderr)
+        print(f"forward  {ms * 1e3:9.1f} us  wall {wall / a.steps * 1e3:9.1f} us", file=sys.stderr)
+
+    res = {
+        "metric": METRIC, "value": tokens / (ms * 1e-3), "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "m": w.m, "k": w.k, "s": w.s,
+                   "grid": [w.grid_h, w.grid_w], "pool": [w.pool_h, w.pool_w]},
+        "roofline": {"bound": "hbm", "kernel": f"{dom} step", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "step_ms": per,
+    }
+    if not a.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(w, Q, K, V)
+    print(json.dumps(res))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -77,7 +77,8 @@ def check_slice(w: synth.Workload, Q, K, V, gpu: Dict[str, np.ndarray], z: int,
         u = 2.0 ** -23
         gamma = (2 ** -16 + (2 * d + 4) * u) if w.dtype == "bf16" else (u + (d + 4) * u)
         bound = gamma * qn[:, None] * kmax
-        excess = (np.abs(g_s - S) / bound).max()
+        diff = np.abs(g_s - S)
+        excess = np.where(bound > 0, diff / np.where(bound > 0, bound, 1.0), np.where(diff > 0, np.inf, 0.0)).max()
         assert excess <= 1.0, f"slice {z}: score error {excess:.3g} x the bound"
 
     Vt = oracle.shared_expert(Qt, k64, v64)

@@ -32,9 +32,10 @@ __device__ __forceinline__ void stage_rows(T* dst, int stride, RowFn rowptr, int
 #pragma unroll
   for (int c = tid; c < TOTAL; c += 256) {
     const int r = c / CPR, cc = (c % CPR) * EPC;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < nvalid) v = *(const uint4*)(rowptr(r) + cc);
-    *(uint4*)(dst + r * stride + cc) = v;
+    // load unconditionally from a valid row, then zero: a conditional load would
+    // be compiled into a branch that waits for its result
+    const uint4 x = *(const uint4*)(rowptr(min(r, nvalid - 1)) + cc);
+    *(uint4*)(dst + r * stride + cc) = r < nvalid ? x : make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -49,7 +50,8 @@ __device__ __forceinline__ void stage_vt_bf16(uint16_t* Vt, RowFn rowptr, int nv
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int r = kg * 4 + u;
-      v[u] = r < nvalid ? *(const uint4*)(rowptr(r) + cc) : make_uint4(0, 0, 0, 0);
+      const uint4 x = *(const uint4*)(rowptr(min(r, nvalid - 1)) + cc);
+      v[u] = r < nvalid ? x : make_uint4(0, 0, 0, 0);
     }
     const uint32_t* w0 = (const uint32_t*)&v[0];
     const uint32_t* w1 = (const uint32_t*)&v[1];
@@ -65,6 +67,65 @@ __device__ __forceinline__ void stage_vt_bf16(uint16_t* Vt, RowFn rowptr, int nv
     }
   }
 }
+
+// A thread's share of one 64-row block, held in registers so the loads can be
+// issued early (prefetch) and written to LDS later.
+template <typename T, int D>
+struct RowRegs {
+  static constexpr int EPC = 16 / sizeof(T), CPR = D / EPC, PER = kKeyBlock * CPR / 256;
+  uint4 v[PER];
+  template <typename RowFn>
+  __device__ __forceinline__ void load(RowFn rowptr, int nvalid, int tid) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid + 256 * u, r = c / CPR, cc = (c % CPR) * EPC;
+      const uint4 x = *(const uint4*)(rowptr(min(r, nvalid - 1)) + cc);   // unconditional: no branch, no wait
+      v[u] = r < nvalid ? x : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void store(T* dst, int stride, int tid) const {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid + 256 * u, r = c / CPR, cc = (c % CPR) * EPC;
+      *(uint4*)(dst + r * stride + cc) = v[u];
+    }
+  }
+};
+
+// Same for a bf16 V block that is written transposed (V^T [D][64 + pad]). Each
+// thread holds RPT consecutive rows of one 8-element column chunk, so the
+// transposed writes are RPT keys wide.
+template <int D>
+struct VtRegs {
+  static constexpr int CPR = D / 8, RPT = kKeyBlock * CPR / 256;   // 2 rows (d = 64) or 4 rows (d = 128)
+  uint4 v[RPT];
+  template <typename RowFn>
+  __device__ __forceinline__ void load(RowFn rowptr, int nvalid, int tid) {
+    const int kg = tid / CPR, cc = (tid % CPR) * 8;
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) {
+      const int r = kg * RPT + u;
+      const uint4 x = *(const uint4*)(rowptr(min(r, nvalid - 1)) + cc);
+      v[u] = r < nvalid ? x : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* Vt, int tid) const {
+    constexpr int VSTR = Tiles<uint16_t, D>::VSTR;
+    const int kg = tid / CPR, cc = (tid % CPR) * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int sh = (e & 1) * 16, q = e >> 1;
+      uint32_t h[RPT];
+#pragma unroll
+      for (int u = 0; u < RPT; ++u) h[u] = (((const uint32_t*)&v[u])[q] >> sh) & 0xFFFFu;
+      if constexpr (RPT == 4) {
+        *(uint2*)(Vt + (cc + e) * VSTR + kg * 4) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+      } else {
+        *(uint32_t*)(Vt + (cc + e) * VSTR + kg * 2) = h[0] | (h[1] << 16);
+      }
+    }
+  }
+};
 
 // S^T block (64 keys x 16 queries) for bf16. Query side: QP parts in registers
 // (qf[p][ks] is lane's 8 elements 32*ks + 8*(lane/16) of query lane%16). Key
@@ -106,24 +167,34 @@ __device__ __forceinline__ void qk_f32(const float* Ks, const float (&qf)[D / 4]
   }
 }
 
-// Online softmax over one block. x holds log2-domain logits (masked keys are
-// -inf; every block has at least one live key). On return x holds the
-// unnormalised probabilities, and the returned factor rescales earlier sums.
-__device__ __forceinline__ float online_softmax(f32x4 (&x)[4], float& mrun, float& lrun) {
+// Online softmax over one block of raw scores (lane's keys 16 kt + 4 (lane/16) + j;
+// keys at or beyond `live` are masked). Works in the log2 domain: with
+// c = log2(e) / sqrt(d), p = 2^(c s - m). On return x holds the unnormalised
+// probabilities; the returned factor rescales earlier sums.
+__device__ __forceinline__ float online_softmax(f32x4 (&x)[4], int live, float c, float& mrun, float& lrun,
+                                                int lane) {
+  if (live < kKeyBlock) {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (16 * kt + 4 * g + j >= live) x[kt][j] = -INFINITY;
+  }
   float bm = -INFINITY;
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
     for (int j = 0; j < 4; ++j) bm = fmaxf(bm, x[kt][j]);
   bm = quad_max(bm);
-  const float mnew = fmaxf(mrun, bm);
+  const float mnew = fmaxf(mrun, bm * c);
   const float alpha = exp2f(mrun - mnew);
   float sum = 0.f;
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float p = exp2f(x[kt][j] - mnew);
+      const float p = exp2f(fmaf(x[kt][j], c, -mnew));
       x[kt][j] = p;
       sum += p;
     }

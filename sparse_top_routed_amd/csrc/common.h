@@ -13,11 +13,9 @@ constexpr int WAVE = 64;
 // ---------------------------------------------------------------- bf16 bits
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// float -> bf16 bits, round to nearest even (inputs here are finite).
+// float -> bf16 bits, round to nearest even (gfx950 converts in hardware).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // double -> bf16 bits, round to nearest even, without a detour through float
@@ -80,6 +78,55 @@ __device__ __forceinline__ float quad_sum(float v) {
   return v + __shfl_xor(v, 32, WAVE);
 }
 
+// Orders LDS traffic between the lanes of one wave (waves execute their LDS
+// operations in order; this stops the compiler from moving them across).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Exclusive prefix sum across the lanes of a wave; `total` gets the wave sum.
+__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t& total) {
+  const int lane = threadIdx.x & 63;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = __shfl_up(x, o, WAVE);
+    if (lane >= o) x += t;
+  }
+  total = __shfl(x, 63, WAVE);
+  return x - v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor(v, o, WAVE));
+  return v;
+}
+
+// DPP-based reductions (no LDS round trip): within each row of 16 lanes, then
+// across the four rows with readlane; the result is wave-uniform.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_sum_uniform(uint32_t x) {
+  x += dpp_u32<0xB1>(x);    // quad_perm [1,0,3,2]
+  x += dpp_u32<0x4E>(x);    // quad_perm [2,3,0,1]
+  x += dpp_u32<0x141>(x);   // row_half_mirror
+  x += dpp_u32<0x140>(x);   // row_mirror
+  return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) + __builtin_amdgcn_readlane(x, 32) +
+         __builtin_amdgcn_readlane(x, 48);
+}
+__device__ __forceinline__ uint32_t wave_max_uniform(uint32_t x) {
+  x = max(x, dpp_u32<0xB1>(x));
+  x = max(x, dpp_u32<0x4E>(x));
+  x = max(x, dpp_u32<0x141>(x));
+  x = max(x, dpp_u32<0x140>(x));
+  return max(max((uint32_t)__builtin_amdgcn_readlane(x, 0), (uint32_t)__builtin_amdgcn_readlane(x, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane(x, 32), (uint32_t)__builtin_amdgcn_readlane(x, 48)));
+}
+
 // Inclusive prefix sum over the 256 threads of a block, in thread order.
 __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wtot, uint32_t& total) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -110,8 +157,10 @@ __device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 }  // namespace mita

@@ -11,6 +11,8 @@
 // also attends the m landmark pairs and writes the output; with s > 1 it writes
 // an unnormalised partial per (query, slot) and the combine kernel attends the
 // landmark pairs and merges the s + 1 partial softmaxes.
+#include <type_traits>
+
 #include "attn_core.h"
 
 namespace mita {
@@ -36,9 +38,11 @@ __global__ __launch_bounds__(256) void bucket_hist_kernel(const int32_t* __restr
     if (h[i]) atomicAdd(&bcount[(size_t)z * m + i], h[i]);
 }
 
-// Exclusive scans of the bucket sizes and of their query-tile counts, per slice.
+// Exclusive scan of the bucket sizes, then the table of query tiles (at most
+// kQueryTile rows of one bucket each) that the gather kernel walks; unused
+// entries are marked with expert -1.
 __global__ __launch_bounds__(256) void bucket_scan_kernel(const uint32_t* __restrict__ bcount, uint32_t* __restrict__ boff,
-                                                          uint32_t* __restrict__ toff, int m) {
+                                                          int4* __restrict__ tiles, int m, int max_tiles) {
   __shared__ uint32_t wtot[4];
   const int z = blockIdx.x, tid = threadIdx.x;
   const int per = (m + 255) / 256, i0 = min(m, tid * per), i1 = min(m, i0 + per);
@@ -49,14 +53,15 @@ __global__ __launch_bounds__(256) void bucket_scan_kernel(const uint32_t* __rest
   uint32_t oc = block_incl_scan(sc, wtot, totc) - sc;
   uint32_t ot = block_incl_scan(st, wtot, tott) - st;
   uint32_t* bo = boff + (size_t)z * (m + 1);
-  uint32_t* to = toff + (size_t)z * (m + 1);
+  int4* tz = tiles + (size_t)z * max_tiles;
   for (int i = i0; i < i1; ++i) {
     bo[i] = oc;
-    to[i] = ot;
+    for (uint32_t r = 0; r < c[i]; r += kQueryTile, ++ot)
+      tz[ot] = make_int4(i, (int)r, (int)min((uint32_t)kQueryTile, c[i] - r), (int)(oc + r));
     oc += c[i];
-    ot += (c[i] + kQueryTile - 1) / kQueryTile;
   }
-  if (tid == 0) { bo[m] = totc; to[m] = tott; }
+  if (tid == 0) bo[m] = totc;
+  for (int t = (int)tott + tid; t < max_tiles; t += 256) tz[t] = make_int4(-1, 0, 0, 0);
 }
 
 // Scatter (query * s + slot) into its bucket; ranges are reserved per workgroup.
@@ -94,13 +99,15 @@ template <typename T, int D>
 struct QFrag {
   uint4 b[1][D / 32];
   float f[D / 4];
-  __device__ __forceinline__ void load(const T* qrow, bool ok, int g) {
+  // qrow must be a valid row; absent rows (padding) load a real row and their
+  // results are never written, since every row of the tile is independent.
+  __device__ __forceinline__ void load(const T* qrow, int g) {
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) b[0][ks] = ok ? *(const uint4*)(qrow + 32 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
+      for (int ks = 0; ks < D / 32; ++ks) b[0][ks] = *(const uint4*)(qrow + 32 * ks + 8 * g);
     } else {
 #pragma unroll
-      for (int ks = 0; ks < D / 4; ++ks) f[ks] = ok ? qrow[4 * ks + g] : 0.f;
+      for (int ks = 0; ks < D / 4; ++ks) f[ks] = qrow[4 * ks + g];
     }
   }
 };
@@ -117,17 +124,12 @@ struct AttnLds {
 template <typename T, int D, int KP>
 __device__ __forceinline__ void attend_block(AttnLds<T, D>& sm, const QFrag<T, D>& qf, int live, float sl2e,
                                              float& mrun, float& lrun, f32x4 (&o)[D / 16], int lane) {
-  const int g = lane >> 4;
   f32x4 acc[4];
   if constexpr (sizeof(T) == 2)
     qk_bf16<D, KP, 1>((const uint16_t*)sm.k0, (const uint16_t*)sm.k1, qf.b, acc, lane);
   else
     qk_f32<D>((const float*)sm.k0, qf.f, acc, lane);
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[kt][j] = (16 * kt + 4 * g + j < live) ? acc[kt][j] * sl2e : -INFINITY;
-  const float alpha = online_softmax(acc, mrun, lrun);
+  const float alpha = online_softmax(acc, live, sl2e, mrun, lrun, lane);
   rescale<D>(o, alpha);
   if constexpr (sizeof(T) == 2)
     pv_bf16<D>((const uint16_t*)sm.v, acc, o, lane);
@@ -135,28 +137,55 @@ __device__ __forceinline__ void attend_block(AttnLds<T, D>& sm, const QFrag<T, D
     pv_f32<D>((const float*)sm.v, acc, o, lane);
 }
 
-// Attention over the m landmark pairs (keys Q~, values V~). Block-uniform call.
+// Register copies of one key block and its value block (bf16 values transposed).
+template <typename T, int D, int KP>
+struct KVRegs {
+  RowRegs<T, D> k[KP];
+  std::conditional_t<sizeof(T) == 2, VtRegs<D>, RowRegs<T, D>> v;
+  __device__ __forceinline__ void store(AttnLds<T, D>& sm, int tid) const {
+    using TL = Tiles<T, D>;
+    k[0].store(sm.k0, TL::KSTR, tid);
+    if constexpr (KP == 2) k[1].store(sm.k1, TL::KSTR, tid);
+    if constexpr (sizeof(T) == 2) v.store((uint16_t*)sm.v, tid); else v.store(sm.v, TL::VSTR, tid);
+  }
+};
+
+// Landmark block lb0 of slice z: keys Q~ (hi and lo planes for bf16), values V~.
 template <typename T, int D>
-__device__ __forceinline__ void attend_landmarks(AttnLds<T, D>& sm, const QFrag<T, D>& qf, const void* qtop,
-                                                 const void* vtop, int z, int m, float sl2e, float& mrun, float& lrun,
-                                                 f32x4 (&o)[D / 16], int tid) {
-  using TL = Tiles<T, D>;
-  constexpr bool BF = TL::BF;
-  const int lane = tid & 63;
+__device__ __forceinline__ void load_landmarks(KVRegs<T, D, sizeof(T) == 2 ? 2 : 1>& R, const void* qtop,
+                                               const void* vtop, int z, int m, int lb0, int tid) {
+  constexpr bool BF = sizeof(T) == 2;
   const T* p0 = BF ? (const T*)((const uint16_t*)qtop + (size_t)z * 2 * m * D) : (const T*)((const float*)qtop + (size_t)z * m * D);
-  const T* p1 = p0 + (size_t)m * D;
   const T* vz = BF ? (const T*)((const uint16_t*)vtop + (size_t)z * m * D) : (const T*)((const float*)vtop + (size_t)z * m * D);
+  const int live = min(kKeyBlock, m - lb0);
+  R.k[0].load([&](int rr) { return p0 + (size_t)(lb0 + rr) * D; }, live, tid);
+  if constexpr (BF) R.k[1].load([&](int rr) { return p0 + (size_t)(m + lb0 + rr) * D; }, live, tid);
+  R.v.load([&](int rr) { return vz + (size_t)(lb0 + rr) * D; }, live, tid);
+}
+
+// Routed block kb of one expert: token rows K[I[kb + r]], V[I[kb + r]].
+template <typename T, int D>
+__device__ __forceinline__ void load_routed(KVRegs<T, D, 1>& R, const T* Kz, const T* Vz, const int32_t* Ie, int k,
+                                            int kb, int tid) {
+  const int live = min(kKeyBlock, k - kb);
+  R.k[0].load([&](int rr) { return Kz + (size_t)Ie[kb + rr] * D; }, live, tid);
+  R.v.load([&](int rr) { return Vz + (size_t)Ie[kb + rr] * D; }, live, tid);
+}
+
+// Attention over the m landmark pairs (keys Q~, values V~), block 0 already in
+// registers (R). Block-uniform call; ends with the LDS tiles free again.
+template <typename T, int D>
+__device__ __forceinline__ void attend_landmarks(AttnLds<T, D>& sm, KVRegs<T, D, sizeof(T) == 2 ? 2 : 1>& R,
+                                                 const QFrag<T, D>& qf, const void* qtop, const void* vtop, int z,
+                                                 int m, float sl2e, float& mrun, float& lrun, f32x4 (&o)[D / 16],
+                                                 int tid) {
+  constexpr int KP = sizeof(T) == 2 ? 2 : 1;
+  const int lane = tid & 63;
   for (int lb0 = 0; lb0 < m; lb0 += kKeyBlock) {
-    const int live = min(kKeyBlock, m - lb0);
-    stage_rows<T, D>(sm.k0, TL::KSTR, [&](int rr) { return p0 + (size_t)(lb0 + rr) * D; }, live, tid);
-    if constexpr (BF) {
-      stage_rows<T, D>(sm.k1, TL::KSTR, [&](int rr) { return p1 + (size_t)(lb0 + rr) * D; }, live, tid);
-      stage_vt_bf16<D>((uint16_t*)sm.v, [&](int rr) { return (const uint16_t*)vz + (size_t)(lb0 + rr) * D; }, live, tid);
-    } else {
-      stage_rows<T, D>(sm.v, TL::VSTR, [&](int rr) { return vz + (size_t)(lb0 + rr) * D; }, live, tid);
-    }
+    if (lb0 > 0) load_landmarks<T, D>(R, qtop, vtop, z, m, lb0, tid);
+    R.store(sm, tid);
     __syncthreads();
-    attend_block<T, D, BF ? 2 : 1>(sm, qf, live, sl2e, mrun, lrun, o, lane);
+    attend_block<T, D, KP>(sm, qf, min(kKeyBlock, m - lb0), sl2e, mrun, lrun, o, lane);
     __syncthreads();
   }
 }
@@ -174,61 +203,45 @@ __device__ __forceinline__ void store4(T* dst, float a, float b, float c, float 
 template <typename T, int D, bool FUSED>
 __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                      const T* __restrict__ V, const int32_t* __restrict__ I,
-                                                     const uint32_t* __restrict__ boff, const uint32_t* __restrict__ toff,
-                                                     const int32_t* __restrict__ perm, const void* __restrict__ qtop,
-                                                     const void* __restrict__ vtop, T* __restrict__ out,
-                                                     float* __restrict__ pacc, float* __restrict__ pml, int N, int m,
-                                                     int k, int s, float sl2e) {
+                                                     const int4* __restrict__ tiles, const int32_t* __restrict__ perm,
+                                                     const void* __restrict__ qtop, const void* __restrict__ vtop,
+                                                     T* __restrict__ out, float* __restrict__ pacc,
+                                                     float* __restrict__ pml, int N, int m, int k, int s,
+                                                     int max_tiles, float sl2e) {
   using TL = Tiles<T, D>;
   constexpr bool BF = TL::BF;
   __shared__ AttnLds<T, D> sm;
-  __shared__ int s_e, s_start, s_cnt;
   const int t = blockIdx.x, z = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15,
             g = lane >> 4;
-  const uint32_t* tz = toff + (size_t)z * (m + 1);
-  const uint32_t* bz = boff + (size_t)z * (m + 1);
-  if (tid == 0) {
-    if ((uint32_t)t >= tz[m]) {
-      s_e = -1;
-    } else {
-      int lo = 0, hi = m - 1;  // last e with tz[e] <= t
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (tz[mid] <= (uint32_t)t) lo = mid; else hi = mid - 1;
-      }
-      s_e = lo;
-      s_start = (int)(t - tz[lo]) * kQueryTile;
-      s_cnt = min(kQueryTile, (int)(bz[lo + 1] - bz[lo]) - s_start);
-    }
-  }
-  __syncthreads();
-  const int e = s_e;
+  const int4 te = tiles[(size_t)z * max_tiles + t];   // (expert, first row, rows, perm offset)
+  const int e = te.x;
   if (e < 0) return;
+  const int32_t* Ie = I + ((size_t)z * m + e) * k;
+  const T* Kz = K + (size_t)z * N * D;
+  const T* Vz = V + (size_t)z * N * D;
+  // first wave of loads: the query ids, the first landmark block, the first routed block
   const int rowi = 16 * w + r;
-  const bool ok = rowi < s_cnt;
-  const int entry = ok ? perm[(size_t)z * N * s + bz[e] + s_start + rowi] : 0;
+  const bool ok = rowi < te.z;
+  const int entry = perm[(size_t)z * N * s + te.w + min(rowi, te.z - 1)];
+  KVRegs<T, D, BF ? 2 : 1> LR;
+  if constexpr (FUSED) load_landmarks<T, D>(LR, qtop, vtop, z, m, 0, tid);
+  KVRegs<T, D, 1> RR;
+  load_routed<T, D>(RR, Kz, Vz, Ie, k, 0, tid);
   const int q = entry / s, slot = entry % s;
   QFrag<T, D> qf;
-  qf.load(Q + ((size_t)z * N + q) * D, ok, g);
+  qf.load(Q + ((size_t)z * N + q) * D, g);
 
   float mrun = -INFINITY, lrun = 0.f;
   f32x4 o[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if constexpr (FUSED) attend_landmarks<T, D>(sm, qf, qtop, vtop, z, m, sl2e, mrun, lrun, o, tid);
+  if constexpr (FUSED) attend_landmarks<T, D>(sm, LR, qf, qtop, vtop, z, m, sl2e, mrun, lrun, o, tid);
 
-  const int32_t* Ie = I + ((size_t)z * m + e) * k;
-  const T* Kz = K + (size_t)z * N * D;
-  const T* Vz = V + (size_t)z * N * D;
   for (int kb = 0; kb < k; kb += kKeyBlock) {
-    const int live = min(kKeyBlock, k - kb);
-    stage_rows<T, D>(sm.k0, TL::KSTR, [&](int rr) { return Kz + (size_t)Ie[kb + rr] * D; }, live, tid);
-    if constexpr (BF)
-      stage_vt_bf16<D>((uint16_t*)sm.v, [&](int rr) { return (const uint16_t*)Vz + (size_t)Ie[kb + rr] * D; }, live, tid);
-    else
-      stage_rows<T, D>(sm.v, TL::VSTR, [&](int rr) { return Vz + (size_t)Ie[kb + rr] * D; }, live, tid);
+    RR.store(sm, tid);
     __syncthreads();
-    attend_block<T, D, 1>(sm, qf, live, sl2e, mrun, lrun, o, lane);
+    if (kb + kKeyBlock < k) load_routed<T, D>(RR, Kz, Vz, Ie, k, kb + kKeyBlock, tid);   // prefetch
+    attend_block<T, D, 1>(sm, qf, min(kKeyBlock, k - kb), sl2e, mrun, lrun, o, lane);
     __syncthreads();
   }
 
@@ -261,12 +274,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Q, c
   const int q = blockIdx.x * kQueryTile + 16 * w + r;
   const bool ok = q < N;
   QFrag<T, D> qf;
-  qf.load(Q + ((size_t)z * N + (ok ? q : 0)) * D, ok, g);
+  qf.load(Q + ((size_t)z * N + (ok ? q : N - 1)) * D, g);
   float mrun = -INFINITY, lrun = 0.f;
   f32x4 o[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  attend_landmarks<T, D>(sm, qf, qtop, vtop, z, m, sl2e, mrun, lrun, o, tid);
+  {
+    KVRegs<T, D, sizeof(T) == 2 ? 2 : 1> LR;
+    load_landmarks<T, D>(LR, qtop, vtop, z, m, 0, tid);
+    attend_landmarks<T, D>(sm, LR, qf, qtop, vtop, z, m, sl2e, mrun, lrun, o, tid);
+  }
   const float l = quad_sum(lrun);
   if (!ok) return;
   const size_t p0 = ((size_t)z * N + q) * s;
@@ -313,7 +330,7 @@ static hipError_t gather_launch(const Plan& p, const void* Q, const void* K, con
                      (uint32_t*)(ws + p.ws.bcount), Ns, p.m);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bucket_scan_kernel, dim3(p.BH), dim3(256), 0, st, (const uint32_t*)(ws + p.ws.bcount),
-                     (uint32_t*)(ws + p.ws.boff), (uint32_t*)(ws + p.ws.toff), p.m);
+                     (uint32_t*)(ws + p.ws.boff), (int4*)(ws + p.ws.tiles), p.m, p.max_tiles);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bucket_scatter_kernel, bgrid, dim3(256), (size_t)p.m * 8, st, (const int32_t*)(ws + p.ws.E),
                      (const uint32_t*)(ws + p.ws.boff), (uint32_t*)(ws + p.ws.bcursor), (int32_t*)(ws + p.ws.perm), Ns,
@@ -325,16 +342,15 @@ static hipError_t gather_launch(const Plan& p, const void* Q, const void* K, con
   const dim3 ggrid(p.max_tiles, p.BH);
   if (p.s == 1) {
     hipLaunchKernelGGL((gather_kernel<T, D, true>), ggrid, dim3(256), 0, st, (const T*)Q, (const T*)K, (const T*)V,
-                       (const int32_t*)(ws + p.ws.I), (const uint32_t*)(ws + p.ws.boff),
-                       (const uint32_t*)(ws + p.ws.toff), (const int32_t*)(ws + p.ws.perm),
+                       (const int32_t*)(ws + p.ws.I), (const int4*)(ws + p.ws.tiles), (const int32_t*)(ws + p.ws.perm),
                        (const void*)(ws + p.ws.qtop), vtop, (T*)out, (float*)nullptr, (float*)nullptr, p.N, p.m, p.k,
-                       p.s, sl2e);
+                       p.s, p.max_tiles, sl2e);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((gather_kernel<T, D, false>), ggrid, dim3(256), 0, st, (const T*)Q, (const T*)K, (const T*)V,
-                     (const int32_t*)(ws + p.ws.I), (const uint32_t*)(ws + p.ws.boff), (const uint32_t*)(ws + p.ws.toff),
-                     (const int32_t*)(ws + p.ws.perm), (const void*)(ws + p.ws.qtop), vtop, (T*)out,
-                     (float*)(ws + p.ws.pacc), (float*)(ws + p.ws.pml), p.N, p.m, p.k, p.s, sl2e);
+                     (const int32_t*)(ws + p.ws.I), (const int4*)(ws + p.ws.tiles), (const int32_t*)(ws + p.ws.perm),
+                     (const void*)(ws + p.ws.qtop), vtop, (T*)out, (float*)(ws + p.ws.pacc), (float*)(ws + p.ws.pml),
+                     p.N, p.m, p.k, p.s, p.max_tiles, sl2e);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((combine_kernel<T, D>), dim3(p.qtiles, p.BH), dim3(256), 0, st, (const T*)Q,
                      (const void*)(ws + p.ws.qtop), vtop, (const float*)(ws + p.ws.pacc), (const float*)(ws + p.ws.pml),

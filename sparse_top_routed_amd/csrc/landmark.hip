@@ -28,6 +28,7 @@ __global__ __launch_bounds__(256) void landmark_kernel(const T* __restrict__ K, 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
   const int lm = lt * kLandmarkTile + 16 * w + r;
   const bool lm_ok = lm < m;
+  const int lmc = lm_ok ? lm : m - 1;   // padding lanes compute on a real landmark, never write
   const int k0 = c * lchunk, k1 = min(N, k0 + lchunk);
   const T* Kz = K + (size_t)z * N * D;
   const T* Vz = V + (size_t)z * N * D;
@@ -40,12 +41,11 @@ __global__ __launch_bounds__(256) void landmark_kernel(const T* __restrict__ K, 
     for (int p = 0; p < 2; ++p)
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks)
-        qb[p][ks] = lm_ok ? *(const uint4*)(qt + ((size_t)(z * 2 + p) * m + lm) * D + 32 * ks + 8 * g)
-                          : make_uint4(0, 0, 0, 0);
+        qb[p][ks] = *(const uint4*)(qt + ((size_t)(z * 2 + p) * m + lmc) * D + 32 * ks + 8 * g);
   } else {
     const float* qt = (const float*)qtop;
 #pragma unroll
-    for (int ks = 0; ks < D / 4; ++ks) qf[ks] = lm_ok ? qt[((size_t)z * m + lm) * D + 4 * ks + g] : 0.f;
+    for (int ks = 0; ks < D / 4; ++ks) qf[ks] = qt[((size_t)z * m + lmc) * D + 4 * ks + g];
   }
 
   float mrun = -INFINITY, lrun = 0.f, kmx = 0.f;
@@ -100,11 +100,7 @@ __global__ __launch_bounds__(256) void landmark_kernel(const T* __restrict__ K, 
         }
       }
     }
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[kt][j] = (kb + 16 * kt + 4 * g + j < k1) ? acc[kt][j] * sl2e : -INFINITY;
-    const float alpha = online_softmax(acc, mrun, lrun);
+    const float alpha = online_softmax(acc, nvalid, sl2e, mrun, lrun, lane);
     rescale<D>(o, alpha);
     if constexpr (BF)
       pv_bf16<D>((const uint16_t*)Vs, acc, o, lane);

@@ -102,7 +102,7 @@ mita_status make_plan(const mita_shape* shape, int m, int k, int s, Plan* p, con
   L.counters_bytes = off - L.counters;
   L.rflag = take(bh * N * 4);
   L.boff = take(bh * (m + 1) * 4);
-  L.toff = take(bh * (m + 1) * 4);
+  L.tiles = take(bh * (size_t)P.max_tiles * 16);
   L.perm = take(bh * N * s * 4);
   if (s > 1) {
     L.pacc = take(bh * N * s * d * 4);

@@ -14,6 +14,7 @@ constexpr int kLandmarkTile = 64;     // landmarks per workgroup in the shared-e
 constexpr int kKeyBlock = 64;         // keys per LDS block in the attention kernels
 constexpr int kQueryTile = 64;        // queries per workgroup in the router, gather and combine kernels
 constexpr int kTopkSegMax = 8192;     // scores per workgroup in the segment select kernel
+constexpr int kTopkWaveMax = 4096;    // rows up to this length are selected by one wave each
 constexpr int kRouteFastMaxS = 6;     // the router keeps per-lane top lists up to this s
 
 // Workspace offsets (bytes) of every intermediate buffer.
@@ -36,7 +37,7 @@ struct Layout {
   size_t bcount;    // u32 [BH, m]        queries routed to each expert
   size_t bcursor;   // u32 [BH, m]        scatter cursors
   size_t boff;      // u32 [BH, m + 1]    bucket offsets
-  size_t toff;      // u32 [BH, m + 1]    tile offsets (query tiles of kQueryTile per bucket)
+  size_t tiles;     // int4 [BH, max_tiles] query tiles: (expert, first row, rows, perm offset) or -1
   size_t perm;      // i32 [BH, N * s]    (query * s + slot) grouped by expert
   size_t pacc;      // f32 [BH, N, s, d]  per-slot partial outputs (s > 1)
   size_t pml;       // f32 [BH, N, s, 2]  per-slot (max, sum)

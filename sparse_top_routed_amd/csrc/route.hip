@@ -16,6 +16,23 @@
 
 namespace mita {
 
+// Insert into a descending top list. Within a lane the landmarks arrive in
+// increasing id, so an equal later value must stay below: strict comparison.
+template <int TM>
+__device__ __forceinline__ void list_insert_ordered(float (&tv)[TM], int (&ti)[TM], float v, int i) {
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const bool better = v > tv[j];
+    const float ov = tv[j];
+    const int oi = ti[j];
+    tv[j] = better ? v : ov;
+    ti[j] = better ? i : oi;
+    v = better ? ov : v;
+    i = better ? oi : i;
+  }
+}
+
+// Same with ties broken by the lower id (merging lists of different lanes).
 template <int TM>
 __device__ __forceinline__ void list_insert(float (&tv)[TM], int (&ti)[TM], float v, int i) {
 #pragma unroll
@@ -50,31 +67,22 @@ __global__ __launch_bounds__(256) void route_fast_kernel(const T* __restrict__ Q
   const int z = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
   const int q = blockIdx.x * kQueryTile + 16 * w + r;
   const bool q_ok = q < N;
-  const T* qrow = Q + ((size_t)z * N + (q_ok ? q : 0)) * D;
+  const T* qrow = Q + ((size_t)z * N + (q_ok ? q : N - 1)) * D;   // padding rows reuse a real row
 
+  // issue every independent load before the first wait: the query fragments,
+  // the landmark norms and (inside the loop) the first landmark block
   uint4 qb[1][D / 32];
   float qf[D / 4];
-  float sq = 0.f;
   if constexpr (BF) {
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
-      qb[0][ks] = q_ok ? *(const uint4*)(qrow + 32 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
-      const uint16_t* h = (const uint16_t*)&qb[0][ks];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { const float x = bf16_to_f32(h[e]); sq = fmaf(x, x, sq); }
-    }
+    for (int ks = 0; ks < D / 32; ++ks)
+      qb[0][ks] = *(const uint4*)(qrow + 32 * ks + 8 * g);
   } else {
 #pragma unroll
-    for (int ks = 0; ks < D / 4; ++ks) {
-      qf[ks] = q_ok ? qrow[4 * ks + g] : 0.f;
-      sq = fmaf(qf[ks], qf[ks], sq);
-    }
+    for (int ks = 0; ks < D / 4; ++ks) qf[ks] = qrow[4 * ks + g];
   }
-  const float qn = sqrtf(quad_sum(sq)) * 1.0001f;
   float qtm = 0.f;
   for (int i = tid; i < m; i += 256) qtm = fmaxf(qtm, qtnorm[(size_t)z * m + i]);
-  qtm = wave_max(qtm);
-  if (lane == 0) s_red[w] = qtm;
 
   float tv[TM];
   int ti[TM];
@@ -100,7 +108,7 @@ __global__ __launch_bounds__(256) void route_fast_kernel(const T* __restrict__ Q
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int li = lb0 + 16 * kt + 4 * g + j;
-        if (li < m) list_insert<TM>(tv, ti, acc[kt][j], li);
+        if (li < m) list_insert_ordered<TM>(tv, ti, acc[kt][j], li);
       }
   }
 #pragma unroll
@@ -113,6 +121,22 @@ __global__ __launch_bounds__(256) void route_fast_kernel(const T* __restrict__ Q
     for (int j = 0; j < TM; ++j) list_insert<TM>(tv, ti, ov[j], oi[j]);
   }
 
+  float sq = 0.f;
+  if constexpr (BF) {
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const uint16_t* h = (const uint16_t*)&qb[0][ks];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { const float x = bf16_to_f32(h[e]); sq = fmaf(x, x, sq); }
+    }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < D / 4; ++ks) sq = fmaf(qf[ks], qf[ks], sq);
+  }
+  const float qn = sqrtf(quad_sum(sq)) * 1.0001f;
+  qtm = wave_max(qtm);
+  if (lane == 0) s_red[w] = qtm;
+  __syncthreads();
   const double qtmax = (double)fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
   const double Eq = gamma * (double)qn * qtmax;
   // s-th and (s+1)-th entries without dynamic register indexing
@@ -241,7 +265,8 @@ static hipError_t route_launch(const Plan& p, const void* Q, char* ws, hipStream
   hipError_t e = hipSuccess;
   const bool fast = p.s <= kRouteFastMaxS;
   if (fast) {
-    if (p.s <= 2) e = route_fast_launch<T, D, 4>(p, Q, ws, st);
+    if (p.s == 1) e = route_fast_launch<T, D, 3>(p, Q, ws, st);
+    else if (p.s == 2) e = route_fast_launch<T, D, 4>(p, Q, ws, st);
     else if (p.s <= 4) e = route_fast_launch<T, D, 6>(p, Q, ws, st);
     else e = route_fast_launch<T, D, 8>(p, Q, ws, st);
     if (e != hipSuccess) return e;

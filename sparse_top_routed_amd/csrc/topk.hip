@@ -339,9 +339,393 @@ __global__ __launch_bounds__(256) void topk_row_kernel(const uint32_t* __restric
   }
 }
 
+// ---------------------------------------------------------------- rows of up to 4096 scores
+// One wave owns a whole row in registers (lane l holds scores 64 i + l, so every
+// register index is one coalesced 256-byte load and, in index order, a run of 64).
+// Counting is done with ballots (the popcounts run on the scalar unit, leaving
+// one vector compare per element). Steps:
+//   1. the top 4 key bits of the k-th largest score by a bit search (they hold
+//      sign and high exponent bits, which take few values);
+//   2. the next 8 bits by an LDS histogram over the scores sharing those 4 bits;
+//   3. every score >= (that 12-bit bucket's lower edge - 2E) goes, in index
+//      order, to an LDS list (typically k plus a few dozen);
+//   4. on the list: the exact k-th largest by a bit search, the band within 2E
+//      of it re-scored in fp64 (one lane per member), output in index order.
+// Rows whose list would overflow (massive ties) take a slower general path.
+// No block barriers: the four waves of a workgroup work on four rows.
+constexpr int kWaveCap = 512;
+
+__device__ __forceinline__ uint32_t ballot_count(bool p) { return (uint32_t)__popcll(__ballot(p)); }
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ void wave_bucket(const uint32_t* hist, uint32_t need, int lane, uint32_t& bin,
+                                            uint32_t& above) {
+  uint32_t h[4], ls = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) { h[b] = hist[4 * lane + b]; ls += h[b]; }
+  uint32_t suf = ls;  // bins of lanes >= lane
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = __shfl_down(suf, o, WAVE);
+    if (lane + o < 64) suf += t;
+  }
+  const uint32_t ab = suf - ls;
+  const bool cross = ab < need && suf >= need;
+  uint32_t mybin = 0, myab = 0;
+  if (cross) {
+    uint32_t run = ab;
+#pragma unroll
+    for (int b = 3; b >= 0; --b) {
+      if (run + h[b] >= need) { mybin = 4 * lane + b; myab = run; break; }
+      run += h[b];
+    }
+  }
+  const uint64_t msk = __ballot(cross);
+  const int src = msk ? __ffsll((unsigned long long)msk) - 1 : 0;
+  bin = __shfl(mybin, src, WAVE);
+  above = __shfl(myab, src, WAVE);
+}
+
+template <typename T>
+__device__ __forceinline__ double kval64(const T* kr, int c) {
+  if constexpr (sizeof(T) == 2) return (double)bf16_to_f32(((const uint16_t*)kr)[c]);
+  else return (double)kr[c];
+}
+
+// fp64 dot product of a landmark query (fp64) with one key row, by one lane; the
+// key row is fetched in 16-byte pieces that are all in flight together.
+template <typename T, int D>
+__device__ __forceinline__ double dot64_row(const double* __restrict__ q, const T* __restrict__ kr) {
+  constexpr int EPC = 16 / sizeof(T);
+  uint4 kc[D / EPC];
+#pragma unroll
+  for (int c = 0; c < D / EPC; ++c) kc[c] = *(const uint4*)(kr + c * EPC);
+  double s = 0.0;
+#pragma unroll
+  for (int c = 0; c < D / EPC; ++c) {
+    if constexpr (sizeof(T) == 2) {
+      const uint16_t* h = (const uint16_t*)&kc[c];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s = fma(q[8 * c + e], (double)bf16_to_f32(h[e]), s);
+    } else {
+      const float* f = (const float*)&kc[c];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = fma(q[4 * c + e], (double)f[e], s);
+    }
+  }
+  return s;
+}
+
+__device__ __forceinline__ void band_keys(double Tf, double E, uint32_t& hiKey, uint32_t& loKey) {
+  hiKey = (Tf + 2.0 * E < INFINITY) ? f32_key(round_up_f32(Tf + 2.0 * E)) : 0xFFFFFFFFu;
+  loKey = (Tf - 2.0 * E > -INFINITY) ? max(1u, f32_key(round_down_f32(Tf - 2.0 * E))) : 1u;
+}
+
+template <typename T, int D, int PL>
+__global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict__ S, const float* __restrict__ qtnorm,
+                                                        const float* __restrict__ kmax, int nsplit,
+                                                        const double* __restrict__ qt64, const T* __restrict__ K,
+                                                        int32_t* __restrict__ I, uint32_t* __restrict__ gen_list,
+                                                        uint32_t* __restrict__ gen_count, int N, int m, int k,
+                                                        double gamma, int rows) {
+  __shared__ uint32_t hist_s[4][256 + 64];   // 256 bins + one trash bin per lane
+  __shared__ uint32_t ckey_s[4][kWaveCap + 64];
+  __shared__ uint32_t cidx_s[4][kWaveCap + 64];
+  __shared__ double csc_s[4][kWaveCap];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int row = blockIdx.x * 4 + w;
+  if (row >= rows) return;
+  uint32_t* hist = hist_s[w];
+  uint32_t* ckey = ckey_s[w];
+  uint32_t* cidx = cidx_s[w];
+  double* csc = csc_s[w];
+  const int z = row / m;
+  const float* Srow = S + (size_t)row * N;
+  const T* Kz = K + (size_t)z * N * D;
+  const double* qrow = qt64 + (size_t)row * D;
+
+  // small loads first, so waiting for them does not wait for the row
+  float kmx = 0.f;
+  for (int c = lane; c < nsplit; c += 64) kmx = fmaxf(kmx, kmax[(size_t)z * nsplit + c]);
+  const float qtn = qtnorm[row];
+  // lane l owns scores [l PL, (l + 1) PL): a contiguous run, so the index order
+  // of the candidates is (lane, position) and needs a single prefix scan
+  const int n0 = lane * PL;
+  uint32_t kv[PL];
+  if ((N & 3) == 0) {
+#pragma unroll
+    for (int j = 0; j < PL / 4; ++j) {
+      const int n = n0 + 4 * j;
+      const float4 x = *(const float4*)(Srow + min(n, N - 4));   // unconditional (no branch, no wait)
+      kv[4 * j + 0] = n < N ? f32_key(x.x) : 0u;                  // 0: absent (no finite score maps to 0)
+      kv[4 * j + 1] = n < N ? f32_key(x.y) : 0u;
+      kv[4 * j + 2] = n < N ? f32_key(x.z) : 0u;
+      kv[4 * j + 3] = n < N ? f32_key(x.w) : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int n = n0 + i;
+      const float x = Srow[min(n, N - 1)];
+      kv[i] = n < N ? f32_key(x) : 0u;
+    }
+  }
+  for (int b = lane; b < 256 + 64; b += 64) hist[b] = 0;
+  const double E = gamma * (double)qtn * (double)wave_max(kmx);
+
+  // 1. top key byte of the k-th largest: walk the distinct top bytes downwards
+  //    from the maximum (they are few: sign and high exponent bits)
+  uint32_t lmax = 0;
+#pragma unroll
+  for (int i = 0; i < PL; ++i) lmax = max(lmax, kv[i]);
+  uint32_t b8 = wave_max_uniform(lmax) >> 24, above8 = 0;
+  for (;;) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) c += (kv[i] >> 24) == b8 ? 1u : 0u;
+    c = wave_sum_uniform(c);
+    if (above8 + c >= (uint32_t)k || b8 == 0) break;
+    above8 += c;
+    uint32_t nm = 0;   // largest key under the current top byte
+#pragma unroll
+    for (int i = 0; i < PL; ++i) nm = ((kv[i] >> 24) < b8) ? max(nm, kv[i]) : nm;
+    b8 = wave_max_uniform(nm) >> 24;
+  }
+  // 2. next byte by an LDS histogram over the scores under that top byte (the
+  //    others count into per-lane trash bins: no branches, no conflicts)
+  wave_sync();
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const uint32_t bin = ((kv[i] >> 24) == b8 && kv[i]) ? ((kv[i] >> 16) & 255u) : 256u + lane;
+    atomicAdd(&hist[bin], 1u);
+  }
+  wave_sync();
+  uint32_t b16, above16;
+  wave_bucket(hist, (uint32_t)k - above8, lane, b16, above16);
+  const uint32_t edge = (b8 << 24) | (b16 << 16);
+  uint32_t kt = 1u;
+  if (edge >= 0x00800000u) {
+    const double t = (double)key_f32(edge) - 2.0 * E;
+    if (t > -INFINITY) kt = max(1u, f32_key(round_down_f32(t)));
+  }
+  // 3. candidates (>= kt) in index order
+  uint32_t cl = 0;
+#pragma unroll
+  for (int i = 0; i < PL; ++i) cl += kv[i] >= kt ? 1u : 0u;
+  uint32_t cnt;
+  uint32_t pos = wave_excl_scan(cl, cnt);
+  if (cnt > (uint32_t)kWaveCap) {   // massive ties: the general kernel takes the row
+    if (lane == 0) gen_list[atomicAdd(gen_count, 1u)] = (uint32_t)row;
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const bool p = kv[i] >= kt;
+    const uint32_t dst = p ? pos : (uint32_t)(kWaveCap + lane);   // trash slot: no branch
+    ckey[dst] = kv[i];
+    cidx[dst] = (uint32_t)(n0 + i);
+    pos += p ? 1u : 0u;
+  }
+  wave_sync();
+  int32_t* Irow = I + (size_t)row * k;
+
+  // 4. exact k-th largest among the list (candidate j sits at slot j / 64 of lane j % 64)
+  constexpr int SL = kWaveCap / 64;
+  const int ns = (int)((cnt + 63) / 64);
+  uint32_t ck[SL];
+#pragma unroll
+  for (int sl = 0; sl < SL; ++sl) {
+    const uint32_t j = sl * 64 + lane;
+    ck[sl] = (sl < ns && j < cnt) ? ckey[j] : 0u;
+  }
+  uint32_t that = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = that | (1u << b);
+    uint32_t c = 0;
+#pragma unroll
+    for (int sl = 0; sl < SL; ++sl)
+      if (sl < ns) c += ballot_count(ck[sl] >= cand);
+    if (c >= (uint32_t)k) that = cand;
+  }
+  uint32_t hiKey, loKey;
+  band_keys((double)key_f32(that), E, hiKey, loKey);
+  uint32_t cin = 0, nb = 0;
+  // band members: their list slots go to the (now free) histogram array
+#pragma unroll
+  for (int sl = 0; sl < SL; ++sl) {
+    if (sl < ns) {
+      cin += ballot_count(ck[sl] > hiKey);
+      const bool inb = ck[sl] >= loKey && ck[sl] <= hiKey;
+      const uint64_t msk = __ballot(inb);
+      if (inb) {
+        const uint32_t bp = nb + lanes_below(msk);
+        if (bp < 256u) hist[bp] = sl * 64 + lane;
+      }
+      nb += (uint32_t)__popcll(msk);
+    }
+  }
+  const uint32_t need = (uint32_t)k - cin;
+  wave_sync();
+  // fp64 scores of the band members, one lane per member
+  if (nb <= 256u) {
+    for (uint32_t b0 = 0; b0 < nb; b0 += 64) {
+      const uint32_t bi = b0 + lane;
+      if (bi < nb) {
+        const uint32_t slot = hist[bi];
+        csc[slot] = dot64_row<T, D>(qrow, Kz + (size_t)cidx[slot] * D);
+      }
+    }
+  } else {
+    for (uint32_t j = lane; j < cnt; j += 64)
+      if (ckey[j] >= loKey && ckey[j] <= hiKey) csc[j] = dot64_row<T, D>(qrow, Kz + (size_t)cidx[j] * D);
+  }
+  wave_sync();
+  // selection and output in index order
+  uint32_t outpos = 0;
+#pragma unroll
+  for (int sl = 0; sl < SL; ++sl) {
+    if (sl < ns) {
+      const uint32_t j = sl * 64 + lane;
+      bool sel = false;
+      if (j < cnt) {
+        if (ck[sl] > hiKey) {
+          sel = true;
+        } else if (ck[sl] >= loKey) {
+          const double sj = csc[j];
+          const uint32_t ij = cidx[j];
+          uint32_t rank = 0;
+          for (uint32_t i2 = 0; i2 < cnt; ++i2) {
+            const uint32_t ki = ckey[i2];
+            if (ki >= loKey && ki <= hiKey) {
+              const double si = csc[i2];
+              rank += (si > sj || (si == sj && cidx[i2] < ij)) ? 1u : 0u;
+            }
+          }
+          sel = rank < need;
+        }
+      }
+      const uint64_t msk = __ballot(sel);
+      if (sel) {
+        const uint32_t op = outpos + lanes_below(msk);
+        if (op < (uint32_t)k) Irow[op] = (int32_t)cidx[j];
+      }
+      outpos += (uint32_t)__popcll(msk);
+    }
+  }
+}
+
+// Rows the wave kernel could not list (massive ties): one wave per row, straight
+// from the score row in global memory. Exact k-th largest by a bit search over
+// the order keys; the band around it decided by fp64 scores (recomputed on the
+// fly) with a bit search over fp64 order keys; ties to the lower index.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void topk_general_kernel(const float* __restrict__ S, const float* __restrict__ qtnorm,
+                                                          const float* __restrict__ kmax, int nsplit,
+                                                          const double* __restrict__ qt64, const T* __restrict__ K,
+                                                          int32_t* __restrict__ I, const uint32_t* __restrict__ gen_list,
+                                                          const uint32_t* __restrict__ gen_count, int N, int m, int k,
+                                                          double gamma) {
+  const int lane = threadIdx.x;
+  const uint32_t total = *gen_count;
+  for (uint32_t t = blockIdx.x; t < total; t += gridDim.x) {
+    const int row = (int)gen_list[t], z = row / m;
+    const float* Srow = S + (size_t)row * N;
+    const T* Kz = K + (size_t)z * N * D;
+    const double* qrow = qt64 + (size_t)row * D;
+    float kmx = 0.f;
+    for (int c = lane; c < nsplit; c += 64) kmx = fmaxf(kmx, kmax[(size_t)z * nsplit + c]);
+    const double E = gamma * (double)qtnorm[row] * (double)wave_max(kmx);
+    uint32_t pfx = 0;
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t cand = pfx | (1u << b);
+      uint32_t c = 0;
+      for (int n = lane; n < N; n += 64) c += f32_key(Srow[n]) >= cand ? 1u : 0u;
+      if (wave_sum_uniform(c) >= (uint32_t)k) pfx = cand;
+    }
+    uint32_t hiKey, loKey;
+    band_keys((double)key_f32(pfx), E, hiKey, loKey);
+    uint32_t cin = 0;
+    for (int n = lane; n < N; n += 64) cin += f32_key(Srow[n]) > hiKey ? 1u : 0u;
+    const uint32_t need = (uint32_t)k - wave_sum_uniform(cin);
+    auto score = [&](int n) {
+      const T* kr = Kz + (size_t)n * D;
+      double sc = 0.0;
+      for (int c = 0; c < D; ++c) sc = fma(qrow[c], kval64<T>(kr, c), sc);
+      return sc;
+    };
+    uint64_t p64 = 0;
+    for (int b = 63; b >= 0; --b) {
+      const uint64_t cand = p64 | (1ull << b);
+      uint32_t c = 0;
+      for (int n = lane; n < N; n += 64) {
+        const uint32_t x = f32_key(Srow[n]);
+        if (x >= loKey && x <= hiKey) c += f64_key(score(n)) >= cand ? 1u : 0u;
+      }
+      if (wave_sum_uniform(c) >= need) p64 = cand;
+    }
+    uint32_t gtl = 0;
+    for (int n = lane; n < N; n += 64) {
+      const uint32_t x = f32_key(Srow[n]);
+      if (x >= loKey && x <= hiKey) gtl += f64_key(score(n)) > p64 ? 1u : 0u;
+    }
+    const uint32_t ties_needed = need - wave_sum_uniform(gtl);
+    int32_t* Irow = I + (size_t)row * k;
+    uint32_t outpos = 0, ties_seen = 0;
+    for (int c0 = 0; c0 < N; c0 += 64) {
+      const int n = c0 + lane;
+      bool sel = false, tie = false;
+      if (n < N) {
+        const uint32_t x = f32_key(Srow[n]);
+        if (x > hiKey) {
+          sel = true;
+        } else if (x >= loKey) {
+          const uint64_t k64 = f64_key(score(n));
+          sel = k64 > p64;
+          tie = k64 == p64;
+        }
+      }
+      const uint64_t tm = __ballot(tie);
+      if (tie && ties_seen + lanes_below(tm) < ties_needed) sel = true;
+      ties_seen += (uint32_t)__popcll(tm);
+      const uint64_t sm = __ballot(sel);
+      if (sel) {
+        const uint32_t op = outpos + lanes_below(sm);
+        if (op < (uint32_t)k) Irow[op] = n;
+      }
+      outpos += (uint32_t)__popcll(sm);
+    }
+  }
+}
+
+__global__ void topk_zero_kernel(uint32_t* __restrict__ p) { *p = 0u; }
+
 template <typename T, int D>
 static hipError_t topk_launch(const Plan& p, const void* K, char* ws, hipStream_t st) {
   const int rows = p.BH * p.m;
+  if (p.N <= kTopkWaveMax) {
+    uint32_t* gen_count = (uint32_t*)(ws + p.ws.counters) + 32;   // counter of rows for the general kernel
+    uint32_t* gen_list = (uint32_t*)(ws + p.ws.cand_idx);
+    hipLaunchKernelGGL(topk_zero_kernel, dim3(1), dim3(1), 0, st, gen_count);
+    const dim3 grid((rows + 3) / 4);
+    auto args = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, (const float*)(ws + p.ws.S), (const float*)(ws + p.ws.qtnorm),
+                         (const float*)(ws + p.ws.kmax), p.nsplit, (const double*)(ws + p.ws.qt64), (const T*)K,
+                         (int32_t*)(ws + p.ws.I), gen_list, gen_count, p.N, p.m, p.k, p.gamma_qk, rows);
+    };
+    if (p.N <= 1024) args(topk_wave_kernel<T, D, 16>);
+    else if (p.N <= 2048) args(topk_wave_kernel<T, D, 32>);
+    else if (p.N <= 3328) args(topk_wave_kernel<T, D, 52>);
+    else args(topk_wave_kernel<T, D, 64>);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((topk_general_kernel<T, D>), dim3(256), dim3(64), 0, st, (const float*)(ws + p.ws.S),
+                       (const float*)(ws + p.ws.qtnorm), (const float*)(ws + p.ws.kmax), p.nsplit,
+                       (const double*)(ws + p.ws.qt64), (const T*)K, (int32_t*)(ws + p.ws.I),
+                       (const uint32_t*)gen_list, (const uint32_t*)gen_count, p.N, p.m, p.k, p.gamma_qk);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(topk_segment_kernel, dim3(p.G, rows), dim3(256), 0, st, (const float*)(ws + p.ws.S),
                      (const float*)(ws + p.ws.qtnorm), (const float*)(ws + p.ws.kmax), p.nsplit,
                      (uint32_t*)(ws + p.ws.cand_key), (uint32_t*)(ws + p.ws.cand_idx), (uint32_t*)(ws + p.ws.cand_cnt),

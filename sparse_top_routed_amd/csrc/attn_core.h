@@ -188,13 +188,14 @@ __device__ __forceinline__ float online_softmax(f32x4 (&x)[4], int live, float c
     for (int j = 0; j < 4; ++j) bm = fmaxf(bm, x[kt][j]);
   bm = quad_max(bm);
   const float mnew = fmaxf(mrun, bm * c);
-  const float alpha = exp2f(mrun - mnew);
+  // raw v_exp_f32 (no denormal range fix-up: probabilities below 2^-126 flush to 0)
+  const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
   float sum = 0.f;
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float p = exp2f(fmaf(x[kt][j], c, -mnew));
+      const float p = __builtin_amdgcn_exp2f(fmaf(x[kt][j], c, -mnew));
       x[kt][j] = p;
       sum += p;
     }

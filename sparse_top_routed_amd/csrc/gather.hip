@@ -123,7 +123,9 @@ struct AttnLds {
 // One 64-key block of attention for the wave's 16 queries, keys already staged.
 template <typename T, int D, int KP>
 __device__ __forceinline__ void attend_block(AttnLds<T, D>& sm, const QFrag<T, D>& qf, int live, float sl2e,
-                                             float& mrun, float& lrun, f32x4 (&o)[D / 16], int lane) {
+                                             float& mrun, float& lrun, f32x4 (&o)[D / 16], int lane,
+                                             bool wave_live = true) {
+  if (!wave_live) return;   // all 16 rows of this wave are padding (wave-uniform)
   f32x4 acc[4];
   if constexpr (sizeof(T) == 2)
     qk_bf16<D, KP, 1>((const uint16_t*)sm.k0, (const uint16_t*)sm.k1, qf.b, acc, lane);
@@ -178,14 +180,14 @@ template <typename T, int D>
 __device__ __forceinline__ void attend_landmarks(AttnLds<T, D>& sm, KVRegs<T, D, sizeof(T) == 2 ? 2 : 1>& R,
                                                  const QFrag<T, D>& qf, const void* qtop, const void* vtop, int z,
                                                  int m, float sl2e, float& mrun, float& lrun, f32x4 (&o)[D / 16],
-                                                 int tid) {
+                                                 int tid, bool wave_live = true) {
   constexpr int KP = sizeof(T) == 2 ? 2 : 1;
   const int lane = tid & 63;
   for (int lb0 = 0; lb0 < m; lb0 += kKeyBlock) {
     if (lb0 > 0) load_landmarks<T, D>(R, qtop, vtop, z, m, lb0, tid);
     R.store(sm, tid);
     __syncthreads();
-    attend_block<T, D, KP>(sm, qf, min(kKeyBlock, m - lb0), sl2e, mrun, lrun, o, lane);
+    attend_block<T, D, KP>(sm, qf, min(kKeyBlock, m - lb0), sl2e, mrun, lrun, o, lane, wave_live);
     __syncthreads();
   }
 }
@@ -235,13 +237,14 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ Q, co
   f32x4 o[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if constexpr (FUSED) attend_landmarks<T, D>(sm, LR, qf, qtop, vtop, z, m, sl2e, mrun, lrun, o, tid);
+  const bool wave_live = 16 * w < te.z;
+  if constexpr (FUSED) attend_landmarks<T, D>(sm, LR, qf, qtop, vtop, z, m, sl2e, mrun, lrun, o, tid, wave_live);
 
   for (int kb = 0; kb < k; kb += kKeyBlock) {
     RR.store(sm, tid);
     __syncthreads();
     if (kb + kKeyBlock < k) load_routed<T, D>(RR, Kz, Vz, Ie, k, kb + kKeyBlock, tid);   // prefetch
-    attend_block<T, D, 1>(sm, qf, min(kKeyBlock, k - kb), sl2e, mrun, lrun, o, lane);
+    attend_block<T, D, 1>(sm, qf, min(kKeyBlock, k - kb), sl2e, mrun, lrun, o, lane, wave_live);
     __syncthreads();
   }
 

@@ -431,16 +431,16 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
                                                         uint32_t* __restrict__ gen_count, int N, int m, int k,
                                                         double gamma, int rows) {
   __shared__ uint32_t hist_s[4][256 + 64];   // 256 bins + one trash bin per lane
-  __shared__ uint32_t ckey_s[4][kWaveCap + 64];
-  __shared__ uint32_t cidx_s[4][kWaveCap + 64];
+  __shared__ uint2 cand_s[4][kWaveCap + 64];   // (order key, token id), then trash slots
   __shared__ double csc_s[4][kWaveCap];
+  __shared__ uint8_t kflag_s[4][kWaveCap];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int row = blockIdx.x * 4 + w;
   if (row >= rows) return;
   uint32_t* hist = hist_s[w];
-  uint32_t* ckey = ckey_s[w];
-  uint32_t* cidx = cidx_s[w];
+  uint2* cand = cand_s[w];
   double* csc = csc_s[w];
+  uint8_t* kflag = kflag_s[w];
   const int z = row / m;
   const float* Srow = S + (size_t)row * N;
   const T* Kz = K + (size_t)z * N * D;
@@ -450,14 +450,14 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
   float kmx = 0.f;
   for (int c = lane; c < nsplit; c += 64) kmx = fmaxf(kmx, kmax[(size_t)z * nsplit + c]);
   const float qtn = qtnorm[row];
-  // lane l owns scores [l PL, (l + 1) PL): a contiguous run, so the index order
-  // of the candidates is (lane, position) and needs a single prefix scan
-  const int n0 = lane * PL;
+  // coalesced: register group j holds scores 4 (64 j + lane) + c, c < 4, so each
+  // load instruction reads 1 KiB contiguously; index order is (group, lane, c)
+  constexpr int PG = PL / 4;
   uint32_t kv[PL];
   if ((N & 3) == 0) {
 #pragma unroll
-    for (int j = 0; j < PL / 4; ++j) {
-      const int n = n0 + 4 * j;
+    for (int j = 0; j < PG; ++j) {
+      const int n = (64 * j + lane) * 4;
       const float4 x = *(const float4*)(Srow + min(n, N - 4));   // unconditional (no branch, no wait)
       kv[4 * j + 0] = n < N ? f32_key(x.x) : 0u;                  // 0: absent (no finite score maps to 0)
       kv[4 * j + 1] = n < N ? f32_key(x.y) : 0u;
@@ -466,11 +466,13 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < PL; ++i) {
-      const int n = n0 + i;
-      const float x = Srow[min(n, N - 1)];
-      kv[i] = n < N ? f32_key(x) : 0u;
-    }
+    for (int j = 0; j < PG; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int n = (64 * j + lane) * 4 + c;
+        const float x = Srow[min(n, N - 1)];
+        kv[4 * j + c] = n < N ? f32_key(x) : 0u;
+      }
   }
   for (int b = lane; b < 256 + 64; b += 64) hist[b] = 0;
   const double E = gamma * (double)qtn * (double)wave_max(kmx);
@@ -510,44 +512,73 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
     const double t = (double)key_f32(edge) - 2.0 * E;
     if (t > -INFINITY) kt = max(1u, f32_key(round_down_f32(t)));
   }
-  // 3. candidates (>= kt) in index order
-  uint32_t cl = 0;
+  // 3. candidates (>= kt) in index order: per-group counts, three groups per
+  //    word (10-bit fields), one prefix scan per word
+  constexpr int PW = (PG + 2) / 3;
+  uint32_t gofs[PG];
+  uint32_t cnt = 0;
 #pragma unroll
-  for (int i = 0; i < PL; ++i) cl += kv[i] >= kt ? 1u : 0u;
-  uint32_t cnt;
-  uint32_t pos = wave_excl_scan(cl, cnt);
+  for (int wdx = 0; wdx < PW; ++wdx) {
+    uint32_t packed = 0;
+#pragma unroll
+    for (int f = 0; f < 3; ++f) {
+      const int j = 3 * wdx + f;
+      if (j < PG) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) c += kv[4 * j + cc] >= kt ? 1u : 0u;
+        packed |= c << (10 * f);
+      }
+    }
+    uint32_t tot;
+    const uint32_t ex = wave_excl_scan(packed, tot);
+#pragma unroll
+    for (int f = 0; f < 3; ++f) {
+      const int j = 3 * wdx + f;
+      if (j < PG) {
+        gofs[j] = cnt + ((ex >> (10 * f)) & 1023u);
+        cnt += (tot >> (10 * f)) & 1023u;
+      }
+    }
+  }
   if (cnt > (uint32_t)kWaveCap) {   // massive ties: the general kernel takes the row
     if (lane == 0) gen_list[atomicAdd(gen_count, 1u)] = (uint32_t)row;
     return;
   }
 #pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    const bool p = kv[i] >= kt;
-    const uint32_t dst = p ? pos : (uint32_t)(kWaveCap + lane);   // trash slot: no branch
-    ckey[dst] = kv[i];
-    cidx[dst] = (uint32_t)(n0 + i);
-    pos += p ? 1u : 0u;
+  for (int j = 0; j < PG; ++j) {
+    uint32_t pos = gofs[j];
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const uint32_t x = kv[4 * j + cc];
+      const bool p = x >= kt;
+      const uint32_t dst = p ? pos : (uint32_t)(kWaveCap + lane);   // trash slot: no branch
+      cand[dst] = make_uint2(x, (uint32_t)((64 * j + lane) * 4 + cc));
+      pos += p ? 1u : 0u;
+    }
   }
   wave_sync();
-  int32_t* Irow = I + (size_t)row * k;
 
-  // 4. exact k-th largest among the list (candidate j sits at slot j / 64 of lane j % 64)
+  // 4. exact k-th largest: it lies in the 16-bit bucket [edge, edge + 2^16) and is
+  //    the r-th largest there, r = k - (scores above the bucket); search the low
+  //    16 bits among the bucket's candidates (candidate j: slot j / 64 of lane j % 64)
   constexpr int SL = kWaveCap / 64;
   const int ns = (int)((cnt + 63) / 64);
   uint32_t ck[SL];
 #pragma unroll
   for (int sl = 0; sl < SL; ++sl) {
     const uint32_t j = sl * 64 + lane;
-    ck[sl] = (sl < ns && j < cnt) ? ckey[j] : 0u;
+    ck[sl] = (sl < ns && j < cnt) ? cand[j].x : 0u;
   }
-  uint32_t that = 0;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t cand = that | (1u << b);
+  const uint32_t r = (uint32_t)k - above8 - above16;
+  uint32_t that = edge;
+  for (int b = 15; b >= 0; --b) {
+    const uint32_t tst = that | (1u << b);
     uint32_t c = 0;
 #pragma unroll
     for (int sl = 0; sl < SL; ++sl)
-      if (sl < ns) c += ballot_count(ck[sl] >= cand);
-    if (c >= (uint32_t)k) that = cand;
+      if (sl < ns) c += ballot_count(ck[sl] >= tst && ck[sl] < edge + 0x10000u);
+    if (c >= r) that = tst;
   }
   uint32_t hiKey, loKey;
   band_keys((double)key_f32(that), E, hiKey, loKey);
@@ -567,49 +598,80 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
     }
   }
   const uint32_t need = (uint32_t)k - cin;
-  wave_sync();
-  // fp64 scores of the band members, one lane per member
-  if (nb <= 256u) {
-    for (uint32_t b0 = 0; b0 < nb; b0 += 64) {
-      const uint32_t bi = b0 + lane;
-      if (bi < nb) {
-        const uint32_t slot = hist[bi];
-        csc[slot] = dot64_row<T, D>(qrow, Kz + (size_t)cidx[slot] * D);
+  // keep[sl]: band members that make the cut. When the band holds exactly as many
+  // members as places left, no re-scoring is needed (the usual case: the band
+  // is the k-th score alone).
+  bool keep[SL];
+#pragma unroll
+  for (int sl = 0; sl < SL; ++sl) keep[sl] = nb == need;
+  if (nb != need) {
+    wave_sync();
+    if (nb <= 256u) {
+      // fp64 scores, one lane per member, then ranks by (score desc, index asc)
+      for (uint32_t b0 = 0; b0 < nb; b0 += 64) {
+        const uint32_t bi = b0 + lane;
+        if (bi < nb) {
+          const uint32_t slot = hist[bi];
+          csc[slot] = dot64_row<T, D>(qrow, Kz + (size_t)cand[slot].y * D);
+        }
+      }
+      wave_sync();
+      for (uint32_t b0 = 0; b0 < nb; b0 += 64) {
+        const uint32_t bi = b0 + lane;
+        if (bi < nb) {
+          const uint32_t slot = hist[bi];
+          const double sj = csc[slot];
+          const uint32_t ij = cand[slot].y;
+          uint32_t rank = 0;
+          for (uint32_t f = 0; f < nb; ++f) {
+            const uint32_t sf = hist[f];
+            const double si = csc[sf];
+            rank += (si > sj || (si == sj && cand[sf].y < ij)) ? 1u : 0u;
+          }
+          kflag[slot] = rank < need ? 1 : 0;
+        }
+      }
+    } else {
+      for (uint32_t j = lane; j < cnt; j += 64) {
+        const uint32_t kj = cand[j].x;
+        if (kj >= loKey && kj <= hiKey) csc[j] = dot64_row<T, D>(qrow, Kz + (size_t)cand[j].y * D);
+      }
+      wave_sync();
+      for (uint32_t j = lane; j < cnt; j += 64) {
+        const uint32_t kj = cand[j].x;
+        if (kj < loKey || kj > hiKey) continue;
+        const double sj = csc[j];
+        const uint32_t ij = cand[j].y;
+        uint32_t rank = 0;
+        for (uint32_t i2 = 0; i2 < cnt; ++i2) {
+          const uint32_t ki = cand[i2].x;
+          if (ki >= loKey && ki <= hiKey) {
+            const double si = csc[i2];
+            rank += (si > sj || (si == sj && cand[i2].y < ij)) ? 1u : 0u;
+          }
+        }
+        kflag[j] = rank < need ? 1 : 0;
       }
     }
-  } else {
-    for (uint32_t j = lane; j < cnt; j += 64)
-      if (ckey[j] >= loKey && ckey[j] <= hiKey) csc[j] = dot64_row<T, D>(qrow, Kz + (size_t)cidx[j] * D);
+    wave_sync();
+#pragma unroll
+    for (int sl = 0; sl < SL; ++sl) {
+      const uint32_t j = sl * 64 + lane;
+      keep[sl] = (sl < ns && j < cnt && ck[sl] >= loKey && ck[sl] <= hiKey) ? kflag[j] != 0 : false;
+    }
   }
-  wave_sync();
-  // selection and output in index order
+  // output in index order: members above the band and the band members kept
+  int32_t* Irow = I + (size_t)row * k;
   uint32_t outpos = 0;
 #pragma unroll
   for (int sl = 0; sl < SL; ++sl) {
     if (sl < ns) {
       const uint32_t j = sl * 64 + lane;
-      bool sel = false;
-      if (j < cnt) {
-        if (ck[sl] > hiKey) {
-          sel = true;
-        } else if (ck[sl] >= loKey) {
-          const double sj = csc[j];
-          const uint32_t ij = cidx[j];
-          uint32_t rank = 0;
-          for (uint32_t i2 = 0; i2 < cnt; ++i2) {
-            const uint32_t ki = ckey[i2];
-            if (ki >= loKey && ki <= hiKey) {
-              const double si = csc[i2];
-              rank += (si > sj || (si == sj && cidx[i2] < ij)) ? 1u : 0u;
-            }
-          }
-          sel = rank < need;
-        }
-      }
+      const bool sel = j < cnt && (ck[sl] > hiKey || (ck[sl] >= loKey && keep[sl]));
       const uint64_t msk = __ballot(sel);
       if (sel) {
         const uint32_t op = outpos + lanes_below(msk);
-        if (op < (uint32_t)k) Irow[op] = (int32_t)cidx[j];
+        if (op < (uint32_t)k) Irow[op] = (int32_t)cand[j].y;
       }
       outpos += (uint32_t)__popcll(msk);
     }

@@ -202,6 +202,102 @@ __device__ __forceinline__ void store4(T* dst, float a, float b, float c, float 
   }
 }
 
+// LDS of the persistent gather kernel: the routed key/value block, the slice's
+// landmark block (kept resident while consecutive tiles share a slice; also the
+// staging area when m > 64) and the workgroup's list of tiles.
+template <typename T, int D, bool FUSED>
+struct GatherLds {
+  using TL = Tiles<T, D>;
+  __align__(16) T rk[TL::KTILE];
+  __align__(16) T rv[TL::VTILE];
+  AttnLds<T, D> lm;      // landmark block (used only when the landmark part is fused)
+  int4 tile[256];
+  int tz[256];
+  uint32_t wtot[4];
+};
+template <typename T, int D>
+struct GatherLds<T, D, false> {
+  using TL = Tiles<T, D>;
+  __align__(16) T rk[TL::KTILE];
+  __align__(16) T rv[TL::VTILE];
+  int4 tile[256];
+  int tz[256];
+  uint32_t wtot[4];
+};
+
+template <typename T, int D, int KP>
+__device__ __forceinline__ void attend_tiles(const T* kt0, const T* kt1, const T* vt, const QFrag<T, D>& qf,
+                                             int live, float sl2e, float& mrun, float& lrun, f32x4 (&o)[D / 16],
+                                             int lane) {
+  f32x4 acc[4];
+  if constexpr (sizeof(T) == 2)
+    qk_bf16<D, KP, 1>((const uint16_t*)kt0, (const uint16_t*)kt1, qf.b, acc, lane);
+  else
+    qk_f32<D>((const float*)kt0, qf.f, acc, lane);
+  const float alpha = online_softmax(acc, live, sl2e, mrun, lrun, lane);
+  rescale<D>(o, alpha);
+  if constexpr (sizeof(T) == 2)
+    pv_bf16<D>((const uint16_t*)vt, acc, o, lane);
+  else
+    pv_f32<D>((const float*)vt, acc, o, lane);
+}
+
+// Row indices (token ids) of a thread's share of one 64-row routed block,
+// fetched ahead of the rows themselves.
+template <typename T, int D>
+struct RowIdx {
+  static constexpr int PK = RowRegs<T, D>::PER;
+  static constexpr int PV = sizeof(T) == 2 ? VtRegs<D>::RPT : RowRegs<T, D>::PER;
+  int ik[PK], iv[PV];
+  __device__ __forceinline__ void load(const int32_t* Ie, int k, int kb, int tid) {
+    constexpr int CPR = RowRegs<T, D>::CPR;
+#pragma unroll
+    for (int u = 0; u < PK; ++u) ik[u] = Ie[min(kb + (tid + 256 * u) / CPR, k - 1)];
+#pragma unroll
+    for (int u = 0; u < PV; ++u) {
+      const int r = sizeof(T) == 2 ? (tid / VtRegs<D>::CPR) * VtRegs<D>::RPT + u : (tid + 256 * u) / CPR;
+      iv[u] = Ie[min(kb + r, k - 1)];
+    }
+  }
+};
+
+// Rows of a routed block from already-fetched indices (rows r >= live are zero).
+template <typename T, int D>
+__device__ __forceinline__ void load_rows(KVRegs<T, D, 1>& R, const RowIdx<T, D>& ix, const T* Kz, const T* Vz,
+                                          int live, int tid) {
+  using RK = RowRegs<T, D>;
+#pragma unroll
+  for (int u = 0; u < RK::PER; ++u) {
+    const int c = tid + 256 * u, r = c / RK::CPR, cc = (c % RK::CPR) * RK::EPC;
+    const uint4 x = *(const uint4*)(Kz + (size_t)ix.ik[u] * D + cc);
+    R.k[0].v[u] = r < live ? x : make_uint4(0, 0, 0, 0);
+  }
+  if constexpr (sizeof(T) == 2) {
+    using VR = VtRegs<D>;
+    const int kg = tid / VR::CPR, cc = (tid % VR::CPR) * 8;
+#pragma unroll
+    for (int u = 0; u < VR::RPT; ++u) {
+      const uint4 x = *(const uint4*)(Vz + (size_t)ix.iv[u] * D + cc);
+      R.v.v[u] = kg * VR::RPT + u < live ? x : make_uint4(0, 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < RK::PER; ++u) {
+      const int c = tid + 256 * u, r = c / RK::CPR, cc = (c % RK::CPR) * RK::EPC;
+      const uint4 x = *(const uint4*)(Vz + (size_t)ix.iv[u] * D + cc);
+      R.v.v[u] = r < live ? x : make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+// Persistent expert-grouped attention. Workgroup b walks the tile-table entries
+// [b C, (b + 1) C) (slice-major, so consecutive tiles mostly share a slice):
+// it lists the real tiles in LDS and streams their 64-key routed blocks
+// (block j = tile j / B, keys 64 (j % B), B = ceil(k / 64)). While block j
+// computes, the rows of block j + 1 (their indices already in registers) and the
+// indices of block j + 2 are in flight, so no prefetch waits on a dependent
+// load. With s = 1 each tile also attends the slice's landmark pairs, kept
+// resident in LDS while the slice does not change.
 template <typename T, int D, bool FUSED>
 __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                      const T* __restrict__ V, const int32_t* __restrict__ I,
@@ -209,60 +305,141 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ Q, co
                                                      const void* __restrict__ qtop, const void* __restrict__ vtop,
                                                      T* __restrict__ out, float* __restrict__ pacc,
                                                      float* __restrict__ pml, int N, int m, int k, int s,
-                                                     int max_tiles, float sl2e) {
+                                                     int max_tiles, long total, int chunk, float sl2e) {
   using TL = Tiles<T, D>;
   constexpr bool BF = TL::BF;
-  __shared__ AttnLds<T, D> sm;
-  const int t = blockIdx.x, z = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15,
-            g = lane >> 4;
-  const int4 te = tiles[(size_t)z * max_tiles + t];   // (expert, first row, rows, perm offset)
-  const int e = te.x;
-  if (e < 0) return;
-  const int32_t* Ie = I + ((size_t)z * m + e) * k;
-  const T* Kz = K + (size_t)z * N * D;
-  const T* Vz = V + (size_t)z * N * D;
-  // first wave of loads: the query ids, the first landmark block, the first routed block
+  constexpr int KP = BF ? 2 : 1;
+  __shared__ GatherLds<T, D, FUSED> sm;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
   const int rowi = 16 * w + r;
-  const bool ok = rowi < te.z;
-  const int entry = perm[(size_t)z * N * s + te.w + min(rowi, te.z - 1)];
-  KVRegs<T, D, BF ? 2 : 1> LR;
-  if constexpr (FUSED) load_landmarks<T, D>(LR, qtop, vtop, z, m, 0, tid);
-  KVRegs<T, D, 1> RR;
-  load_routed<T, D>(RR, Kz, Vz, Ie, k, 0, tid);
-  const int q = entry / s, slot = entry % s;
-  QFrag<T, D> qf;
-  qf.load(Q + ((size_t)z * N + q) * D, g);
+  const long c0 = (long)blockIdx.x * chunk, c1 = min(total, c0 + chunk);
+  const bool resident = FUSED && m <= kKeyBlock;
+  const int B = (k + kKeyBlock - 1) / kKeyBlock;
 
-  float mrun = -INFINITY, lrun = 0.f;
-  f32x4 o[D / 16];
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const bool wave_live = 16 * w < te.z;
-  if constexpr (FUSED) attend_landmarks<T, D>(sm, LR, qf, qtop, vtop, z, m, sl2e, mrun, lrun, o, tid, wave_live);
-
-  for (int kb = 0; kb < k; kb += kKeyBlock) {
-    RR.store(sm, tid);
+  for (long base = c0; base < c1; base += 256) {
+    // list the real tiles of this batch of entries
+    const long ent = base + tid;
+    const int4 te = ent < c1 ? tiles[ent] : make_int4(-1, 0, 0, 0);
+    const uint32_t f = te.x >= 0 ? 1u : 0u;
+    uint32_t nt;
+    const uint32_t pos = block_incl_scan(f, sm.wtot, nt) - f;
+    if (f) {
+      sm.tile[pos] = te;
+      sm.tz[pos] = (int)(ent / max_tiles);
+    }
     __syncthreads();
-    if (kb + kKeyBlock < k) load_routed<T, D>(RR, Kz, Vz, Ie, k, kb + kKeyBlock, tid);   // prefetch
-    attend_block<T, D, 1>(sm, qf, min(kKeyBlock, k - kb), sl2e, mrun, lrun, o, lane, wave_live);
-    __syncthreads();
-  }
+    if (nt == 0) continue;
+    const int nblk = (int)nt * B;
+    // block j -> (slice, expert index list, key offset); past the end: the last block
+    auto blk = [&](int j, int& zb, const int32_t*& Ieb, int& kbb) {
+      j = min(j, nblk - 1);
+      const int ti = j / B;
+      zb = sm.tz[ti];
+      Ieb = I + ((size_t)zb * m + sm.tile[ti].x) * k;
+      kbb = (j % B) * kKeyBlock;
+    };
 
-  const float l = quad_sum(lrun);
-  if (!ok) return;
-  if constexpr (FUSED) {
-    T* orow = out + ((size_t)z * N + q) * D;
-    const float inv = 1.f / l;
+    // prologue: rows of block 0, indices of block 1, query ids and rows of tile 0
+    RowIdx<T, D> ix;
+    KVRegs<T, D, 1> RR;
+    {
+      int zb, kbb;
+      const int32_t* Ieb;
+      blk(0, zb, Ieb, kbb);
+      ix.load(Ieb, k, kbb, tid);
+      load_rows<T, D>(RR, ix, K + (size_t)zb * N * D, V + (size_t)zb * N * D, min(kKeyBlock, k - kbb), tid);
+      blk(1, zb, Ieb, kbb);
+      ix.load(Ieb, k, kbb, tid);
+    }
+    int4 cur = sm.tile[0];
+    int zc = sm.tz[0], zl = -1;
+    int entry = perm[(size_t)zc * N * s + cur.w + min(rowi, cur.z - 1)];
+    QFrag<T, D> qf;
+    qf.load(Q + ((size_t)zc * N + entry / s) * D, g);
+    int entry_n = entry;
+    QFrag<T, D> qf_n = qf;
+    float mrun = -INFINITY, lrun = 0.f;
+    f32x4 o[D / 16];
+
+    for (int j = 0; j < nblk; ++j) {
+      const int ti = j / B, kb = (j % B) * kKeyBlock;
+      if (kb == 0) {   // a new tile (block-uniform)
+        if (j > 0) {
+          cur = sm.tile[ti];
+          zc = sm.tz[ti];
+          entry = entry_n;
+          qf = qf_n;
+        }
+        const int tn = min(ti + 1, (int)nt - 1);   // query ids of the next tile
+        const int4 nx = sm.tile[tn];
+        entry_n = perm[(size_t)sm.tz[tn] * N * s + nx.w + min(rowi, nx.z - 1)];
+        mrun = -INFINITY;
+        lrun = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-      store4<T>(orow + 16 * dt + 4 * g, o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
-  } else {
-    const size_t ps = ((size_t)z * N + q) * s + slot;
-    float* prow = pacc + ps * D;
+        for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (FUSED) {
+          const bool wl = 16 * w < cur.z;
+          if (resident) {
+            if (zc != zl) {   // the slice's landmark block, staged once (uniform branch)
+              KVRegs<T, D, KP> LR;
+              load_landmarks<T, D>(LR, qtop, vtop, zc, m, 0, tid);
+              LR.store(sm.lm, tid);
+              zl = zc;
+            }
+            __syncthreads();
+            if (wl) attend_tiles<T, D, KP>(sm.lm.k0, sm.lm.k1, sm.lm.v, qf, m, sl2e, mrun, lrun, o, lane);
+          } else {
+            for (int lb0 = 0; lb0 < m; lb0 += kKeyBlock) {
+              KVRegs<T, D, KP> LR;
+              load_landmarks<T, D>(LR, qtop, vtop, zc, m, lb0, tid);
+              __syncthreads();
+              LR.store(sm.lm, tid);
+              __syncthreads();
+              if (wl) attend_tiles<T, D, KP>(sm.lm.k0, sm.lm.k1, sm.lm.v, qf, min(kKeyBlock, m - lb0), sl2e, mrun,
+                                             lrun, o, lane);
+            }
+          }
+        }
+      }
+      __syncthreads();   // earlier readers of the routed tile are done
+      RR.k[0].store(sm.rk, TL::KSTR, tid);
+      if constexpr (BF) RR.v.store((uint16_t*)sm.rv, tid); else RR.v.store(sm.rv, TL::VSTR, tid);
+      __syncthreads();
+      {   // rows of block j + 1 (indices in hand), indices of block j + 2; never branch
+        int zb, kbb;
+        const int32_t* Ieb;
+        blk(j + 1, zb, Ieb, kbb);
+        load_rows<T, D>(RR, ix, K + (size_t)zb * N * D, V + (size_t)zb * N * D, min(kKeyBlock, k - kbb), tid);
+        blk(j + 2, zb, Ieb, kbb);
+        ix.load(Ieb, k, kbb, tid);
+        const int tn = min(ti + 1, (int)nt - 1);
+        qf_n.load(Q + ((size_t)sm.tz[tn] * N + entry_n / s) * D, g);
+      }
+      const bool wave_live = 16 * w < cur.z;
+      if (wave_live) attend_tiles<T, D, 1>(sm.rk, nullptr, sm.rv, qf, min(kKeyBlock, k - kb), sl2e, mrun, lrun, o, lane);
+
+      if (kb + kKeyBlock >= k) {   // last block of the tile: write it out
+        const float l = quad_sum(lrun);
+        const int q = entry / s, slot = entry % s;
+        if (rowi < cur.z) {
+          if constexpr (FUSED) {
+            T* orow = out + ((size_t)zc * N + q) * D;
+            const float inv = 1.f / l;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-      *(float4*)(prow + 16 * dt + 4 * g) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
-    if (g == 0) *(float2*)(pml + ps * 2) = make_float2(mrun, l);
+            for (int dt = 0; dt < D / 16; ++dt)
+              store4<T>(orow + 16 * dt + 4 * g, o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+          } else {
+            const size_t ps = ((size_t)zc * N + q) * s + slot;
+            float* prow = pacc + ps * D;
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt)
+              *(float4*)(prow + 16 * dt + 4 * g) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+            if (g == 0) *(float2*)(pml + ps * 2) = make_float2(mrun, l);
+          }
+        }
+      }
+    }
+    __syncthreads();   // the tile list is rewritten by the next batch
   }
 }
 
@@ -342,18 +519,31 @@ static hipError_t gather_launch(const Plan& p, const void* Q, const void* K, con
 
   const float sl2e = (float)(1.4426950408889634 / sqrt((double)D));
   const void* vtop = p.dtype == MITA_BF16 ? (const void*)(ws + p.ws.vt16) : (const void*)(ws + p.ws.vt32);
-  const dim3 ggrid(p.max_tiles, p.BH);
+  static int n_cu = 0, occ_f = 0, occ_p = 0;
+  if (n_cu == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      n_cu = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_f, gather_kernel<T, D, true>, 256, 0) != hipSuccess) occ_f = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_p, gather_kernel<T, D, false>, 256, 0) != hipSuccess) occ_p = 1;
+  }
+  // persistent grid: one resident workgroup per slot, each walking a contiguous chunk
+  const long total = (long)p.max_tiles * p.BH;
+  const int slots = n_cu * std::max(1, p.s == 1 ? occ_f : occ_p);
+  const int groups = (int)std::min<long>(total, slots);
+  const int chunk = (int)((total + groups - 1) / groups);
+  const int grid = (int)((total + chunk - 1) / chunk);
   if (p.s == 1) {
-    hipLaunchKernelGGL((gather_kernel<T, D, true>), ggrid, dim3(256), 0, st, (const T*)Q, (const T*)K, (const T*)V,
+    hipLaunchKernelGGL((gather_kernel<T, D, true>), dim3(grid), dim3(256), 0, st, (const T*)Q, (const T*)K, (const T*)V,
                        (const int32_t*)(ws + p.ws.I), (const int4*)(ws + p.ws.tiles), (const int32_t*)(ws + p.ws.perm),
                        (const void*)(ws + p.ws.qtop), vtop, (T*)out, (float*)nullptr, (float*)nullptr, p.N, p.m, p.k,
-                       p.s, p.max_tiles, sl2e);
+                       p.s, p.max_tiles, total, chunk, sl2e);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((gather_kernel<T, D, false>), ggrid, dim3(256), 0, st, (const T*)Q, (const T*)K, (const T*)V,
+  hipLaunchKernelGGL((gather_kernel<T, D, false>), dim3(grid), dim3(256), 0, st, (const T*)Q, (const T*)K, (const T*)V,
                      (const int32_t*)(ws + p.ws.I), (const int4*)(ws + p.ws.tiles), (const int32_t*)(ws + p.ws.perm),
                      (const void*)(ws + p.ws.qtop), vtop, (T*)out, (float*)(ws + p.ws.pacc), (float*)(ws + p.ws.pml),
-                     p.N, p.m, p.k, p.s, p.max_tiles, sl2e);
+                     p.N, p.m, p.k, p.s, p.max_tiles, total, chunk, sl2e);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((combine_kernel<T, D>), dim3(p.qtiles, p.BH), dim3(256), 0, st, (const T*)Q,
                      (const void*)(ws + p.ws.qtop), vtop, (const float*)(ws + p.ws.pacc), (const float*)(ws + p.ws.pml),

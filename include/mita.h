@@ -103,13 +103,14 @@ mita_status mita_topk(const void* K, int m, int k, int s, const mita_shape* shap
 
 /* Step 4 (routing). E_out: int32 [B, H, N, s], the routed landmarks of each
  * query, ordered by decreasing score. The set is exact in the same sense as
- * step 3; the order among the s entries follows the fp32 scores. */
+ * step 3; the order among the s entries follows the fp32 scores. Also groups
+ * the (query, expert) pairs by expert (a counting sort) for step 5. */
 mita_status mita_route(const void* Q, int m, int k, int s, const mita_shape* shape, void* workspace,
                        size_t workspace_bytes, int32_t* E_out, void* stream);
 
-/* Step 5 (output): buckets the (query, expert) pairs by expert, runs attention of
- * each bucket over its expert's gathered keys and the shared expert, and merges
- * the s + 1 partial softmaxes of each query into out. */
+/* Step 5 (output): runs attention of each expert's bucket of queries over the
+ * expert's gathered keys (and, for s = 1, the shared expert), and merges the
+ * s + 1 partial softmaxes of each query into out. */
 mita_status mita_gather(const void* Q, const void* K, const void* V, int m, int k, int s, void* out,
                         const mita_shape* shape, void* workspace, size_t workspace_bytes, void* stream);
 

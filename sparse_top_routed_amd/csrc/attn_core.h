@@ -69,7 +69,10 @@ __device__ __forceinline__ void stage_vt_bf16(uint16_t* Vt, RowFn rowptr, int nv
 }
 
 // A thread's share of one 64-row block, held in registers so the loads can be
-// issued early (prefetch) and written to LDS later.
+// issued early (prefetch) and written to LDS later. Rows r >= nvalid repeat row
+// nvalid - 1 (a real row, so finite): every consumer masks those keys out of
+// the softmax. Zeroing them with a select after the load would let the compiler
+// turn the load into a branch that waits for it, which defeats the prefetch.
 template <typename T, int D>
 struct RowRegs {
   static constexpr int EPC = 16 / sizeof(T), CPR = D / EPC, PER = kKeyBlock * CPR / 256;
@@ -79,8 +82,7 @@ struct RowRegs {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int c = tid + 256 * u, r = c / CPR, cc = (c % CPR) * EPC;
-      const uint4 x = *(const uint4*)(rowptr(min(r, nvalid - 1)) + cc);   // unconditional: no branch, no wait
-      v[u] = r < nvalid ? x : make_uint4(0, 0, 0, 0);
+      v[u] = ld16(rowptr(min(r, nvalid - 1)) + cc);
     }
   }
   __device__ __forceinline__ void store(T* dst, int stride, int tid) const {
@@ -105,8 +107,7 @@ struct VtRegs {
 #pragma unroll
     for (int u = 0; u < RPT; ++u) {
       const int r = kg * RPT + u;
-      const uint4 x = *(const uint4*)(rowptr(min(r, nvalid - 1)) + cc);
-      v[u] = r < nvalid ? x : make_uint4(0, 0, 0, 0);
+      v[u] = ld16(rowptr(min(r, nvalid - 1)) + cc);
     }
   }
   __device__ __forceinline__ void store(uint16_t* Vt, int tid) const {

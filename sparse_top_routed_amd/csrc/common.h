@@ -7,6 +7,14 @@ namespace mita {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte global load as one vector value (a uint4 aggregate copy can end up
+// as a memcpy into a stack slot).
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  const u32x4 x = *(const u32x4*)p;
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
 
 constexpr int WAVE = 64;
 

@@ -496,9 +496,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Q, c
     store4<T>(orow + 16 * dt + 4 * g, o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
 }
 
-template <typename T, int D>
-static hipError_t gather_launch(const Plan& p, const void* Q, const void* K, const void* V, void* out, char* ws,
-                                hipStream_t st) {
+// Counting sort of the (query, slot) pairs by expert and the tile table.
+hipError_t launch_bucket(const Plan& p, char* ws, hipStream_t st) {
   const int Ns = p.N * p.s;
   const int nclear = (int)((p.ws.bcursor + (size_t)p.BH * p.m * 4 - p.ws.bcount) / 4);
   hipLaunchKernelGGL(clear_kernel, dim3(std::min(1024, (nclear + 255) / 256)), dim3(256), 0, st,
@@ -516,7 +515,13 @@ static hipError_t gather_launch(const Plan& p, const void* Q, const void* K, con
                      (const uint32_t*)(ws + p.ws.boff), (uint32_t*)(ws + p.ws.bcursor), (int32_t*)(ws + p.ws.perm), Ns,
                      p.m);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  return hipSuccess;
+}
 
+template <typename T, int D>
+static hipError_t gather_launch(const Plan& p, const void* Q, const void* K, const void* V, void* out, char* ws,
+                                hipStream_t st) {
+  hipError_t e = hipSuccess;
   const float sl2e = (float)(1.4426950408889634 / sqrt((double)D));
   const void* vtop = p.dtype == MITA_BF16 ? (const void*)(ws + p.ws.vt16) : (const void*)(ws + p.ws.vt32);
   static int n_cu = 0, occ_f = 0, occ_p = 0;

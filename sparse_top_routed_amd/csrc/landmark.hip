@@ -4,12 +4,16 @@
 // the deformable experts, so one pass produces both).
 //
 // Flash-style: a workgroup takes 64 landmarks (16 per wave) and one chunk of
-// keys, streams the chunk through LDS 64 keys at a time, writes the unscaled
-// scores, and keeps an online softmax. Chunks are merged by a second kernel.
+// keys, streams the chunk through LDS 64 keys at a time (the next block is
+// fetched into registers while the current one computes), writes the unscaled
+// scores, and keeps an online softmax. A second kernel merges the chunks'
+// partial softmaxes into V~.
 // bf16 inputs: Q~ enters the MFMA as two bf16 parts (hi + lo) so the scores
 // carry ~16 more bits than a bf16 Q~ would; fp32 inputs use the fp32 MFMA.
 // The workgroups of landmark tile 0 also record max_n |K_n|_2 per chunk, which
 // bounds the score error for the exact top-k of step 3.
+#include <type_traits>
+
 #include "attn_core.h"
 
 namespace mita {
@@ -33,6 +37,11 @@ __global__ __launch_bounds__(256) void landmark_kernel(const T* __restrict__ K, 
   const T* Kz = K + (size_t)z * N * D;
   const T* Vz = V + (size_t)z * N * D;
 
+  // first key/value block into registers, then the landmark fragments
+  RowRegs<T, D> KR;
+  std::conditional_t<BF, VtRegs<D>, RowRegs<T, D>> VR;
+  KR.load([&](int rr) { return Kz + (size_t)(k0 + rr) * D; }, min(kKeyBlock, k1 - k0), tid);
+  VR.load([&](int rr) { return Vz + (size_t)(k0 + rr) * D; }, min(kKeyBlock, k1 - k0), tid);
   uint4 qb[2][D / 32];
   float qf[D / 4];
   if constexpr (BF) {
@@ -52,19 +61,21 @@ __global__ __launch_bounds__(256) void landmark_kernel(const T* __restrict__ K, 
   f32x4 o[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float* Srow = S + ((size_t)z * m + (lm_ok ? lm : 0)) * N;
+  float* Srow = S + ((size_t)z * m + lmc) * N;
   const bool vec_store = (N & 3) == 0;
+  const int last_kb = k0 + ((k1 - k0 - 1) / kKeyBlock) * kKeyBlock;
 
   for (int kb = k0; kb < k1; kb += kKeyBlock) {
     const int nvalid = min(kKeyBlock, k1 - kb);
-    auto krow = [&](int rr) { return Kz + (size_t)(kb + rr) * D; };
-    auto vrow = [&](int rr) { return Vz + (size_t)(kb + rr) * D; };
-    stage_rows<T, D>(Ks, TL::KSTR, krow, nvalid, tid);
-    if constexpr (BF)
-      stage_vt_bf16<D>((uint16_t*)Vs, vrow, nvalid, tid);
-    else
-      stage_rows<T, D>(Vs, TL::VSTR, vrow, nvalid, tid);
+    KR.store(Ks, TL::KSTR, tid);
+    if constexpr (BF) VR.store((uint16_t*)Vs, tid); else VR.store(Vs, TL::VSTR, tid);
     __syncthreads();
+    {   // prefetch the next block (the last block again at the end: no branch)
+      const int nb = min(kb + kKeyBlock, last_kb);
+      const int nv = min(kKeyBlock, k1 - nb);
+      KR.load([&](int rr) { return Kz + (size_t)(nb + rr) * D; }, nv, tid);
+      VR.load([&](int rr) { return Vz + (size_t)(nb + rr) * D; }, nv, tid);
+    }
 
     if (lt == 0) {  // squared norms of the staged keys: 4 threads per row
       const int row = tid >> 2, part = tid & 3;
@@ -118,44 +129,58 @@ __global__ __launch_bounds__(256) void landmark_kernel(const T* __restrict__ K, 
       kmax[(size_t)z * nsplit + c] = sqrtf(mx) * 1.0001f + 1e-30f;
     }
   }
+  // partial softmax of this chunk: [max, sum, pad, pad, acc[D]] per landmark
   lrun = quad_sum(lrun);
   if (lm_ok) {
-    float* P = lpart + (((size_t)z * m + lm) * nsplit + c) * (D + 2);
-    if (g == 0) {
-      P[0] = mrun;
-      P[1] = lrun;
-    }
+    float* P = lpart + (((size_t)z * m + lm) * nsplit + c) * (D + 4);
+    if (g == 0) *(float2*)P = make_float2(mrun, lrun);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) P[2 + 16 * dt + 4 * g + j] = o[dt][j];
+      *(float4*)(P + 4 + 16 * dt + 4 * g) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
   }
 }
 
-// Merge the per-chunk partial softmaxes of each landmark: one wave per row.
+// Merge the chunks' partial softmaxes of each landmark into V~: four threads
+// per landmark, d/4 columns each. (A "last chunk merges" scheme inside the
+// kernel above would need device-scope fences, which write back the L2 of the
+// XCD for every workgroup: far dearer than this launch.)
 template <int D>
 __global__ __launch_bounds__(256) void landmark_merge_kernel(const float* __restrict__ lpart, float* __restrict__ vt32,
                                                              uint16_t* __restrict__ vt16, int rows, int nsplit) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  constexpr int CW = D / 4;
+  const int t = blockIdx.x * 256 + threadIdx.x, row = t >> 2, col = (t & 3) * CW;
   if (row >= rows) return;
-  const float* P = lpart + (size_t)row * nsplit * (D + 2);
+  const float* Pr = lpart + (size_t)row * nsplit * (D + 4);
   float M = -INFINITY;
-  for (int c = 0; c < nsplit; ++c) M = fmaxf(M, P[(size_t)c * (D + 2)]);
-  float L = 0.f, acc[D / 64];
+#pragma unroll 4
+  for (int cc = 0; cc < nsplit; ++cc) M = fmaxf(M, Pr[(size_t)cc * (D + 4)]);
+  float L = 0.f;
+  float4 av[CW / 4];
 #pragma unroll
-  for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
-  for (int c = 0; c < nsplit; ++c) {
-    const float* Pc = P + (size_t)c * (D + 2);
-    const float f = exp2f(Pc[0] - M);
-    L += f * Pc[1];
+  for (int e = 0; e < CW / 4; ++e) av[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 2
+  for (int cc = 0; cc < nsplit; ++cc) {
+    const float* Pc = Pr + (size_t)cc * (D + 4);
+    const float2 ml = *(const float2*)Pc;
+    const float f = __builtin_amdgcn_exp2f(ml.x - M);
+    L = fmaf(f, ml.y, L);
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) acc[e] += f * Pc[2 + lane + 64 * e];
+    for (int e = 0; e < CW / 4; ++e) {
+      const float4 x = *(const float4*)(Pc + 4 + col + 4 * e);
+      av[e].x = fmaf(f, x.x, av[e].x);
+      av[e].y = fmaf(f, x.y, av[e].y);
+      av[e].z = fmaf(f, x.z, av[e].z);
+      av[e].w = fmaf(f, x.w, av[e].w);
+    }
   }
+  const float inv = 1.f / L;
+  float* o32 = vt32 + (size_t)row * D + col;
+  uint16_t* o16 = vt16 + (size_t)row * D + col;
 #pragma unroll
-  for (int e = 0; e < D / 64; ++e) {
-    const float v = acc[e] / L;
-    vt32[(size_t)row * D + lane + 64 * e] = v;
-    vt16[(size_t)row * D + lane + 64 * e] = f32_to_bf16(v);
+  for (int e = 0; e < CW / 4; ++e) {
+    const float4 v = make_float4(av[e].x * inv, av[e].y * inv, av[e].z * inv, av[e].w * inv);
+    *(float4*)(o32 + 4 * e) = v;
+    *(uint2*)(o16 + 4 * e) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
   }
 }
 
@@ -169,7 +194,7 @@ static hipError_t landmark_launch(const Plan& p, const void* K, const void* V, c
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rows = p.BH * p.m;
-  hipLaunchKernelGGL((landmark_merge_kernel<D>), dim3((rows + 3) / 4), dim3(256), 0, st,
+  hipLaunchKernelGGL((landmark_merge_kernel<D>), dim3((rows * 4 + 255) / 256), dim3(256), 0, st,
                      (const float*)(ws + p.ws.lpart), (float*)(ws + p.ws.vt32), (uint16_t*)(ws + p.ws.vt16), rows,
                      p.nsplit);
   return hipGetLastError();

@@ -85,7 +85,7 @@ mita_status make_plan(const mita_shape* shape, int m, int k, int s, Plan* p, con
   L.qt64 = take(bh * m * d * 8);
   L.qtop = take(bh * m * d * 4);
   L.qtnorm = take(bh * m * 4);
-  L.lpart = take(bh * m * P.nsplit * (d + 2) * 4);
+  L.lpart = take(bh * m * P.nsplit * (d + 4) * 4);
   L.kmax = take(bh * P.nsplit * 4);
   L.vt32 = take(bh * m * d * 4);
   L.vt16 = take(bh * m * d * 2);
@@ -222,6 +222,7 @@ mita_status mita_route(const void* Q, int m, int k, int s, const mita_shape* sha
   char* ws = (char*)workspace;
   if ((st = hip_status(launch_clear(P, ws, hs), "clear")) != MITA_OK) return st;
   if ((st = hip_status(launch_route(P, Q, ws, hs), "route")) != MITA_OK) return st;
+  if ((st = hip_status(launch_bucket(P, ws, hs), "bucket")) != MITA_OK) return st;
   return copy_out(E_out, ws + P.ws.E, (size_t)P.BH * P.N * s * 4, hs, "route copy-out");
 }
 
@@ -251,6 +252,7 @@ mita_status mita_forward(const void* Q, const void* K, const void* V, int m, int
   if ((st = hip_status(launch_topk(P, K, ws, hs), "topk")) != MITA_OK) return st;
   if ((st = hip_status(launch_clear(P, ws, hs), "clear")) != MITA_OK) return st;
   if ((st = hip_status(launch_route(P, Q, ws, hs), "route")) != MITA_OK) return st;
+  if ((st = hip_status(launch_bucket(P, ws, hs), "bucket")) != MITA_OK) return st;
   return hip_status(launch_gather(P, Q, K, V, out, ws, hs), "gather");
 }
 

@@ -22,7 +22,7 @@ struct Layout {
   size_t qt64;      // f64 [BH, m, d]     landmark queries
   size_t qtop;      // bf16 [BH, 2, m, d] hi/lo split of Q~ (bf16 path) or f32 [BH, m, d]
   size_t qtnorm;    // f32 [BH, m]        upper bound of |q~_i|_2
-  size_t lpart;     // f32 [BH, m, nsplit, d + 2]  per-chunk (max, sum, acc) of the shared expert
+  size_t lpart;     // f32 [BH, m, nsplit, d + 4]  per-chunk (max, sum, pad, pad, acc) of the shared expert
   size_t kmax;      // f32 [BH, nsplit]   upper bound of max_n |K_n|_2 per key chunk
   size_t vt32;      // f32 [BH, m, d]     shared expert V~
   size_t vt16;      // bf16 [BH, m, d]    V~ rounded to bf16 (MFMA operand)
@@ -75,6 +75,7 @@ hipError_t launch_pool(const Plan& p, const void* Q, char* ws, hipStream_t st);
 hipError_t launch_landmark(const Plan& p, const void* K, const void* V, char* ws, hipStream_t st);
 hipError_t launch_topk(const Plan& p, const void* K, char* ws, hipStream_t st);
 hipError_t launch_route(const Plan& p, const void* Q, char* ws, hipStream_t st);
+hipError_t launch_bucket(const Plan& p, char* ws, hipStream_t st);
 hipError_t launch_gather(const Plan& p, const void* Q, const void* K, const void* V, void* out, char* ws,
                          hipStream_t st);
 

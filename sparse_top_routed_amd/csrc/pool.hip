@@ -17,8 +17,9 @@ namespace mita {
 // flight, and the row groups are summed with shuffles.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ Q, double* __restrict__ qt64,
-                                                   void* __restrict__ qtop, float* __restrict__ qtnorm, int N,
-                                                   int m, int grid_h, int grid_w, int pool_h, int pool_w) {
+                                                   void* __restrict__ qtop, float* __restrict__ qtnorm,
+                                                   int N, int m,
+                                                   int grid_h, int grid_w, int pool_h, int pool_w) {
   constexpr int TPR = D / 8;          // lanes per row, 8 elements each
   constexpr int RPW = WAVE / TPR;     // rows per wave step
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6), z = blockIdx.y, lane = threadIdx.x & 63;
@@ -103,8 +104,7 @@ template <typename T, int D>
 static hipError_t pool_launch(const Plan& p, const void* Q, char* ws, hipStream_t st) {
   dim3 grid((p.m + 3) / 4, p.BH);
   hipLaunchKernelGGL((pool_kernel<T, D>), grid, dim3(256), 0, st, (const T*)Q, (double*)(ws + p.ws.qt64),
-                     (void*)(ws + p.ws.qtop), (float*)(ws + p.ws.qtnorm), p.N, p.m, p.grid_h, p.grid_w, p.pool_h,
-                     p.pool_w);
+                     (void*)(ws + p.ws.qtop), (float*)(ws + p.ws.qtnorm), p.N, p.m, p.grid_h, p.grid_w, p.pool_h, p.pool_w);
   return hipGetLastError();
 }
 

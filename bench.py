@@ -41,6 +41,55 @@ def step_bytes(w) -> dict:
     }
 
 
+# Kernel sources each step's dominant kernel is built from: a stored traffic
+# figure is only reported while these files are byte-identical to the ones it
+# was measured on.
+KERNEL_SOURCES = {
+    "gather": ["sparse_top_routed_amd/csrc/gather.hip", "sparse_top_routed_amd/csrc/attn_core.h"],
+    "topk": ["sparse_top_routed_amd/csrc/topk.hip"],
+    "route": ["sparse_top_routed_amd/csrc/route.hip", "sparse_top_routed_amd/csrc/attn_core.h"],
+    "landmark": ["sparse_top_routed_amd/csrc/landmark.hip", "sparse_top_routed_amd/csrc/attn_core.h"],
+    "pool": ["sparse_top_routed_amd/csrc/pool.hip"],
+}
+COMMON_SOURCES = ["sparse_top_routed_amd/csrc/common.h", "sparse_top_routed_amd/csrc/plan.h",
+                  "sparse_top_routed_amd/build.py"]
+KERNEL_NAMES = {
+    "gather": "gather_kernel", "topk": "topk_wave_kernel", "route": "route_fast_kernel",
+    "landmark": "landmark_kernel", "pool": "pool_kernel",
+}
+
+
+def sources_sha256(step: str) -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[step] + COMMON_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(step: str, workload: str):
+    """HBM bytes per launch of the step's dominant kernel, from the rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary under profiles/, or None when there is none
+    or the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAMES[step]}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ": " in line:
+                key, val = line[2:].split(": ", 1)
+                vals[key.strip()] = val.strip().strip("`")
+    if vals.get("source_sha256") != sources_sha256(step):
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(w, Q, K, V, budget_s: float = 12.0) -> dict:
     import numpy as np
     from threadpoolctl import threadpool_limits
@@ -70,7 +119,15 @@ def main() -> int:
     ap.add_argument("--workload", default="vit_b")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--breakdown", action="store_true", help="print per-step times to stderr")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run 3 elementwise copies of 512 MiB (read and write 2^29 bytes each), the "
+                         "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
+    ap.add_argument("--print-sha", action="store_true", help="print the dominant kernels' source hashes and exit")
     a = ap.parse_args()
+    if a.print_sha:
+        for step in KERNEL_SOURCES:
+            print(step, KERNEL_NAMES[step], sources_sha256(step))
+        return 0
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the MiTA forward here runs on a single MI355X "
               "(no sharding, no collectives); run it with --gpus 1", file=sys.stderr)
@@ -133,7 +190,14 @@ def main() -> int:
         for n in names:
             print(f"{n:9s} {per[n] * 1e3:9.1f} us  {nbytes[n] / (per[n] * 1e-3) / 1e9:8.1f} GB/s (algorithmic)",
                   file=sys.stderr)
-        print(f"forward  {ms * 1e3:9.1f} us  wall {wall / a.steps * 1e3:9.1f} us", file=sys.stderr)
+        print(f"forward  {ms * 1e3:9.1f} us  wall {wall / a.steps * 1e6:9.1f} us", file=sys.stderr)
+    if a.copy_calibration:
+        src = torch.ones(1 << 27, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     res = {
         "metric": METRIC, "value": tokens / (ms * 1e-3), "unit": "query-tokens/s", "n_gpus": 1,
@@ -141,8 +205,9 @@ def main() -> int:
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "m": w.m, "k": w.k, "s": w.s,
                    "grid": [w.grid_h, w.grid_w], "pool": [w.pool_h, w.pool_w]},
-        "roofline": {"bound": "hbm", "kernel": f"{dom} step", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "roofline": {"bound": "hbm", "kernel": KERNEL_NAMES[dom], "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": stored_traffic(dom, w.name), "algorithmic_bytes": nbytes[dom]},
         "step_ms": per,
     }
     if not a.no_cpu:

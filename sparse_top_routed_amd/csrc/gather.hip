@@ -104,7 +104,7 @@ struct QFrag {
   __device__ __forceinline__ void load(const T* qrow, int g) {
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) b[0][ks] = *(const uint4*)(qrow + 32 * ks + 8 * g);
+      for (int ks = 0; ks < D / 32; ++ks) b[0][ks] = ld16(qrow + 32 * ks + 8 * g);
     } else {
 #pragma unroll
       for (int ks = 0; ks < D / 4; ++ks) f[ks] = qrow[4 * ks + g];
@@ -261,31 +261,30 @@ struct RowIdx {
   }
 };
 
-// Rows of a routed block from already-fetched indices (rows r >= live are zero).
+// Rows of a routed block from already-fetched indices. The indices are clamped
+// to the expert's last token, so rows past the block's end repeat a real row;
+// the softmax masks those keys. (No select after the load: the compiler would
+// turn it into a branch, and the registers it leaves pending force a full wait
+// further on.)
 template <typename T, int D>
 __device__ __forceinline__ void load_rows(KVRegs<T, D, 1>& R, const RowIdx<T, D>& ix, const T* Kz, const T* Vz,
-                                          int live, int tid) {
+                                          int tid) {
   using RK = RowRegs<T, D>;
 #pragma unroll
   for (int u = 0; u < RK::PER; ++u) {
-    const int c = tid + 256 * u, r = c / RK::CPR, cc = (c % RK::CPR) * RK::EPC;
-    const uint4 x = *(const uint4*)(Kz + (size_t)ix.ik[u] * D + cc);
-    R.k[0].v[u] = r < live ? x : make_uint4(0, 0, 0, 0);
+    const int c = tid + 256 * u, cc = (c % RK::CPR) * RK::EPC;
+    R.k[0].v[u] = ld16(Kz + (size_t)ix.ik[u] * D + cc);
   }
   if constexpr (sizeof(T) == 2) {
     using VR = VtRegs<D>;
-    const int kg = tid / VR::CPR, cc = (tid % VR::CPR) * 8;
+    const int cc = (tid % VR::CPR) * 8;
 #pragma unroll
-    for (int u = 0; u < VR::RPT; ++u) {
-      const uint4 x = *(const uint4*)(Vz + (size_t)ix.iv[u] * D + cc);
-      R.v.v[u] = kg * VR::RPT + u < live ? x : make_uint4(0, 0, 0, 0);
-    }
+    for (int u = 0; u < VR::RPT; ++u) R.v.v[u] = ld16(Vz + (size_t)ix.iv[u] * D + cc);
   } else {
 #pragma unroll
     for (int u = 0; u < RK::PER; ++u) {
-      const int c = tid + 256 * u, r = c / RK::CPR, cc = (c % RK::CPR) * RK::EPC;
-      const uint4 x = *(const uint4*)(Vz + (size_t)ix.iv[u] * D + cc);
-      R.v.v[u] = r < live ? x : make_uint4(0, 0, 0, 0);
+      const int c = tid + 256 * u, cc = (c % RK::CPR) * RK::EPC;
+      R.v.v[u] = ld16(Vz + (size_t)ix.iv[u] * D + cc);
     }
   }
 }
@@ -347,47 +346,70 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ Q, co
       const int32_t* Ieb;
       blk(0, zb, Ieb, kbb);
       ix.load(Ieb, k, kbb, tid);
-      load_rows<T, D>(RR, ix, K + (size_t)zb * N * D, V + (size_t)zb * N * D, min(kKeyBlock, k - kbb), tid);
+      load_rows<T, D>(RR, ix, K + (size_t)zb * N * D, V + (size_t)zb * N * D, tid);
       blk(1, zb, Ieb, kbb);
       ix.load(Ieb, k, kbb, tid);
     }
+    // query ids: tile 0 and 1 now, tile t + 2 while tile t runs; query rows of
+    // tile t + 1 while tile t runs (their ids arrived a tile earlier)
+    auto qid = [&](int t) {
+      t = min(t, (int)nt - 1);
+      const int4 te = sm.tile[t];
+      return perm[(size_t)sm.tz[t] * N * s + te.w + min(rowi, te.z - 1)];
+    };
     int4 cur = sm.tile[0];
     int zc = sm.tz[0], zl = -1;
-    int entry = perm[(size_t)zc * N * s + cur.w + min(rowi, cur.z - 1)];
+    int entry = qid(0), entry_n = qid(1), entry_nn = entry_n;
     QFrag<T, D> qf;
     qf.load(Q + ((size_t)zc * N + entry / s) * D, g);
-    int entry_n = entry;
     QFrag<T, D> qf_n = qf;
     float mrun = -INFINITY, lrun = 0.f;
     f32x4 o[D / 16];
 
     for (int j = 0; j < nblk; ++j) {
       const int ti = j / B, kb = (j % B) * kKeyBlock;
-      if (kb == 0) {   // a new tile (block-uniform)
+      const bool newtile = kb == 0;   // block-uniform
+      if (newtile) {
         if (j > 0) {
           cur = sm.tile[ti];
           zc = sm.tz[ti];
           entry = entry_n;
+          entry_n = entry_nn;
           qf = qf_n;
         }
-        const int tn = min(ti + 1, (int)nt - 1);   // query ids of the next tile
-        const int4 nx = sm.tile[tn];
-        entry_n = perm[(size_t)sm.tz[tn] * N * s + nx.w + min(rowi, nx.z - 1)];
+        entry_nn = qid(ti + 2);
         mrun = -INFINITY;
         lrun = 0.f;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (FUSED) {
-          const bool wl = 16 * w < cur.z;
+      }
+      __syncthreads();   // earlier readers of the routed (and landmark) tiles are done
+      RR.k[0].store(sm.rk, TL::KSTR, tid);
+      if constexpr (BF) RR.v.store((uint16_t*)sm.rv, tid); else RR.v.store(sm.rv, TL::VSTR, tid);
+      if constexpr (FUSED) {
+        if (resident && newtile && zc != zl) {   // the slice's landmark block, staged once per slice
+          KVRegs<T, D, KP> LR;
+          load_landmarks<T, D>(LR, qtop, vtop, zc, m, 0, tid);
+          LR.store(sm.lm, tid);
+          zl = zc;
+        }
+      }
+      __syncthreads();
+      {   // rows of block j + 1 (indices in hand), indices of block j + 2, query rows of the next tile
+        int zb, kbb;
+        const int32_t* Ieb;
+        blk(j + 1, zb, Ieb, kbb);
+        load_rows<T, D>(RR, ix, K + (size_t)zb * N * D, V + (size_t)zb * N * D, tid);
+        blk(j + 2, zb, Ieb, kbb);
+        ix.load(Ieb, k, kbb, tid);
+        const int tn = min(ti + 1, (int)nt - 1);
+        qf_n.load(Q + ((size_t)sm.tz[tn] * N + entry_n / s) * D, g);
+      }
+      const bool wave_live = 16 * w < cur.z;
+      if constexpr (FUSED) {
+        if (newtile) {
           if (resident) {
-            if (zc != zl) {   // the slice's landmark block, staged once (uniform branch)
-              KVRegs<T, D, KP> LR;
-              load_landmarks<T, D>(LR, qtop, vtop, zc, m, 0, tid);
-              LR.store(sm.lm, tid);
-              zl = zc;
-            }
-            __syncthreads();
-            if (wl) attend_tiles<T, D, KP>(sm.lm.k0, sm.lm.k1, sm.lm.v, qf, m, sl2e, mrun, lrun, o, lane);
+            if (wave_live) attend_tiles<T, D, KP>(sm.lm.k0, sm.lm.k1, sm.lm.v, qf, m, sl2e, mrun, lrun, o, lane);
           } else {
             for (int lb0 = 0; lb0 < m; lb0 += kKeyBlock) {
               KVRegs<T, D, KP> LR;
@@ -395,27 +417,13 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ Q, co
               __syncthreads();
               LR.store(sm.lm, tid);
               __syncthreads();
-              if (wl) attend_tiles<T, D, KP>(sm.lm.k0, sm.lm.k1, sm.lm.v, qf, min(kKeyBlock, m - lb0), sl2e, mrun,
-                                             lrun, o, lane);
+              if (wave_live)
+                attend_tiles<T, D, KP>(sm.lm.k0, sm.lm.k1, sm.lm.v, qf, min(kKeyBlock, m - lb0), sl2e, mrun, lrun,
+                                       o, lane);
             }
           }
         }
       }
-      __syncthreads();   // earlier readers of the routed tile are done
-      RR.k[0].store(sm.rk, TL::KSTR, tid);
-      if constexpr (BF) RR.v.store((uint16_t*)sm.rv, tid); else RR.v.store(sm.rv, TL::VSTR, tid);
-      __syncthreads();
-      {   // rows of block j + 1 (indices in hand), indices of block j + 2; never branch
-        int zb, kbb;
-        const int32_t* Ieb;
-        blk(j + 1, zb, Ieb, kbb);
-        load_rows<T, D>(RR, ix, K + (size_t)zb * N * D, V + (size_t)zb * N * D, min(kKeyBlock, k - kbb), tid);
-        blk(j + 2, zb, Ieb, kbb);
-        ix.load(Ieb, k, kbb, tid);
-        const int tn = min(ti + 1, (int)nt - 1);
-        qf_n.load(Q + ((size_t)sm.tz[tn] * N + entry_n / s) * D, g);
-      }
-      const bool wave_live = 16 * w < cur.z;
       if (wave_live) attend_tiles<T, D, 1>(sm.rk, nullptr, sm.rv, qf, min(kKeyBlock, k - kb), sl2e, mrun, lrun, o, lane);
 
       if (kb + kKeyBlock >= k) {   // last block of the tile: write it out

@@ -20,6 +20,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the softmax reads every score tile, and
+    # accumulation registers would cost a copy instruction per element each way
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

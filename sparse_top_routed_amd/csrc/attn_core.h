@@ -39,35 +39,6 @@ __device__ __forceinline__ void stage_rows(T* dst, int stride, RowFn rowptr, int
   }
 }
 
-// Copy 64 bf16 rows into V^T [D][64 + pad]; rows r >= nvalid are zero.
-template <int D, typename RowFn>
-__device__ __forceinline__ void stage_vt_bf16(uint16_t* Vt, RowFn rowptr, int nvalid, int tid) {
-  constexpr int VSTR = Tiles<uint16_t, D>::VSTR, CPR = D / 8, TOTAL = (kKeyBlock / 4) * CPR;
-#pragma unroll
-  for (int c = tid; c < TOTAL; c += 256) {
-    const int kg = c / CPR, cc = (c % CPR) * 8;
-    uint4 v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = kg * 4 + u;
-      const uint4 x = *(const uint4*)(rowptr(min(r, nvalid - 1)) + cc);
-      v[u] = r < nvalid ? x : make_uint4(0, 0, 0, 0);
-    }
-    const uint32_t* w0 = (const uint32_t*)&v[0];
-    const uint32_t* w1 = (const uint32_t*)&v[1];
-    const uint32_t* w2 = (const uint32_t*)&v[2];
-    const uint32_t* w3 = (const uint32_t*)&v[3];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int sh = (e & 1) * 16, q = e >> 1;
-      uint2 out;
-      out.x = ((w0[q] >> sh) & 0xFFFFu) | (((w1[q] >> sh) & 0xFFFFu) << 16);
-      out.y = ((w2[q] >> sh) & 0xFFFFu) | (((w3[q] >> sh) & 0xFFFFu) << 16);
-      *(uint2*)(Vt + (cc + e) * VSTR + kg * 4) = out;
-    }
-  }
-}
-
 // A thread's share of one 64-row block, held in registers so the loads can be
 // issued early (prefetch) and written to LDS later. Rows r >= nvalid repeat row
 // nvalid - 1 (a real row, so finite): every consumer masks those keys out of
@@ -94,9 +65,19 @@ struct RowRegs {
   }
 };
 
-// Same for a bf16 V block that is written transposed (V^T [D][64 + pad]). Each
-// thread holds RPT consecutive rows of one 8-element column chunk, so the
-// transposed writes are RPT keys wide.
+// Slot of key quad qd (keys 4 qd .. 4 qd + 3) in row d of a bf16 V^T tile.
+// The XOR swizzle spreads both access patterns over distinct LDS banks: the
+// transposed writes (a wave covers d rows 8 apart) and the MFMA operand reads
+// (16 consecutive rows, one quad each).
+template <int D>
+__device__ __forceinline__ int vt_quad(int d, int qd) {
+  const int c = (d >> 3) & (D / 8 - 1);
+  return qd ^ (D == 64 ? ((c << 1) | (c & 1)) : c);
+}
+
+// Same for a bf16 V block that is written transposed (V^T [D][64 + pad], key
+// quads placed by vt_quad). Each thread holds RPT consecutive rows of one
+// 8-element column chunk, so the transposed writes are RPT keys wide.
 template <int D>
 struct VtRegs {
   static constexpr int CPR = D / 8, RPT = kKeyBlock * CPR / 256;   // 2 rows (d = 64) or 4 rows (d = 128)
@@ -115,14 +96,15 @@ struct VtRegs {
     const int kg = tid / CPR, cc = (tid % CPR) * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int sh = (e & 1) * 16, q = e >> 1;
-      uint32_t h[RPT];
-#pragma unroll
-      for (int u = 0; u < RPT; ++u) h[u] = (((const uint32_t*)&v[u])[q] >> sh) & 0xFFFFu;
+      // element e of each row: low halves (e even) or high halves (e odd) of word e / 2
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      const int q = e >> 1, d = cc + e;
+      const uint32_t w01 = __builtin_amdgcn_perm(((const uint32_t*)&v[1])[q], ((const uint32_t*)&v[0])[q], sel);
       if constexpr (RPT == 4) {
-        *(uint2*)(Vt + (cc + e) * VSTR + kg * 4) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        const uint32_t w23 = __builtin_amdgcn_perm(((const uint32_t*)&v[3])[q], ((const uint32_t*)&v[2])[q], sel);
+        *(uint2*)(Vt + d * VSTR + 4 * vt_quad<D>(d, kg)) = make_uint2(w01, w23);
       } else {
-        *(uint32_t*)(Vt + (cc + e) * VSTR + kg * 2) = h[0] | (h[1] << 16);
+        *(uint32_t*)(Vt + d * VSTR + 4 * vt_quad<D>(d, kg >> 1) + 2 * (kg & 1)) = w01;
       }
     }
   }
@@ -227,8 +209,10 @@ __device__ __forceinline__ void pv_bf16(const uint16_t* Vt, const f32x4 (&p)[4],
     b.w = pack_bf16x2(p[2 * h + 1][2], p[2 * h + 1][3]);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const uint16_t* row = Vt + (16 * dt + r) * VSTR + 32 * h + 4 * g;
-      const uint2 lo = *(const uint2*)row, hi = *(const uint2*)(row + 16);
+      const int d = 16 * dt + r;
+      const uint16_t* row = Vt + d * VSTR;
+      const uint2 lo = *(const uint2*)(row + 4 * vt_quad<D>(d, 8 * h + g));
+      const uint2 hi = *(const uint2*)(row + 4 * vt_quad<D>(d, 8 * h + 4 + g));
       o[dt] = mma_bf16(make_uint4(lo.x, lo.y, hi.x, hi.y), b, o[dt]);
     }
   }

@@ -451,6 +451,156 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ Q, co
   }
 }
 
+// Scores of one staged 64-key block against the wave's 16 queries (S^T tile),
+// keys past `live` set to -inf.
+template <typename T, int D, int KP>
+__device__ __forceinline__ void block_scores(const T* k0, const T* k1, const QFrag<T, D>& qf, int live,
+                                             f32x4 (&x)[4], int lane) {
+  if constexpr (sizeof(T) == 2)
+    qk_bf16<D, KP, 1>((const uint16_t*)k0, (const uint16_t*)k1, qf.b, x, lane);
+  else
+    qk_f32<D>((const float*)k0, qf.f, x, lane);
+  if (live < kKeyBlock) {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (16 * kt + 4 * g + j >= live) x[kt][j] = -INFINITY;
+  }
+}
+
+// s = 1 with k <= 64 and m <= 64: every tile is one routed block plus the
+// slice's landmark block, so the softmax over the m + k keys is taken in one
+// pass (no running rescale). Same persistent walk and prefetch distances as
+// gather_kernel: rows of tile t + 1, expert indices of tile t + 2, query rows of
+// tile t + 1 and query ids of tile t + 2 are in flight while tile t computes.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void gather1_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                      const T* __restrict__ V, const int32_t* __restrict__ I,
+                                                      const int4* __restrict__ tiles, const int32_t* __restrict__ perm,
+                                                      const void* __restrict__ qtop, const void* __restrict__ vtop,
+                                                      T* __restrict__ out, int N, int m, int k, int max_tiles,
+                                                      long total, int chunk, float sl2e) {
+  using TL = Tiles<T, D>;
+  constexpr bool BF = TL::BF;
+  constexpr int KP = BF ? 2 : 1;
+  __shared__ GatherLds<T, D, true> sm;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
+  const int rowi = 16 * w + r;
+  const long c0 = (long)blockIdx.x * chunk, c1 = min(total, c0 + chunk);
+
+  for (long base = c0; base < c1; base += 256) {
+    const long ent = base + tid;
+    const int4 te = ent < c1 ? tiles[ent] : make_int4(-1, 0, 0, 0);
+    const uint32_t f = te.x >= 0 ? 1u : 0u;
+    uint32_t nt;
+    const uint32_t pos = block_incl_scan(f, sm.wtot, nt) - f;
+    if (f) {
+      sm.tile[pos] = te;
+      sm.tz[pos] = (int)(ent / max_tiles);
+    }
+    __syncthreads();
+    if (nt == 0) continue;
+    const int last = (int)nt - 1;
+    auto expert = [&](int t) {   // index list of tile t's expert (past the end: the last tile)
+      t = min(t, last);
+      return I + ((size_t)sm.tz[t] * m + sm.tile[t].x) * k;
+    };
+    auto qid = [&](int t) {      // query id of this thread's row of tile t
+      t = min(t, last);
+      const int4 e = sm.tile[t];
+      return perm[(size_t)sm.tz[t] * N + e.w + min(rowi, e.z - 1)];
+    };
+    auto slice_kv = [&](int t, const T*& Kb, const T*& Vb) {
+      const size_t o = (size_t)sm.tz[min(t, last)] * N * D;
+      Kb = K + o;
+      Vb = V + o;
+    };
+
+    RowIdx<T, D> ix;
+    KVRegs<T, D, 1> RR;
+    {
+      const T *Kb, *Vb;
+      ix.load(expert(0), k, 0, tid);
+      slice_kv(0, Kb, Vb);
+      load_rows<T, D>(RR, ix, Kb, Vb, tid);
+      ix.load(expert(1), k, 0, tid);
+    }
+    int q = qid(0), q_n = qid(1), q_nn = q_n;
+    QFrag<T, D> qf;
+    qf.load(Q + ((size_t)sm.tz[0] * N + q) * D, g);
+    QFrag<T, D> qf_n = qf;
+    int zl = -1;
+
+    for (int t = 0; t < (int)nt; ++t) {
+      const int4 cur = sm.tile[t];
+      const int zc = sm.tz[t];
+      if (t > 0) {
+        q = q_n;
+        q_n = q_nn;
+        qf = qf_n;
+      }
+      q_nn = qid(t + 2);
+      __syncthreads();   // readers of the previous tile's blocks are done
+      RR.k[0].store(sm.rk, TL::KSTR, tid);
+      if constexpr (BF) RR.v.store((uint16_t*)sm.rv, tid); else RR.v.store(sm.rv, TL::VSTR, tid);
+      if (zc != zl) {   // the slice's landmark block (uniform branch)
+        KVRegs<T, D, KP> LR;
+        load_landmarks<T, D>(LR, qtop, vtop, zc, m, 0, tid);
+        LR.store(sm.lm, tid);
+        zl = zc;
+      }
+      __syncthreads();
+      {   // rows of tile t + 1 (indices in hand), indices of tile t + 2, query rows of tile t + 1
+        const T *Kb, *Vb;
+        slice_kv(t + 1, Kb, Vb);
+        load_rows<T, D>(RR, ix, Kb, Vb, tid);
+        ix.load(expert(t + 2), k, 0, tid);
+        qf_n.load(Q + ((size_t)sm.tz[min(t + 1, last)] * N + q_n) * D, g);
+      }
+      if (16 * w < cur.z) {   // wave has live rows (uniform)
+        f32x4 xl[4], xr[4];
+        block_scores<T, D, KP>(sm.lm.k0, sm.lm.k1, qf, m, xl, lane);
+        block_scores<T, D, 1>(sm.rk, nullptr, qf, k, xr, lane);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fmaxf(xl[kt][j], xr[kt][j]));
+        mx = quad_max(mx) * sl2e;
+        float l = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            xl[kt][j] = __builtin_amdgcn_exp2f(fmaf(xl[kt][j], sl2e, -mx));
+            xr[kt][j] = __builtin_amdgcn_exp2f(fmaf(xr[kt][j], sl2e, -mx));
+            l += xl[kt][j] + xr[kt][j];
+          }
+        f32x4 o[D / 16];
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (BF) {
+          pv_bf16<D>((const uint16_t*)sm.lm.v, xl, o, lane);
+          pv_bf16<D>((const uint16_t*)sm.rv, xr, o, lane);
+        } else {
+          pv_f32<D>((const float*)sm.lm.v, xl, o, lane);
+          pv_f32<D>((const float*)sm.rv, xr, o, lane);
+        }
+        const float inv = 1.f / quad_sum(l);
+        if (rowi < cur.z) {
+          T* orow = out + ((size_t)zc * N + q) * D;
+#pragma unroll
+          for (int dt = 0; dt < D / 16; ++dt)
+            store4<T>(orow + 16 * dt + 4 * g, o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+        }
+      }
+    }
+    __syncthreads();   // the tile list is rewritten by the next batch
+  }
+}
+
 // s > 1: landmark part for 64 consecutive queries, merged with their s partials.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Q, const void* __restrict__ qtop,
@@ -546,6 +696,18 @@ static hipError_t gather_launch(const Plan& p, const void* Q, const void* K, con
   const int groups = (int)std::min<long>(total, slots);
   const int chunk = (int)((total + groups - 1) / groups);
   const int grid = (int)((total + chunk - 1) / chunk);
+  if (p.s == 1 && p.k <= kKeyBlock && p.m <= kKeyBlock) {
+    static int occ1 = 0;
+    if (occ1 == 0 && hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ1, gather1_kernel<T, D>, 256, 0) != hipSuccess)
+      occ1 = 1;
+    const int g1 = (int)std::min<long>(total, (long)n_cu * std::max(1, occ1));
+    const int ch1 = (int)((total + g1 - 1) / g1);
+    hipLaunchKernelGGL((gather1_kernel<T, D>), dim3((int)((total + ch1 - 1) / ch1)), dim3(256), 0, st, (const T*)Q,
+                       (const T*)K, (const T*)V, (const int32_t*)(ws + p.ws.I), (const int4*)(ws + p.ws.tiles),
+                       (const int32_t*)(ws + p.ws.perm), (const void*)(ws + p.ws.qtop), vtop, (T*)out, p.N, p.m, p.k,
+                       p.max_tiles, total, ch1, sl2e);
+    return hipGetLastError();
+  }
   if (p.s == 1) {
     hipLaunchKernelGGL((gather_kernel<T, D, true>), dim3(grid), dim3(256), 0, st, (const T*)Q, (const T*)K, (const T*)V,
                        (const int32_t*)(ws + p.ws.I), (const int4*)(ws + p.ws.tiles), (const int32_t*)(ws + p.ws.perm),

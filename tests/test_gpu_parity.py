@@ -29,6 +29,9 @@ SMALL = [
     small("exact_router_s7", B=1, H=1, N=1536, grid_w=1536, pool_w=24, k=40, s=7, dtype="bf16"),
     small("multi_segment", B=1, H=1, N=20000, grid_w=20000, pool_w=40, k=300, s=2, dtype="bf16", needle_frac=0.01),
     small("odd_n", B=1, H=1, N=1001, grid_w=1001, pool_w=7, k=1001, s=7, dtype="bf16"),
+    # s = 1 with one key block per expert (k, m <= 64): the one-pass output kernel
+    small("one_block_f32_d128", B=2, H=1, N=700, d=128, grid_w=700, pool_w=50, k=33, s=1),
+    small("one_block_bf16_d128", B=1, H=3, N=4096, d=128, grid_w=4096, pool_w=64, k=64, s=1, dtype="bf16"),
 ]
 
 

@@ -25,17 +25,15 @@ struct Tiles {
 };
 
 // Copy 64 rows into a key tile: row r comes from rowptr(r) (D contiguous
-// elements, 16-byte aligned); rows r >= nvalid are zero.
+// elements, 16-byte aligned); rows r >= nvalid repeat row nvalid - 1, so their
+// scores are finite and the caller excludes them by index.
 template <typename T, int D, typename RowFn>
 __device__ __forceinline__ void stage_rows(T* dst, int stride, RowFn rowptr, int nvalid, int tid) {
   constexpr int EPC = Tiles<T, D>::EPC, CPR = D / EPC, TOTAL = kKeyBlock * CPR;
 #pragma unroll
   for (int c = tid; c < TOTAL; c += 256) {
     const int r = c / CPR, cc = (c % CPR) * EPC;
-    // load unconditionally from a valid row, then zero: a conditional load would
-    // be compiled into a branch that waits for its result
-    const uint4 x = *(const uint4*)(rowptr(min(r, nvalid - 1)) + cc);
-    *(uint4*)(dst + r * stride + cc) = r < nvalid ? x : make_uint4(0, 0, 0, 0);
+    *(uint4*)(dst + r * stride + cc) = ld16(rowptr(min(r, nvalid - 1)) + cc);
   }
 }
 

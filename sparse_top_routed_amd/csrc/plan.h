@@ -16,6 +16,7 @@ constexpr int kQueryTile = 64;        // queries per workgroup in the router, ga
 constexpr int kTopkSegMax = 8192;     // scores per workgroup in the segment select kernel
 constexpr int kTopkWaveMax = 4096;    // rows up to this length are selected by one wave each
 constexpr int kRouteFastMaxS = 6;     // the router keeps per-lane top lists up to this s
+constexpr int kRouteLdsMaxM = 512;    // up to this m, queries the fast router cannot settle are finished in it
 
 // Workspace offsets (bytes) of every intermediate buffer.
 struct Layout {

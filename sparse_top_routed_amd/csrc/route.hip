@@ -37,7 +37,7 @@ template <int TM>
 __device__ __forceinline__ void list_insert(float (&tv)[TM], int (&ti)[TM], float v, int i) {
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
-    const bool better = v > tv[j] || (v == tv[j] && i < ti[j]);
+    const bool better = (v > tv[j]) | ((v == tv[j]) & (i < ti[j]));   // bitwise: no short-circuit branches
     const float ov = tv[j];
     const int oi = ti[j];
     tv[j] = better ? v : ov;
@@ -53,182 +53,66 @@ __device__ __forceinline__ double load_f64(const T* p, int c) {
   else return (double)p[c];
 }
 
-template <typename T, int D, int TM>
-__global__ __launch_bounds__(256) void route_fast_kernel(const T* __restrict__ Q, const void* __restrict__ qtop,
-                                                         const double* __restrict__ qt64,
-                                                         const float* __restrict__ qtnorm, int32_t* __restrict__ E,
-                                                         uint32_t* __restrict__ counters, uint32_t* __restrict__ rflag,
-                                                         int N, int m, int s, double gamma) {
-  using TL = Tiles<T, D>;
-  constexpr bool BF = TL::BF;
-  __shared__ __align__(16) T Ks0[TL::KTILE];
-  __shared__ __align__(16) T Ks1[BF ? TL::KTILE : 8];
-  __shared__ float s_red[4];
-  const int z = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
-  const int q = blockIdx.x * kQueryTile + 16 * w + r;
-  const bool q_ok = q < N;
-  const T* qrow = Q + ((size_t)z * N + (q_ok ? q : N - 1)) * D;   // padding rows reuse a real row
-
-  // issue every independent load before the first wait: the query fragments,
-  // the landmark norms and (inside the loop) the first landmark block
-  uint4 qb[1][D / 32];
-  float qf[D / 4];
-  if constexpr (BF) {
+// Exact top-s of one query by one wave: the query row is staged in LDS (qs, D
+// doubles), every landmark is scored in fp64 against the fp64 Q~ rows (r64, m
+// doubles of LDS; BATCH 16-byte loads in flight per lane), then for s <= 16 the
+// winners are taken one at a time by a wave arg-max over (score desc, id asc);
+// for larger s the s-th largest order key is found by a bit-serial search and
+// the entries at or above it are ranked.
+template <typename T, int D, int BATCH>
+__device__ __forceinline__ void exact_route_wave(const T* qrow, const double* qt64z, int m, int s,
+                                                 int32_t* Eo, double* r64, double* qs, int lane) {
+  // the query row and the first batch of this lane's landmark row are fetched together
+  double qv[(D + 63) / 64];
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks)
-      qb[0][ks] = *(const uint4*)(qrow + 32 * ks + 8 * g);
-  } else {
+  for (int j = 0; j < (D + 63) / 64; ++j) qv[j] = load_f64<T>(qrow, min(lane + 64 * j, D - 1));
+  for (int i0 = 0; i0 < m; i0 += 64) {
+    const int i = min(i0 + lane, m - 1);
+    const double2* qr = (const double2*)(qt64z + (size_t)i * D);
+    double a0 = 0.0, a1 = 0.0;
 #pragma unroll
-    for (int ks = 0; ks < D / 4; ++ks) qf[ks] = qrow[4 * ks + g];
-  }
-  float qtm = 0.f;
-  for (int i = tid; i < m; i += 256) qtm = fmaxf(qtm, qtnorm[(size_t)z * m + i]);
-
-  float tv[TM];
-  int ti[TM];
+    for (int c0 = 0; c0 < D / 2; c0 += BATCH) {
+      double2 x[BATCH];
 #pragma unroll
-  for (int j = 0; j < TM; ++j) { tv[j] = -INFINITY; ti[j] = 0x7FFFFFFF; }
-
-  const T* plane0 = BF ? (const T*)((const uint16_t*)qtop + (size_t)z * 2 * m * D) : (const T*)((const float*)qtop + (size_t)z * m * D);
-  const T* plane1 = BF ? plane0 + (size_t)m * D : plane0;
-  for (int lb0 = 0; lb0 < m; lb0 += kKeyBlock) {
-    const int nvalid = min(kKeyBlock, m - lb0);
-    stage_rows<T, D>(Ks0, TL::KSTR, [&](int rr) { return plane0 + (size_t)(lb0 + rr) * D; }, nvalid, tid);
-    if constexpr (BF)
-      stage_rows<T, D>(Ks1, TL::KSTR, [&](int rr) { return plane1 + (size_t)(lb0 + rr) * D; }, nvalid, tid);
-    __syncthreads();
-    f32x4 acc[4];
-    if constexpr (BF)
-      qk_bf16<D, 2, 1>((const uint16_t*)Ks0, (const uint16_t*)Ks1, qb, acc, lane);
-    else
-      qk_f32<D>((const float*)Ks0, qf, acc, lane);
-    __syncthreads();
+      for (int c = 0; c < BATCH; ++c) x[c] = qr[c0 + c];
+      if (i0 == 0 && c0 == 0) {   // uniform: stage the query row once its loads are in flight
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int li = lb0 + 16 * kt + 4 * g + j;
-        if (li < m) list_insert_ordered<TM>(tv, ti, acc[kt][j], li);
+        for (int j = 0; j < (D + 63) / 64; ++j)
+          if (lane + 64 * j < D) qs[lane + 64 * j] = qv[j];
+        wave_sync();
       }
+#pragma unroll
+      for (int c = 0; c < BATCH; ++c) {
+        a0 = fma(x[c].x, qs[2 * (c0 + c)], a0);
+        a1 = fma(x[c].y, qs[2 * (c0 + c) + 1], a1);
+      }
+    }
+    if (i0 + lane < m) r64[i0 + lane] = a0 + a1;
   }
+  wave_sync();
+  if (s <= 16) {
+    for (int rnd = 0; rnd < s; ++rnd) {
+      double bv = -INFINITY;
+      int bi = 0x7FFFFFFF;
+      for (int i = lane; i < m; i += 64) {   // ids ascend within a lane: strict > keeps the lower id
+        const double v = r64[i];
+        if (v > bv) { bv = v; bi = i; }
+      }
 #pragma unroll
-  for (int sh = 16; sh <= 32; sh <<= 1) {
-    float ov[TM];
-    int oi[TM];
-#pragma unroll
-    for (int j = 0; j < TM; ++j) { ov[j] = __shfl_xor(tv[j], sh, WAVE); oi[j] = __shfl_xor(ti[j], sh, WAVE); }
-#pragma unroll
-    for (int j = 0; j < TM; ++j) list_insert<TM>(tv, ti, ov[j], oi[j]);
-  }
-
-  float sq = 0.f;
-  if constexpr (BF) {
-#pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
-      const uint16_t* h = (const uint16_t*)&qb[0][ks];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { const float x = bf16_to_f32(h[e]); sq = fmaf(x, x, sq); }
+      for (int o = 32; o >= 1; o >>= 1) {
+        const double ov = __shfl_xor(bv, o, WAVE);
+        const int oi = __shfl_xor(bi, o, WAVE);
+        const bool take = (ov > bv) | ((ov == bv) & (oi < bi));
+        bv = take ? ov : bv;
+        bi = take ? oi : bi;
+      }
+      if (lane == 0) {
+        Eo[rnd] = bi;
+        r64[bi] = -INFINITY;   // scores are finite, so a taken entry never wins again
+      }
+      wave_sync();
     }
   } else {
-#pragma unroll
-    for (int ks = 0; ks < D / 4; ++ks) sq = fmaf(qf[ks], qf[ks], sq);
-  }
-  const float qn = sqrtf(quad_sum(sq)) * 1.0001f;
-  qtm = wave_max(qtm);
-  if (lane == 0) s_red[w] = qtm;
-  __syncthreads();
-  const double qtmax = (double)fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  const double Eq = gamma * (double)qn * qtmax;
-  // s-th and (s+1)-th entries without dynamic register indexing
-  float v_s = -INFINITY, v_s1 = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < TM; ++j) {
-    if (j == s - 1) v_s = tv[j];
-    if (j == s) v_s1 = tv[j];
-  }
-  const double That = (double)v_s;
-  bool certain = s >= m, refine = false, queue = false;
-  if (!certain) {
-    certain = (double)v_s - (double)v_s1 > 2.0 * Eq;
-    if (!certain) {
-      if (m <= TM || (double)tv[TM - 1] < That - 2.0 * Eq) refine = true; else queue = true;
-    }
-  }
-  refine = refine && q_ok;
-  int32_t* Eq_out = E + ((size_t)z * N + q) * s;
-  if (q_ok && g == 0) {
-    if (certain) {
-#pragma unroll
-      for (int j = 0; j < TM; ++j)
-        if (j < s) Eq_out[j] = ti[j];
-    } else if (queue) {
-      const uint32_t pos = atomicAdd(&counters[0], 1u);
-      rflag[pos] = (uint32_t)(z * N + q);
-    }
-  }
-  if (__any(refine)) {
-    // fp64 scores of the band entries: the four lanes of a query split d
-    double s64[TM];
-    bool band[TM];
-    int c_in = 0;
-#pragma unroll
-    for (int j = 0; j < TM; ++j) {
-      const double v = (double)tv[j];
-      band[j] = refine && ti[j] < m && v >= That - 2.0 * Eq && v <= That + 2.0 * Eq;
-      c_in += (refine && ti[j] < m && v > That + 2.0 * Eq) ? 1 : 0;
-      double part = 0.0;
-      if (band[j]) {
-        const double* qr = qt64 + ((size_t)z * m + ti[j]) * D;
-        for (int e = 0; e < D / 4; ++e) {
-          const int c = g * (D / 4) + e;
-          part = fma(qr[c], load_f64<T>(qrow, c), part);
-        }
-      }
-      part += __shfl_xor(part, 16, WAVE);
-      part += __shfl_xor(part, 32, WAVE);
-      s64[j] = part;
-    }
-    if (refine && g == 0) {
-      const int need = s - c_in;
-#pragma unroll
-      for (int j = 0; j < TM; ++j)
-        if (j < c_in) Eq_out[j] = ti[j];
-#pragma unroll
-      for (int j = 0; j < TM; ++j) {
-        if (!band[j]) continue;
-        int rank = 0;
-#pragma unroll
-        for (int f = 0; f < TM; ++f)
-          rank += (band[f] && (s64[f] > s64[j] || (s64[f] == s64[j] && ti[f] < ti[j]))) ? 1 : 0;
-        if (rank < need) Eq_out[c_in + rank] = ti[j];
-      }
-    }
-  }
-}
-
-// Exact routing: one wave per query, all m scores in fp64 (kept in LDS), the
-// s-th largest found by a bit-serial search over order keys, then the selected
-// entries ranked by (score desc, id asc). Processes the queued queries, or all
-// queries when `list` is NULL.
-template <typename T, int D>
-__global__ __launch_bounds__(64) void route_exact_kernel(const T* __restrict__ Q, const double* __restrict__ qt64,
-                                                         int32_t* __restrict__ E, const uint32_t* __restrict__ counters,
-                                                         const uint32_t* __restrict__ list, int N, int m, int s,
-                                                         int total) {
-  extern __shared__ double r64[];
-  const int lane = threadIdx.x;
-  const int count = list ? (int)counters[0] : total;
-  for (int t = blockIdx.x; t < count; t += gridDim.x) {
-    const int qid = list ? (int)list[t] : t;
-    const int z = qid / N;
-    const T* qrow = Q + (size_t)qid * D;
-    for (int i = lane; i < m; i += 64) {
-      const double* qr = qt64 + ((size_t)z * m + i) * D;
-      double acc = 0.0;
-      for (int c = 0; c < D; ++c) acc = fma(qr[c], load_f64<T>(qrow, c), acc);
-      r64[i] = acc;
-    }
-    __syncthreads();
     uint64_t pfx = 0;
     for (int b = 63; b >= 0; --b) {
       const uint64_t cand = pfx | (1ull << b);
@@ -236,7 +120,6 @@ __global__ __launch_bounds__(64) void route_exact_kernel(const T* __restrict__ Q
       for (int i = lane; i < m; i += 64) c += f64_key(r64[i]) >= cand ? 1 : 0;
       if (wave_sum_i(c) >= s) pfx = cand;
     }
-    int32_t* Eo = E + (size_t)qid * s;
     for (int i = lane; i < m; i += 64) {
       const uint64_t ki = f64_key(r64[i]);
       if (ki < pfx) continue;
@@ -247,16 +130,306 @@ __global__ __launch_bounds__(64) void route_exact_kernel(const T* __restrict__ Q
       }
       if (rank < s) Eo[rank] = i;
     }
+  }
+  wave_sync();
+}
+
+// Fast router. RES: m <= 64, so the landmark block is staged once for all the
+// workgroup's query tiles and each query's m scores are still in registers when
+// its set is decided: band members are then re-scored in fp64 right there.
+// Otherwise the landmark blocks stream through LDS per tile, each lane keeps a
+// top list, and a query whose band reaches past the list end is queued: to the
+// end of this workgroup (TAIL) or to the exact kernel.
+template <typename T, int D, int TM, bool RES, bool TAIL>
+__global__ __launch_bounds__(256) void route_fast_kernel(const T* __restrict__ Q, const void* __restrict__ qtop,
+                                                         const double* __restrict__ qt64,
+                                                         const float* __restrict__ qtnorm, int32_t* __restrict__ E,
+                                                         uint32_t* __restrict__ counters, uint32_t* __restrict__ rflag,
+                                                         int N, int m, int s, double gamma, int qtiles, int tpw) {
+  using TL = Tiles<T, D>;
+  constexpr bool BF = TL::BF;
+  __shared__ __align__(16) T Ks0[TL::KTILE];
+  __shared__ __align__(16) T Ks1[BF ? TL::KTILE : 8];
+  __shared__ float s_red[4];
+  __shared__ int s_nq;
+  __shared__ int s_q[TAIL ? kQueryTile : 1];                   // queries left for the exact routine
+  __shared__ double s_x[TAIL ? 4 * (kRouteLdsMaxM + D) : 1];   // per wave: m scores + the query row
+  const int z = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
+  const int t0 = blockIdx.x * tpw, t1 = min(qtiles, t0 + tpw);
+  const T* plane0 = BF ? (const T*)((const uint16_t*)qtop + (size_t)z * 2 * m * D) : (const T*)((const float*)qtop + (size_t)z * m * D);
+  const T* plane1 = BF ? plane0 + (size_t)m * D : plane0;
+  const double* qt64z = qt64 + (size_t)z * m * D;
+  auto stage = [&](int lb0) {
+    const int nvalid = min(kKeyBlock, m - lb0);
+    stage_rows<T, D>(Ks0, TL::KSTR, [&](int rr) { return plane0 + (size_t)(lb0 + rr) * D; }, nvalid, tid);
+    if constexpr (BF)
+      stage_rows<T, D>(Ks1, TL::KSTR, [&](int rr) { return plane1 + (size_t)(lb0 + rr) * D; }, nvalid, tid);
+  };
+  auto qrow_of = [&](int t) {   // this thread's query row of tile t (padding rows reuse a real row)
+    const int q = min(t * kQueryTile + 16 * w + r, N - 1);
+    return Q + ((size_t)z * N + q) * D;
+  };
+  auto load_q = [&](uint4 (&qb)[1][D / 32], float (&qf)[D / 4], const T* qrow) {
+    if constexpr (BF) {
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) qb[0][ks] = ld16(qrow + 32 * ks + 8 * g);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < D / 4; ++ks) qf[ks] = qrow[4 * ks + g];
+    }
+  };
+
+  // independent loads first: the first query tile, the landmark norms, the landmark block
+  uint4 qb[1][D / 32], qb_n[1][D / 32];
+  float qf[D / 4], qf_n[D / 4];
+  load_q(qb_n, qf_n, qrow_of(t0));
+  float qtm = 0.f;
+  for (int i = tid; i < m; i += 256) qtm = fmaxf(qtm, qtnorm[(size_t)z * m + i]);
+  if (RES) stage(0);
+  qtm = wave_max(qtm);
+  if (lane == 0) s_red[w] = qtm;
+  if (tid == 0) s_nq = 0;
+  __syncthreads();
+  const double qtmax = (double)fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+
+  for (int t = t0; t < t1; ++t) {
+    if (!RES && TAIL && t > t0) {   // finish the previous tile's queued queries (one wave each)
+      __syncthreads();
+      const int nq = s_nq;
+      double* r64 = s_x + w * (kRouteLdsMaxM + D);
+      for (int e = w; e < nq; e += 4) {
+        const int q = s_q[e];
+        exact_route_wave<T, D, 16>(Q + ((size_t)z * N + q) * D, qt64z, m, s, E + ((size_t)z * N + q) * s, r64,
+                                   r64 + kRouteLdsMaxM, lane);
+      }
+      __syncthreads();
+      if (tid == 0) s_nq = 0;
+    }
+    const int q = t * kQueryTile + 16 * w + r;
+    const bool q_ok = q < N;
+    if constexpr (BF) {
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) qb[0][ks] = qb_n[0][ks];
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < D / 4; ++ks) qf[ks] = qf_n[ks];
+    }
+    load_q(qb_n, qf_n, qrow_of(min(t + 1, t1 - 1)));   // next tile's rows in flight
+
+    float tv[TM];
+    int ti[TM];
+#pragma unroll
+    for (int j = 0; j < TM; ++j) { tv[j] = -INFINITY; ti[j] = 0x7FFFFFFF; }
+    f32x4 acc[4];
+    for (int lb0 = 0; lb0 < m; lb0 += kKeyBlock) {
+      if (!RES) {
+        __syncthreads();   // readers of the previous block are done
+        stage(lb0);
+        __syncthreads();
+      }
+      if constexpr (BF)
+        qk_bf16<D, 2, 1>((const uint16_t*)Ks0, (const uint16_t*)Ks1, qb, acc, lane);
+      else
+        qk_f32<D>((const float*)Ks0, qf, acc, lane);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int li = lb0 + 16 * kt + 4 * g + j;   // past m: -inf never enters the list
+          list_insert_ordered<TM>(tv, ti, li < m ? acc[kt][j] : -INFINITY, li);
+        }
+    }
+#pragma unroll
+    for (int sh = 16; sh <= 32; sh <<= 1) {
+      float ov[TM];
+      int oi[TM];
+#pragma unroll
+      for (int j = 0; j < TM; ++j) { ov[j] = __shfl_xor(tv[j], sh, WAVE); oi[j] = __shfl_xor(ti[j], sh, WAVE); }
+#pragma unroll
+      for (int j = 0; j < TM; ++j) list_insert<TM>(tv, ti, ov[j], oi[j]);
+    }
+
+    float sq = 0.f;
+    if constexpr (BF) {
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const uint16_t* h = (const uint16_t*)&qb[0][ks];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { const float x = bf16_to_f32(h[e]); sq = fmaf(x, x, sq); }
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < D / 4; ++ks) sq = fmaf(qf[ks], qf[ks], sq);
+    }
+    const float qn = sqrtf(quad_sum(sq)) * 1.0001f;
+    const double Eq = gamma * (double)qn * qtmax;
+    // s-th and (s+1)-th entries without dynamic register indexing
+    float v_s = -INFINITY, v_s1 = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      if (j == s - 1) v_s = tv[j];
+      if (j == s) v_s1 = tv[j];
+    }
+    const double That = (double)v_s, lo = That - 2.0 * Eq, hi = That + 2.0 * Eq;
+    const bool certain = s >= m || (double)v_s - (double)v_s1 > 2.0 * Eq;
+    int32_t* Eq_out = E + ((size_t)z * N + min(q, N - 1)) * s;
+    if (q_ok && g == 0 && certain) {
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+        if (j < s) Eq_out[j] = ti[j];
+    }
+    const bool unc = q_ok && !certain;
+    if (!__any(unc)) continue;
+
+    // entries above the band are in for sure; the band is ranked in fp64
+    int c_in = 0;
+#pragma unroll
+    for (int j = 0; j < TM; ++j) c_in += (j < s && (double)tv[j] > hi) ? 1 : 0;
+    const int need = s - c_in;
+    if (unc && g == 0) {
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+        if (j < c_in) Eq_out[j] = ti[j];
+    }
+    // fp64 partial dot of this lane's share of the query with landmark li
+    auto part64 = [&](int li) {
+      const double* qr = qt64z + (size_t)li * D;
+      double part = 0.0;
+      if constexpr (BF) {
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+          const uint16_t* h = (const uint16_t*)&qb[0][ks];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) part = fma(qr[32 * ks + 8 * g + e], (double)bf16_to_f32(h[e]), part);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < D / 4; ++ks) part = fma(qr[4 * ks + g], (double)qf[ks], part);
+      }
+      part += __shfl_xor(part, 16, WAVE);
+      return part + __shfl_xor(part, 32, WAVE);
+    };
+    if constexpr (RES) {
+      // every score of the query is in acc (lanes of the quad hold 16 each):
+      // the band members are re-scored one by one, quad-uniformly
+      uint32_t mk = 0;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int li = 16 * kt + 4 * g + j;
+          const double v = (double)acc[kt][j];
+          mk |= (unc && li < m && v >= lo && v <= hi) ? 1u << (4 * kt + j) : 0u;
+        }
+      uint64_t qm = 0;
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) qm |= (uint64_t)__shfl(mk, r + 16 * gg, WAVE) << (16 * gg);
+      double bv[TM];
+      int bi[TM];
+#pragma unroll
+      for (int j = 0; j < TM; ++j) { bv[j] = -INFINITY; bi[j] = 0x7FFFFFFF; }
+      while (qm) {   // same trip count on the four lanes of a query
+        const int bit = __builtin_ctzll(qm);
+        qm &= qm - 1;
+        const int b = bit & 15, li = 16 * (b >> 2) + 4 * (bit >> 4) + (b & 3);
+        double v = part64(li);
+        int i = li;
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {   // insert by (score desc, id asc)
+          const bool better = (v > bv[j]) | ((v == bv[j]) & (i < bi[j]));
+          const double ov = bv[j];
+          const int oi = bi[j];
+          bv[j] = better ? v : ov;
+          bi[j] = better ? i : oi;
+          v = better ? ov : v;
+          i = better ? oi : i;
+        }
+      }
+      if (unc && g == 0) {
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+          if (j < need) Eq_out[c_in + j] = bi[j];
+      }
+    } else {
+      // the list holds the whole band when its last entry lies below it
+      const bool refine = unc && (m <= TM || (double)tv[TM - 1] < lo);
+      if (unc && !refine && g == 0) {
+        if (TAIL) {
+          s_q[atomicAdd(&s_nq, 1)] = q;
+        } else {
+          const uint32_t pos = atomicAdd(&counters[0], 1u);
+          rflag[pos] = (uint32_t)(z * N + q);
+        }
+      }
+      if (__any(refine)) {
+        double s64[TM];
+        bool band[TM];
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+          const double v = (double)tv[j];
+          band[j] = refine && ti[j] < m && v >= lo && v <= hi;
+          s64[j] = part64(band[j] ? ti[j] : 0);
+        }
+        if (refine && g == 0) {
+#pragma unroll
+          for (int j = 0; j < TM; ++j) {
+            if (!band[j]) continue;
+            int rank = 0;
+#pragma unroll
+            for (int f = 0; f < TM; ++f)
+              rank += (band[f] && ((s64[f] > s64[j]) | ((s64[f] == s64[j]) & (ti[f] < ti[j])))) ? 1 : 0;
+            if (rank < need) Eq_out[c_in + rank] = ti[j];
+          }
+        }
+      }
+    }
+  }
+  if constexpr (!RES && TAIL) {   // the last tile's queued queries
     __syncthreads();
+    const int nq = s_nq;
+    double* r64 = s_x + w * (kRouteLdsMaxM + D);
+    for (int e = w; e < nq; e += 4) {
+      const int q = s_q[e];
+      exact_route_wave<T, D, 16>(Q + ((size_t)z * N + q) * D, qt64z, m, s, E + ((size_t)z * N + q) * s, r64,
+                                 r64 + kRouteLdsMaxM, lane);
+    }
   }
 }
 
+// Exact routing kernel: one wave per query (up to four per workgroup), for the
+// queries the fast kernel queued or for all queries when `list` is NULL (s > 6).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void route_exact_kernel(const T* __restrict__ Q, const double* __restrict__ qt64,
+                                                          int32_t* __restrict__ E, const uint32_t* __restrict__ counters,
+                                                          const uint32_t* __restrict__ list, int N, int m, int s,
+                                                          int total) {
+  extern __shared__ double x64[];   // per wave: [m] scores, then the query row [D]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  double* r64 = x64 + (size_t)w * (m + D);
+  const int count = list ? (int)counters[0] : total;
+  const int nw = blockDim.x >> 6;
+  for (int t = blockIdx.x * nw + w; t < count; t += gridDim.x * nw) {
+    const int qid = list ? (int)list[t] : t;
+    const int z = qid / N;
+    exact_route_wave<T, D, 32>(Q + (size_t)qid * D, qt64 + (size_t)z * m * D, m, s, E + (size_t)qid * s, r64,
+                               r64 + m, lane);
+  }
+}
+
+// Where the queries the fast kernel cannot settle are finished: m <= 64 in the
+// fast kernel itself (all scores at hand); up to kRouteLdsMaxM at the end of each
+// query tile of the fast kernel; beyond that by the exact kernel.
 template <typename T, int D, int TM>
 static hipError_t route_fast_launch(const Plan& p, const void* Q, char* ws, hipStream_t st) {
-  hipLaunchKernelGGL((route_fast_kernel<T, D, TM>), dim3(p.qtiles, p.BH), dim3(256), 0, st, (const T*)Q,
-                     (const void*)(ws + p.ws.qtop), (const double*)(ws + p.ws.qt64), (const float*)(ws + p.ws.qtnorm),
-                     (int32_t*)(ws + p.ws.E), (uint32_t*)(ws + p.ws.counters), (uint32_t*)(ws + p.ws.rflag), p.N, p.m,
-                     p.s, p.gamma_qk);
+  const bool res = p.m <= kKeyBlock, tail = !res && p.m <= kRouteLdsMaxM;
+  const int tpw = res ? 4 : 1;   // several query tiles per workgroup when the landmarks stay staged
+  const dim3 grid((p.qtiles + tpw - 1) / tpw, p.BH);
+  auto kern = res ? route_fast_kernel<T, D, TM, true, false>
+                  : (tail ? route_fast_kernel<T, D, TM, false, true> : route_fast_kernel<T, D, TM, false, false>);
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, (const T*)Q, (const void*)(ws + p.ws.qtop),
+                     (const double*)(ws + p.ws.qt64), (const float*)(ws + p.ws.qtnorm), (int32_t*)(ws + p.ws.E),
+                     (uint32_t*)(ws + p.ws.counters), (uint32_t*)(ws + p.ws.rflag), p.N, p.m, p.s, p.gamma_qk,
+                     p.qtiles, tpw);
   return hipGetLastError();
 }
 
@@ -265,17 +438,22 @@ static hipError_t route_launch(const Plan& p, const void* Q, char* ws, hipStream
   hipError_t e = hipSuccess;
   const bool fast = p.s <= kRouteFastMaxS;
   if (fast) {
-    if (p.s == 1) e = route_fast_launch<T, D, 3>(p, Q, ws, st);
-    else if (p.s == 2) e = route_fast_launch<T, D, 4>(p, Q, ws, st);
-    else if (p.s <= 4) e = route_fast_launch<T, D, 6>(p, Q, ws, st);
-    else e = route_fast_launch<T, D, 8>(p, Q, ws, st);
+    // lists of s + 1 entries: enough to certify the set (m <= 64 re-scores the
+    // band from the scores in registers; larger m queues what the list cannot settle)
+    if (p.s == 1) e = route_fast_launch<T, D, 2>(p, Q, ws, st);
+    else if (p.s == 2) e = route_fast_launch<T, D, 3>(p, Q, ws, st);
+    else if (p.s <= 4) e = route_fast_launch<T, D, 5>(p, Q, ws, st);
+    else e = route_fast_launch<T, D, 7>(p, Q, ws, st);
     if (e != hipSuccess) return e;
+    if (p.m <= kRouteLdsMaxM) return hipSuccess;
   }
   const int total = p.BH * p.N;
-  const int blocks = fast ? 2048 : std::min(total, 65536);
-  hipLaunchKernelGGL((route_exact_kernel<T, D>), dim3(blocks), dim3(64), (size_t)p.m * 8, st, (const T*)Q,
-                     (const double*)(ws + p.ws.qt64), (int32_t*)(ws + p.ws.E), (const uint32_t*)(ws + p.ws.counters),
-                     fast ? (const uint32_t*)(ws + p.ws.rflag) : nullptr, p.N, p.m, p.s, total);
+  const int nw = (size_t)4 * (p.m + p.d) * 8 <= 65536 ? 4 : 1;   // LDS: m scores + the query row per wave
+  const int blocks = fast ? 4096 / nw : std::min((total + nw - 1) / nw, 65536);
+  hipLaunchKernelGGL((route_exact_kernel<T, D>), dim3(blocks), dim3(64 * nw), (size_t)nw * (p.m + p.d) * 8, st,
+                     (const T*)Q, (const double*)(ws + p.ws.qt64), (int32_t*)(ws + p.ws.E),
+                     (const uint32_t*)(ws + p.ws.counters), fast ? (const uint32_t*)(ws + p.ws.rflag) : nullptr, p.N,
+                     p.m, p.s, total);
   return hipGetLastError();
 }
 

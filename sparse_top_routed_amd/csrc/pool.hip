@@ -22,13 +22,18 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ Q, doub
                                                    int grid_h, int grid_w, int pool_h, int pool_w) {
   constexpr int TPR = D / 8;          // lanes per row, 8 elements each
   constexpr int RPW = WAVE / TPR;     // rows per wave step
-  const int i = blockIdx.x * 4 + (threadIdx.x >> 6), z = blockIdx.y, lane = threadIdx.x & 63;
+  // the landmark index is wave-uniform: keep the window arithmetic scalar
+  const int i = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), z = blockIdx.y;
+  const int lane = threadIdx.x & 63;
   if (i >= m) return;
   const int a = i / pool_w, b = i % pool_w;
-  const int r0 = (int)(((int64_t)a * grid_h) / pool_h);
-  const int r1 = (int)(((int64_t)(a + 1) * grid_h + pool_h - 1) / pool_h);
-  const int c0 = (int)(((int64_t)b * grid_w) / pool_w);
-  const int c1 = (int)(((int64_t)(b + 1) * grid_w + pool_w - 1) / pool_w);
+  // window bounds floor(a L / M) and ceil((a + 1) L / M): the products are
+  // integers below 2^53 and a non-integer quotient is at least 1/M away from an
+  // integer, so the rounded fp64 quotient gives the exact floor and ceil
+  const int r0 = (int)floor((double)a * grid_h / pool_h);
+  const int r1 = (int)ceil((double)(a + 1) * grid_h / pool_h);
+  const int c0 = (int)floor((double)b * grid_w / pool_w);
+  const int c1 = (int)ceil((double)(b + 1) * grid_w / pool_w);
   const int wc = c1 - c0, cnt = (r1 - r0) * wc;
   const int col = (lane % TPR) * 8, rsub = lane / TPR;
   const T* base = Q + (size_t)z * N * D;

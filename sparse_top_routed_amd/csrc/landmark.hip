@@ -5,9 +5,12 @@
 //
 // Flash-style: a workgroup takes 64 landmarks (16 per wave) and one chunk of
 // keys, streams the chunk through LDS 64 keys at a time (the next block is
-// fetched into registers while the current one computes), writes the unscaled
-// scores, and keeps an online softmax. A second kernel merges the chunks'
-// partial softmaxes into V~.
+// fetched into registers while the current one computes) and keeps an online
+// softmax. A second kernel merges the chunks' partial softmaxes into V~. The
+// scores themselves do not go to memory: only maxima of groups of 16 (one
+// lane's share of a block) or 64 (a block) per landmark, from which step 3 sets
+// a threshold that its candidates must reach (written out in full only on
+// request, for checking).
 // bf16 inputs: Q~ enters the MFMA as two bf16 parts (hi + lo) so the scores
 // carry ~16 more bits than a bf16 Q~ would; fp32 inputs use the fp32 MFMA.
 // The workgroups of landmark tile 0 also record max_n |K_n|_2 per chunk, which
@@ -21,8 +24,9 @@ namespace mita {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void landmark_kernel(const T* __restrict__ K, const T* __restrict__ V,
                                                        const void* __restrict__ qtop, float* __restrict__ S,
-                                                       float* __restrict__ lpart, float* __restrict__ kmax, int N,
-                                                       int m, int lchunk, int nsplit, float sl2e) {
+                                                       float* __restrict__ lpart, float* __restrict__ kmax,
+                                                       float* __restrict__ bmax, int N, int m, int lchunk, int nsplit,
+                                                       int gq, int nbg, float sl2e) {
   using TL = Tiles<T, D>;
   constexpr bool BF = TL::BF;
   __shared__ __align__(16) T Ks[TL::KTILE];
@@ -61,7 +65,8 @@ __global__ __launch_bounds__(256) void landmark_kernel(const T* __restrict__ K, 
   f32x4 o[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float* Srow = S + ((size_t)z * m + lmc) * N;
+  float* Srow = S ? S + ((size_t)z * m + lmc) * N : nullptr;
+  float* Brow = bmax + ((size_t)z * m + lmc) * nbg;
   const bool vec_store = (N & 3) == 0;
   const int last_kb = k0 + ((k1 - k0 - 1) / kKeyBlock) * kKeyBlock;
 
@@ -98,7 +103,17 @@ __global__ __launch_bounds__(256) void landmark_kernel(const T* __restrict__ K, 
     else
       qk_f32<D>((const float*)Ks, qf, acc, lane);
 
-    if (lm_ok) {
+    {   // group maxima for the top-k threshold: one lane's 16 scores, or the block's 64
+      float gm = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) gm = fmaxf(gm, kb + 16 * kt + 4 * g + j < k1 ? acc[kt][j] : -INFINITY);
+      if (gq == 64) gm = quad_max(gm);
+      const int blk = kb / kKeyBlock;
+      if (lm_ok && (gq == 16 || g == 0)) Brow[gq == 16 ? 4 * blk + g : blk] = gm;
+    }
+    if (Srow && lm_ok) {   // the scores themselves only when asked for
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         const int key = kb + 16 * kt + 4 * g;
@@ -185,12 +200,13 @@ __global__ __launch_bounds__(256) void landmark_merge_kernel(const float* __rest
 }
 
 template <typename T, int D>
-static hipError_t landmark_launch(const Plan& p, const void* K, const void* V, char* ws, hipStream_t st) {
+static hipError_t landmark_launch(const Plan& p, const void* K, const void* V, char* ws, float* S_out,
+                                  hipStream_t st) {
   const float sl2e = (float)(1.4426950408889634 / sqrt((double)D));
   dim3 grid(p.lm_tiles, p.nsplit, p.BH);
   hipLaunchKernelGGL((landmark_kernel<T, D>), grid, dim3(256), 0, st, (const T*)K, (const T*)V,
-                     (const void*)(ws + p.ws.qtop), (float*)(ws + p.ws.S), (float*)(ws + p.ws.lpart),
-                     (float*)(ws + p.ws.kmax), p.N, p.m, p.lchunk, p.nsplit, sl2e);
+                     (const void*)(ws + p.ws.qtop), S_out, (float*)(ws + p.ws.lpart), (float*)(ws + p.ws.kmax),
+                     (float*)(ws + p.ws.bmax), p.N, p.m, p.lchunk, p.nsplit, p.gq, p.nbg, sl2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rows = p.BH * p.m;
@@ -200,10 +216,11 @@ static hipError_t landmark_launch(const Plan& p, const void* K, const void* V, c
   return hipGetLastError();
 }
 
-hipError_t launch_landmark(const Plan& p, const void* K, const void* V, char* ws, hipStream_t st) {
+hipError_t launch_landmark(const Plan& p, const void* K, const void* V, char* ws, float* S_out, hipStream_t st) {
   if (p.dtype == MITA_BF16)
-    return p.d == 64 ? landmark_launch<uint16_t, 64>(p, K, V, ws, st) : landmark_launch<uint16_t, 128>(p, K, V, ws, st);
-  return p.d == 64 ? landmark_launch<float, 64>(p, K, V, ws, st) : landmark_launch<float, 128>(p, K, V, ws, st);
+    return p.d == 64 ? landmark_launch<uint16_t, 64>(p, K, V, ws, S_out, st)
+                     : landmark_launch<uint16_t, 128>(p, K, V, ws, S_out, st);
+  return p.d == 64 ? landmark_launch<float, 64>(p, K, V, ws, S_out, st) : landmark_launch<float, 128>(p, K, V, ws, S_out, st);
 }
 
 }  // namespace mita

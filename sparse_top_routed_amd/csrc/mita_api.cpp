@@ -59,12 +59,18 @@ mita_status make_plan(const mita_shape* shape, int m, int k, int s, Plan* p, con
   P.lchunk = (int)chunk;
   P.nsplit = (int)((sh.N + chunk - 1) / chunk);
 
-  // Top-k select: segments of at most kTopkSegMax scores, multiples of 1024.
-  P.G = (sh.N + kTopkSegMax - 1) / kTopkSegMax;
-  int seg = (sh.N + P.G - 1) / P.G;
-  P.seg = (seg + 1023) / 1024 * 1024;
-  P.G = (sh.N + P.seg - 1) / P.seg;
-
+  // Top-k select: group maxima of the scores give each row a candidate threshold.
+  {
+    const int64_t nblk = (sh.N + kKeyBlock - 1) / kKeyBlock;
+    P.gq = nblk >= 4 * (int64_t)k ? 64 : 16;
+    P.nbg = (int)(nblk * (kKeyBlock / P.gq));
+    int64_t cap = std::max<int64_t>(256, 4 * (int64_t)k);
+    cap = (cap + 63) / 64 * 64;
+    int64_t pw = 256;
+    while (pw < cap) pw *= 2;   // the select kernel is instantiated for powers of two
+    P.cap = pw <= kTopkMaxCap ? (int)pw : 0;
+    P.capc = P.cap ? (int)std::min<int64_t>(P.lchunk, P.cap) : 0;
+  }
   P.qtiles = (sh.N + kQueryTile - 1) / kQueryTile;
   P.max_tiles = (int)(((int64_t)sh.N * s + kQueryTile - 1) / kQueryTile + m);
 
@@ -89,10 +95,12 @@ mita_status make_plan(const mita_shape* shape, int m, int k, int s, Plan* p, con
   L.kmax = take(bh * P.nsplit * 4);
   L.vt32 = take(bh * m * d * 4);
   L.vt16 = take(bh * m * d * 2);
-  L.S = take(bh * m * N * 4);
-  L.cand_key = take(bh * m * N * 4);
-  L.cand_idx = take(bh * m * N * 4);
-  L.cand_cnt = take(bh * m * P.G * 4);
+  L.bmax = take(bh * m * P.nbg * 4);
+  L.thr = take(bh * m * 4);
+  L.cand = take(bh * m * P.nsplit * (size_t)P.capc * 8);
+  L.ccnt = take(bh * m * P.nsplit * 4);
+  L.glist = take((bh * m + 1) * 4);
+  L.gscr = take((size_t)kTopkGeneralWaves * N * 8);
   L.I = take(bh * m * (size_t)k * 4);
   L.E = take(bh * N * s * 4);
   // counters: everything from here to `perm` is cleared before routing
@@ -195,9 +203,9 @@ mita_status mita_landmark(const void* K, const void* V, int m, int k, int s, con
   if ((st = check_ptr(K, "K")) != MITA_OK || (st = check_ptr(V, "V")) != MITA_OK) return st;
   hipStream_t hs = (hipStream_t)stream;
   char* ws = (char*)workspace;
-  if ((st = hip_status(launch_landmark(P, K, V, ws, hs), "landmark")) != MITA_OK) return st;
-  if ((st = copy_out(Vt_out, ws + P.ws.vt32, (size_t)P.BH * m * P.d * 4, hs, "landmark copy-out")) != MITA_OK) return st;
-  return copy_out(S_out, ws + P.ws.S, (size_t)P.BH * m * P.N * 4, hs, "score copy-out");
+  if (S_out && ((uintptr_t)S_out & 15) != 0) { set_error("S_out must be 16-byte aligned"); return MITA_ERR_INVALID_ARG; }
+  if ((st = hip_status(launch_landmark(P, K, V, ws, S_out, hs), "landmark")) != MITA_OK) return st;
+  return copy_out(Vt_out, ws + P.ws.vt32, (size_t)P.BH * m * P.d * 4, hs, "landmark copy-out");
 }
 
 mita_status mita_topk(const void* K, int m, int k, int s, const mita_shape* shape, void* workspace,
@@ -248,7 +256,7 @@ mita_status mita_forward(const void* Q, const void* K, const void* V, int m, int
   hipStream_t hs = (hipStream_t)stream;
   char* ws = (char*)workspace;
   if ((st = hip_status(launch_pool(P, Q, ws, hs), "pool")) != MITA_OK) return st;
-  if ((st = hip_status(launch_landmark(P, K, V, ws, hs), "landmark")) != MITA_OK) return st;
+  if ((st = hip_status(launch_landmark(P, K, V, ws, nullptr, hs), "landmark")) != MITA_OK) return st;
   if ((st = hip_status(launch_topk(P, K, ws, hs), "topk")) != MITA_OK) return st;
   if ((st = hip_status(launch_clear(P, ws, hs), "clear")) != MITA_OK) return st;
   if ((st = hip_status(launch_route(P, Q, ws, hs), "route")) != MITA_OK) return st;

@@ -13,8 +13,9 @@ constexpr int kMaxLandmarks = 4096;
 constexpr int kLandmarkTile = 64;     // landmarks per workgroup in the shared-expert kernel
 constexpr int kKeyBlock = 64;         // keys per LDS block in the attention kernels
 constexpr int kQueryTile = 64;        // queries per workgroup in the router, gather and combine kernels
-constexpr int kTopkSegMax = 8192;     // scores per workgroup in the segment select kernel
-constexpr int kTopkWaveMax = 4096;    // rows up to this length are selected by one wave each
+constexpr int kTopkMaxGroups = 4096;  // group maxima per score row that the threshold kernel ranks
+constexpr int kTopkMaxCap = 4096;     // candidates per row the select kernel holds (larger k: exact fallback)
+constexpr int kTopkGeneralWaves = 64; // waves (each with an fp64 score row of scratch) of the fallback kernel
 constexpr int kRouteFastMaxS = 6;     // the router keeps per-lane top lists up to this s
 constexpr int kRouteLdsMaxM = 512;    // up to this m, queries the fast router cannot settle are finished in it
 
@@ -27,10 +28,12 @@ struct Layout {
   size_t kmax;      // f32 [BH, nsplit]   upper bound of max_n |K_n|_2 per key chunk
   size_t vt32;      // f32 [BH, m, d]     shared expert V~
   size_t vt16;      // bf16 [BH, m, d]    V~ rounded to bf16 (MFMA operand)
-  size_t S;         // f32 [BH, m, N]     approximate scores q~_i . K_n
-  size_t cand_key;  // u32 [BH * m, N]    per-segment candidates of the top-k select (order keys)
-  size_t cand_idx;  // u32 [BH * m, N]    ... and their token ids
-  size_t cand_cnt;  // u32 [BH * m, G]    candidates per segment
+  size_t bmax;      // f32 [BH * m, nbg]  maxima of groups of approximate scores q~_i . K_n
+  size_t thr;       // u32 [BH * m]       order key of the candidate threshold of each score row
+  size_t cand;      // u32x2 [BH * m, nsplit, capc] candidates (order key, token id) per key chunk
+  size_t ccnt;      // u32 [BH * m, nsplit] candidates per chunk (capc + 1: overflow)
+  size_t glist;     // u32 [BH * m + 1]   rows for the exact fallback, count first
+  size_t gscr;      // f64 [kTopkGeneralWaves, N] fp64 score rows of the fallback
   size_t I;         // i32 [BH, m, k]     expert token sets, ascending
   size_t E;         // i32 [BH, N, s]     routed experts per query
   size_t counters;  // u32 block cleared at the start of routing (below)
@@ -57,8 +60,10 @@ struct Plan {
   int lchunk;       // keys per workgroup (multiple of kKeyBlock)
   int nsplit;       // ceil(N / lchunk)
   // top-k select
-  int seg;          // scores per segment workgroup
-  int G;            // segments per row
+  int gq;           // scores per group maximum: 16 (one lane's share of a key block) or 64 (a whole block)
+  int nbg;          // group maxima per row: ceil(N / 64) * 64 / gq
+  int cap;          // candidates per row the select kernel holds (multiple of 64, or 0: fallback for all rows)
+  int capc;         // candidate slots per (row, key chunk): min(lchunk, cap)
   // router and output
   int qtiles;       // ceil(N / kQueryTile)
   int max_tiles;    // upper bound of query tiles over all buckets of one slice
@@ -73,7 +78,7 @@ mita_status make_plan(const mita_shape* shape, int m, int k, int s, Plan* p, con
 // Kernel launchers (one per step; each returns the first HIP error it meets).
 hipError_t launch_clear(const Plan& p, char* ws, hipStream_t st);
 hipError_t launch_pool(const Plan& p, const void* Q, char* ws, hipStream_t st);
-hipError_t launch_landmark(const Plan& p, const void* K, const void* V, char* ws, hipStream_t st);
+hipError_t launch_landmark(const Plan& p, const void* K, const void* V, char* ws, float* S_out, hipStream_t st);
 hipError_t launch_topk(const Plan& p, const void* K, char* ws, hipStream_t st);
 hipError_t launch_route(const Plan& p, const void* Q, char* ws, hipStream_t st);
 hipError_t launch_bucket(const Plan& p, char* ws, hipStream_t st);

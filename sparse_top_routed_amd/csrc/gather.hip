@@ -225,6 +225,20 @@ struct GatherLds<T, D, false> {
   uint32_t wtot[4];
 };
 
+// LDS of the one-pass kernel: two routed key/value blocks (tile t computes from
+// one while tile t + 1 is written to the other), the slice's landmark block and
+// the workgroup's list of tiles.
+template <typename T, int D>
+struct Gather1Lds {
+  using TL = Tiles<T, D>;
+  __align__(16) T rk[2][TL::KTILE];
+  __align__(16) T rv[2][TL::VTILE];
+  AttnLds<T, D> lm;
+  int4 tile[256];
+  int tz[256];
+  uint32_t wtot[4];
+};
+
 template <typename T, int D, int KP>
 __device__ __forceinline__ void attend_tiles(const T* kt0, const T* kt1, const T* vt, const QFrag<T, D>& qf,
                                              int live, float sl2e, float& mrun, float& lrun, f32x4 (&o)[D / 16],
@@ -472,9 +486,10 @@ __device__ __forceinline__ void block_scores(const T* k0, const T* k1, const QFr
 
 // s = 1 with k <= 64 and m <= 64: every tile is one routed block plus the
 // slice's landmark block, so the softmax over the m + k keys is taken in one
-// pass (no running rescale). Same persistent walk and prefetch distances as
-// gather_kernel: rows of tile t + 1, expert indices of tile t + 2, query rows of
-// tile t + 1 and query ids of tile t + 2 are in flight while tile t computes.
+// pass (no running rescale). Same persistent walk as gather_kernel; the routed
+// blocks are double-buffered in LDS, so each tile needs one barrier. Rows of
+// tile t + 2, expert indices of tile t + 3, query rows of tile t + 1 and query
+// ids of tile t + 2 are in flight while tile t computes.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void gather1_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                       const T* __restrict__ V, const int32_t* __restrict__ I,
@@ -485,7 +500,7 @@ __global__ __launch_bounds__(256) void gather1_kernel(const T* __restrict__ Q, c
   using TL = Tiles<T, D>;
   constexpr bool BF = TL::BF;
   constexpr int KP = BF ? 2 : 1;
-  __shared__ GatherLds<T, D, true> sm;
+  __shared__ Gather1Lds<T, D> sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
   const int rowi = 16 * w + r;
   const long c0 = (long)blockIdx.x * chunk, c1 = min(total, c0 + chunk);
@@ -517,7 +532,13 @@ __global__ __launch_bounds__(256) void gather1_kernel(const T* __restrict__ Q, c
       Kb = K + o;
       Vb = V + o;
     };
+    auto store_rows = [&](const KVRegs<T, D, 1>& R, int b) {
+      R.k[0].store(sm.rk[b], TL::KSTR, tid);
+      if constexpr (BF) R.v.store((uint16_t*)sm.rv[b], tid); else R.v.store(sm.rv[b], TL::VSTR, tid);
+    };
 
+    // prologue: tile 0's rows straight to buffer 0, tile 1's rows in registers,
+    // tile 2's indices in flight
     RowIdx<T, D> ix;
     KVRegs<T, D, 1> RR;
     {
@@ -526,6 +547,10 @@ __global__ __launch_bounds__(256) void gather1_kernel(const T* __restrict__ Q, c
       slice_kv(0, Kb, Vb);
       load_rows<T, D>(RR, ix, Kb, Vb, tid);
       ix.load(expert(1), k, 0, tid);
+      store_rows(RR, 0);
+      slice_kv(1, Kb, Vb);
+      load_rows<T, D>(RR, ix, Kb, Vb, tid);
+      ix.load(expert(2), k, 0, tid);
     }
     int q = qid(0), q_n = qid(1), q_nn = q_n;
     QFrag<T, D> qf;
@@ -533,6 +558,8 @@ __global__ __launch_bounds__(256) void gather1_kernel(const T* __restrict__ Q, c
     QFrag<T, D> qf_n = qf;
     int zl = -1;
 
+    // one barrier per tile: at iteration t the rows of tile t + 1 go to the other
+    // buffer, whose last readers (tile t - 1) finished before the barrier
     for (int t = 0; t < (int)nt; ++t) {
       const int4 cur = sm.tile[t];
       const int zc = sm.tz[t];
@@ -542,27 +569,27 @@ __global__ __launch_bounds__(256) void gather1_kernel(const T* __restrict__ Q, c
         qf = qf_n;
       }
       q_nn = qid(t + 2);
-      __syncthreads();   // readers of the previous tile's blocks are done
-      RR.k[0].store(sm.rk, TL::KSTR, tid);
-      if constexpr (BF) RR.v.store((uint16_t*)sm.rv, tid); else RR.v.store(sm.rv, TL::VSTR, tid);
+      __syncthreads();
+      store_rows(RR, (t + 1) & 1);
       if (zc != zl) {   // the slice's landmark block (uniform branch)
         KVRegs<T, D, KP> LR;
         load_landmarks<T, D>(LR, qtop, vtop, zc, m, 0, tid);
         LR.store(sm.lm, tid);
         zl = zc;
+        __syncthreads();
       }
-      __syncthreads();
-      {   // rows of tile t + 1 (indices in hand), indices of tile t + 2, query rows of tile t + 1
+      {   // rows of tile t + 2 (indices in hand), indices of tile t + 3, query rows of tile t + 1
         const T *Kb, *Vb;
-        slice_kv(t + 1, Kb, Vb);
+        slice_kv(t + 2, Kb, Vb);
         load_rows<T, D>(RR, ix, Kb, Vb, tid);
-        ix.load(expert(t + 2), k, 0, tid);
+        ix.load(expert(t + 3), k, 0, tid);
         qf_n.load(Q + ((size_t)sm.tz[min(t + 1, last)] * N + q_n) * D, g);
       }
       if (16 * w < cur.z) {   // wave has live rows (uniform)
+        const int b = t & 1;
         f32x4 xl[4], xr[4];
         block_scores<T, D, KP>(sm.lm.k0, sm.lm.k1, qf, m, xl, lane);
-        block_scores<T, D, 1>(sm.rk, nullptr, qf, k, xr, lane);
+        block_scores<T, D, 1>(sm.rk[b], nullptr, qf, k, xr, lane);
         float mx = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
@@ -583,10 +610,10 @@ __global__ __launch_bounds__(256) void gather1_kernel(const T* __restrict__ Q, c
         for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         if constexpr (BF) {
           pv_bf16<D>((const uint16_t*)sm.lm.v, xl, o, lane);
-          pv_bf16<D>((const uint16_t*)sm.rv, xr, o, lane);
+          pv_bf16<D>((const uint16_t*)sm.rv[b], xr, o, lane);
         } else {
           pv_f32<D>((const float*)sm.lm.v, xl, o, lane);
-          pv_f32<D>((const float*)sm.rv, xr, o, lane);
+          pv_f32<D>((const float*)sm.rv[b], xr, o, lane);
         }
         const float inv = 1.f / quad_sum(l);
         if (rowi < cur.z) {
@@ -696,7 +723,9 @@ static hipError_t gather_launch(const Plan& p, const void* Q, const void* K, con
   const int groups = (int)std::min<long>(total, slots);
   const int chunk = (int)((total + groups - 1) / groups);
   const int grid = (int)((total + chunk - 1) / chunk);
-  if (p.s == 1 && p.k <= kKeyBlock && p.m <= kKeyBlock) {
+  // the one-pass kernel where its double-buffered LDS fits a workgroup
+  constexpr bool one_pass_fits = sizeof(Gather1Lds<T, D>) <= 160 * 1024;
+  if constexpr (one_pass_fits) if (p.s == 1 && p.k <= kKeyBlock && p.m <= kKeyBlock) {
     static int occ1 = 0;
     if (occ1 == 0 && hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ1, gather1_kernel<T, D>, 256, 0) != hipSuccess)
       occ1 = 1;

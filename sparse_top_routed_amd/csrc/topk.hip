@@ -220,23 +220,30 @@ __global__ __launch_bounds__(256) void topk_cand_kernel(const T* __restrict__ K,
 }
 
 // ---------------------------------------------------------------- 3. select
-// One wave per row. The row's candidate lists (index order, chunk after chunk)
-// go to LDS; candidate j is slot j / 64 of lane j % 64 in registers.
-template <typename T, int D, int CAP>
-__global__ __launch_bounds__(64) void topk_select_kernel(const uint2* __restrict__ cand,
-                                                         const uint32_t* __restrict__ ccnt,
-                                                         const float* __restrict__ qtnorm,
-                                                         const float* __restrict__ kmax, int nsplit,
-                                                         const double* __restrict__ qt64, const T* __restrict__ K,
-                                                         int32_t* __restrict__ I, uint32_t* __restrict__ glist,
-                                                         int N, int m, int k, int capc, double gamma) {
+// One wave per row (WPB rows per workgroup). The row's candidate lists (index
+// order, chunk after chunk) go to LDS; candidate j is slot j / 64 of lane j % 64
+// in registers.
+template <typename T, int D, int CAP, int WPB>
+__global__ __launch_bounds__(64 * WPB) void topk_select_kernel(const uint2* __restrict__ cand,
+                                                               const uint32_t* __restrict__ ccnt,
+                                                               const float* __restrict__ qtnorm,
+                                                               const float* __restrict__ kmax, int nsplit,
+                                                               const double* __restrict__ qt64,
+                                                               const T* __restrict__ K, int32_t* __restrict__ I,
+                                                               uint32_t* __restrict__ glist, int N, int m, int k,
+                                                               int capc, double gamma, int rows) {
   constexpr int SL = CAP / 64;
   constexpr int BAND = CAP < kBandMax ? CAP : kBandMax;
-  __shared__ uint2 cs[CAP];
-  __shared__ uint32_t blist[BAND];
-  __shared__ double bsc[BAND];
-  __shared__ uint8_t bkeep[BAND];
-  const int lane = threadIdx.x, row = blockIdx.x, z = row / m;
+  __shared__ uint2 cs_s[WPB][CAP];
+  __shared__ uint32_t blist_s[WPB][BAND];
+  __shared__ double bsc_s[WPB][BAND];
+  __shared__ uint8_t bkeep_s[WPB][BAND];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, row = blockIdx.x * WPB + w, z = row / m;
+  if (row >= rows) return;   // wave-uniform; the waves of a workgroup never synchronise
+  uint2* cs = cs_s[w];
+  uint32_t* blist = blist_s[w];
+  double* bsc = bsc_s[w];
+  uint8_t* bkeep = bkeep_s[w];
   const uint32_t* cnt = ccnt + (size_t)row * nsplit;
   const uint2* segs = cand + (size_t)row * nsplit * capc;
   auto fallback = [&]() {
@@ -256,6 +263,7 @@ __global__ __launch_bounds__(64) void topk_select_kernel(const uint2* __restrict
     if (c < nsplit && c < BAND) blist[c] = total + ex;
     total += tot;
   }
+  total = __builtin_amdgcn_readfirstlane(total);   // wave-uniform: keep the loops below scalar
   if (__any(over) || total > (uint32_t)CAP || nsplit > BAND) {
     fallback();
     return;
@@ -269,7 +277,7 @@ __global__ __launch_bounds__(64) void topk_select_kernel(const uint2* __restrict
   }
   wave_sync();
   const double E = row_bound(qtnorm, kmax, nsplit, row, z, gamma, lane);
-  const int ns = (int)((total + 63) / 64);
+  const int ns = __builtin_amdgcn_readfirstlane((int)((total + 63) / 64));
   uint32_t ck[SL];
 #pragma unroll
   for (int sl = 0; sl < SL; ++sl) {
@@ -302,6 +310,8 @@ __global__ __launch_bounds__(64) void topk_select_kernel(const uint2* __restrict
       nb += (uint32_t)__popcll(msk);
     }
   }
+  nb = __builtin_amdgcn_readfirstlane(nb);
+  cin = __builtin_amdgcn_readfirstlane(cin);
   if (nb > (uint32_t)BAND) {
     fallback();
     return;
@@ -474,18 +484,18 @@ static hipError_t topk_launch(const Plan& p, const void* K, char* ws, hipStream_
                        (const void*)(ws + p.ws.qtop), (const uint32_t*)(ws + p.ws.thr), (uint2*)(ws + p.ws.cand),
                        (uint32_t*)(ws + p.ws.ccnt), p.N, p.m, p.lchunk, p.nsplit, p.capc);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    auto sel = [&](auto kern) {
-      hipLaunchKernelGGL(kern, dim3(rows), dim3(64), 0, st, (const uint2*)(ws + p.ws.cand),
+    auto sel = [&](auto kern, int wpb) {
+      hipLaunchKernelGGL(kern, dim3((rows + wpb - 1) / wpb), dim3(64 * wpb), 0, st, (const uint2*)(ws + p.ws.cand),
                          (const uint32_t*)(ws + p.ws.ccnt), (const float*)(ws + p.ws.qtnorm),
                          (const float*)(ws + p.ws.kmax), p.nsplit, (const double*)(ws + p.ws.qt64), (const T*)K,
-                         (int32_t*)(ws + p.ws.I), glist, p.N, p.m, p.k, p.capc, p.gamma_qk);
+                         (int32_t*)(ws + p.ws.I), glist, p.N, p.m, p.k, p.capc, p.gamma_qk, rows);
     };
-    switch (p.cap) {
-      case 256: sel(topk_select_kernel<T, D, 256>); break;
-      case 512: sel(topk_select_kernel<T, D, 512>); break;
-      case 1024: sel(topk_select_kernel<T, D, 1024>); break;
-      case 2048: sel(topk_select_kernel<T, D, 2048>); break;
-      default: sel(topk_select_kernel<T, D, 4096>); break;
+    switch (p.cap) {   // LDS per wave grows with the capacity: fewer rows per workgroup
+      case 256: sel(topk_select_kernel<T, D, 256, 4>, 4); break;
+      case 512: sel(topk_select_kernel<T, D, 512, 4>, 4); break;
+      case 1024: sel(topk_select_kernel<T, D, 1024, 2>, 2); break;
+      case 2048: sel(topk_select_kernel<T, D, 2048, 1>, 1); break;
+      default: sel(topk_select_kernel<T, D, 4096, 1>, 1); break;
     }
   } else {
     hipLaunchKernelGGL(topk_all_rows_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, glist, rows);

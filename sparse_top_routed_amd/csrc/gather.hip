@@ -496,18 +496,32 @@ __global__ __launch_bounds__(256) void gather1_kernel(const T* __restrict__ Q, c
                                                       const int4* __restrict__ tiles, const int32_t* __restrict__ perm,
                                                       const void* __restrict__ qtop, const void* __restrict__ vtop,
                                                       T* __restrict__ out, int N, int m, int k, int max_tiles,
-                                                      long total, int chunk, float sl2e) {
+                                                      int BH, int gs, float sl2e) {
   using TL = Tiles<T, D>;
   constexpr bool BF = TL::BF;
   constexpr int KP = BF ? 2 : 1;
   __shared__ Gather1Lds<T, D> sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
   const int rowi = 16 * w + r;
-  const long c0 = (long)blockIdx.x * chunk, c1 = min(total, c0 + chunk);
+  // Workgroups go round-robin to the 8 XCDs. The gs workgroups of a group (all
+  // on one XCD) share one slice at a time, each taking every gs-th entry of its
+  // tile table, so the slice's gathered rows, which recur across experts, are
+  // served from that XCD's L2.
+  const int xcd = blockIdx.x % 8, jx = blockIdx.x / 8, gpx = (int)(gridDim.x / 8) / gs;
+  if (jx >= gpx * gs) return;   // workgroup-uniform
+  const int grp = xcd * gpx + jx / gs, jj = jx % gs, ngroups = 8 * gpx;
+  const int per = (max_tiles + gs - 1) / gs;
+  // this workgroup's entries, slice after slice: entry e is table entry
+  // jj + gs (e % per) of slice grp + (e / per) ngroups (interleaved, because the
+  // real tiles sit at the front of each slice's table)
+  const long nent = (long)((BH - grp + ngroups - 1) / ngroups) * per;
 
-  for (long base = c0; base < c1; base += 256) {
-    const long ent = base + tid;
-    const int4 te = ent < c1 ? tiles[ent] : make_int4(-1, 0, 0, 0);
+  for (long base = 0; base < nent; base += 256) {
+    const long e = base + tid;
+    const int zs = grp + (int)(e / per) * ngroups, off = jj + gs * (int)(e % per);
+    const bool in = e < nent && zs < BH && off < max_tiles;
+    const long ent = in ? (long)zs * max_tiles + off : 0;
+    const int4 te = in ? tiles[ent] : make_int4(-1, 0, 0, 0);
     const uint32_t f = te.x >= 0 ? 1u : 0u;
     uint32_t nt;
     const uint32_t pos = block_incl_scan(f, sm.wtot, nt) - f;
@@ -556,7 +570,9 @@ __global__ __launch_bounds__(256) void gather1_kernel(const T* __restrict__ Q, c
     QFrag<T, D> qf;
     qf.load(Q + ((size_t)sm.tz[0] * N + q) * D, g);
     QFrag<T, D> qf_n = qf;
-    int zl = -1;
+    int zl = -1, zn = sm.tz[0];   // slice in the landmark buffer; slice whose block is in LR
+    KVRegs<T, D, KP> LR;          // the next slice's landmark block, fetched a tile ahead
+    load_landmarks<T, D>(LR, qtop, vtop, zn, m, 0, tid);
 
     // one barrier per tile: at iteration t the rows of tile t + 1 go to the other
     // buffer, whose last readers (tile t - 1) finished before the barrier
@@ -571,12 +587,18 @@ __global__ __launch_bounds__(256) void gather1_kernel(const T* __restrict__ Q, c
       q_nn = qid(t + 2);
       __syncthreads();
       store_rows(RR, (t + 1) & 1);
-      if (zc != zl) {   // the slice's landmark block (uniform branch)
-        KVRegs<T, D, KP> LR;
-        load_landmarks<T, D>(LR, qtop, vtop, zc, m, 0, tid);
+      if (zc != zl) {   // a new slice: its landmark block (uniform branch)
+        if (zn != zc) load_landmarks<T, D>(LR, qtop, vtop, zc, m, 0, tid);
         LR.store(sm.lm, tid);
         zl = zc;
         __syncthreads();
+      }
+      {   // the landmark block of the next tile's slice, when that changes
+        const int z1 = sm.tz[min(t + 1, last)];
+        if (z1 != zl && z1 != zn) {
+          load_landmarks<T, D>(LR, qtop, vtop, z1, m, 0, tid);
+          zn = z1;
+        }
       }
       {   // rows of tile t + 2 (indices in hand), indices of tile t + 3, query rows of tile t + 1
         const T *Kb, *Vb;
@@ -729,12 +751,13 @@ static hipError_t gather_launch(const Plan& p, const void* Q, const void* K, con
     static int occ1 = 0;
     if (occ1 == 0 && hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ1, gather1_kernel<T, D>, 256, 0) != hipSuccess)
       occ1 = 1;
-    const int g1 = (int)std::min<long>(total, (long)n_cu * std::max(1, occ1));
-    const int ch1 = (int)((total + g1 - 1) / g1);
-    hipLaunchKernelGGL((gather1_kernel<T, D>), dim3((int)((total + ch1 - 1) / ch1)), dim3(256), 0, st, (const T*)Q,
-                       (const T*)K, (const T*)V, (const int32_t*)(ws + p.ws.I), (const int4*)(ws + p.ws.tiles),
-                       (const int32_t*)(ws + p.ws.perm), (const void*)(ws + p.ws.qtop), vtop, (T*)out, p.N, p.m, p.k,
-                       p.max_tiles, total, ch1, sl2e);
+    // resident workgroups in groups of up to 16 per XCD-slice (a multiple of 8 x gs)
+    const int slots = n_cu * std::max(1, occ1);
+    const int gs = std::max(1, std::min(8, slots / 8));
+    const int g1 = std::max(8 * gs, slots / (8 * gs) * 8 * gs);
+    hipLaunchKernelGGL((gather1_kernel<T, D>), dim3(g1), dim3(256), 0, st, (const T*)Q, (const T*)K, (const T*)V,
+                       (const int32_t*)(ws + p.ws.I), (const int4*)(ws + p.ws.tiles), (const int32_t*)(ws + p.ws.perm),
+                       (const void*)(ws + p.ws.qtop), vtop, (T*)out, p.N, p.m, p.k, p.max_tiles, p.BH, gs, sl2e);
     return hipGetLastError();
   }
   if (p.s == 1) {

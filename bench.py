@@ -29,12 +29,14 @@ def step_bytes(w) -> dict:
     e = 2 if w.dtype == "bf16" else 4
     BH, N, d, m, k, s = w.slices, w.N, w.d, w.m, w.k, w.s
     tok = BH * N * d * e
+    nblk = -(-N // 64)
+    nbg = nblk * (1 if nblk >= 4 * k else 4)   # group maxima per score row (groups of 64 or 16 scores)
     return {
         "pool": tok + BH * m * d * (8 + 4 + 4),
-        # K and V read once, score rows written once (fp32), shared-expert partials
-        "landmark": 2 * tok + BH * m * N * 4,
-        # score rows read once, expert lists written
-        "topk": BH * m * N * 4 + BH * m * k * 4,
+        # K and V read once, group maxima of the score rows written once
+        "landmark": 2 * tok + BH * m * nbg * 4,
+        # group maxima read, K read once more (candidate pass), expert lists written
+        "topk": BH * m * nbg * 4 + tok + BH * m * k * 4,
         "route": tok + BH * N * s * 4,
         # Q read, each expert's k gathered K/V rows once, output written (+ partials when s > 1)
         "gather": 2 * tok + BH * m * k * d * e * 2 + (BH * N * s * (d + 2) * 4 * 2 if s > 1 else 0),
@@ -46,7 +48,7 @@ def step_bytes(w) -> dict:
 # was measured on.
 KERNEL_SOURCES = {
     "gather": ["sparse_top_routed_amd/csrc/gather.hip", "sparse_top_routed_amd/csrc/attn_core.h"],
-    "topk": ["sparse_top_routed_amd/csrc/topk.hip"],
+    "topk": ["sparse_top_routed_amd/csrc/topk.hip", "sparse_top_routed_amd/csrc/attn_core.h"],
     "route": ["sparse_top_routed_amd/csrc/route.hip", "sparse_top_routed_amd/csrc/attn_core.h"],
     "landmark": ["sparse_top_routed_amd/csrc/landmark.hip", "sparse_top_routed_amd/csrc/attn_core.h"],
     "pool": ["sparse_top_routed_amd/csrc/pool.hip"],
@@ -54,7 +56,7 @@ KERNEL_SOURCES = {
 COMMON_SOURCES = ["sparse_top_routed_amd/csrc/common.h", "sparse_top_routed_amd/csrc/plan.h",
                   "sparse_top_routed_amd/build.py"]
 KERNEL_NAMES = {
-    "gather": "gather_kernel", "topk": "topk_wave_kernel", "route": "route_fast_kernel",
+    "gather": "gather1_kernel", "topk": "topk_cand_kernel", "route": "route_fast_kernel",
     "landmark": "landmark_kernel", "pool": "pool_kernel",
 }
 

@@ -66,8 +66,8 @@ typedef struct {
 
 /* Bytes of device workspace that mita_forward and the step entry points need for
  * this shape and (m, k, s); 0 if the arguments are invalid. The workspace holds
- * every intermediate (landmarks, the m x N score rows, expert sets, routing,
- * buckets and partial outputs) and must be 256-byte aligned. */
+ * every intermediate (landmarks, score-group maxima, top-k candidates, expert
+ * sets, routing, buckets and partial outputs) and must be 256-byte aligned. */
 size_t mita_workspace_bytes(const mita_shape* shape, int m, int k, int s);
 
 /* Whole forward pass, steps 1-5: out = MiTA(Q, K, V) with m landmarks, experts of
@@ -88,16 +88,21 @@ mita_status mita_forward(const void* Q, const void* K, const void* V, int m, int
 mita_status mita_pool(const void* Q, int m, int k, int s, const mita_shape* shape, void* workspace,
                       size_t workspace_bytes, double* Qt_out, void* stream);
 
-/* Step 2 (shared expert and score rows). Vt_out: fp32 [B, H, m, d], the shared
- * expert V~. S_out: fp32 [B, H, m, N], the unscaled scores q~_i . K_n as computed
- * on the GPU (fp32 accumulation, used to rank tokens before exact refinement). */
+/* Step 2 (shared expert). Vt_out: fp32 [B, H, m, d], the shared expert V~
+ * (copied from the workspace). The m x N score rows q~_i . K_n are not kept; the
+ * step leaves maxima of groups of them for step 3. S_out, when not NULL, is a
+ * device buffer (fp32 [B, H, m, N], 16-byte aligned) that the kernel fills with
+ * the unscaled scores as computed on the GPU (fp32 accumulation), for checking. */
 mita_status mita_landmark(const void* K, const void* V, int m, int k, int s, const mita_shape* shape,
                           void* workspace, size_t workspace_bytes, float* Vt_out, float* S_out, void* stream);
 
 /* Step 3 (deformable experts). I_out: int32 [B, H, m, k], each row the k token
- * ids of expert i in ascending order. Selection is exact: candidates whose fp32
- * score lies within a proven error bound of the k-th largest are re-scored in
- * fp64 before the cut. */
+ * ids of expert i in ascending order. Selection is exact: the scores are
+ * recomputed and only those above a per-row threshold (set from the group
+ * maxima of step 2, minus the error bound) are kept as candidates; candidates
+ * whose fp32 score lies within a proven error bound of the k-th largest are
+ * re-scored in fp64 before the cut. Rows with too many candidates (massive
+ * ties) are selected from fp64 scores of the whole row. */
 mita_status mita_topk(const void* K, int m, int k, int s, const mita_shape* shape, void* workspace,
                       size_t workspace_bytes, int32_t* I_out, void* stream);
 

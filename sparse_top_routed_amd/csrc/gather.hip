@@ -570,9 +570,7 @@ __global__ __launch_bounds__(256) void gather1_kernel(const T* __restrict__ Q, c
     QFrag<T, D> qf;
     qf.load(Q + ((size_t)sm.tz[0] * N + q) * D, g);
     QFrag<T, D> qf_n = qf;
-    int zl = -1, zn = sm.tz[0];   // slice in the landmark buffer; slice whose block is in LR
-    KVRegs<T, D, KP> LR;          // the next slice's landmark block, fetched a tile ahead
-    load_landmarks<T, D>(LR, qtop, vtop, zn, m, 0, tid);
+    int zl = -1;   // slice in the landmark buffer
 
     // one barrier per tile: at iteration t the rows of tile t + 1 go to the other
     // buffer, whose last readers (tile t - 1) finished before the barrier
@@ -588,17 +586,11 @@ __global__ __launch_bounds__(256) void gather1_kernel(const T* __restrict__ Q, c
       __syncthreads();
       store_rows(RR, (t + 1) & 1);
       if (zc != zl) {   // a new slice: its landmark block (uniform branch)
-        if (zn != zc) load_landmarks<T, D>(LR, qtop, vtop, zc, m, 0, tid);
+        KVRegs<T, D, KP> LR;
+        load_landmarks<T, D>(LR, qtop, vtop, zc, m, 0, tid);
         LR.store(sm.lm, tid);
         zl = zc;
         __syncthreads();
-      }
-      {   // the landmark block of the next tile's slice, when that changes
-        const int z1 = sm.tz[min(t + 1, last)];
-        if (z1 != zl && z1 != zn) {
-          load_landmarks<T, D>(LR, qtop, vtop, z1, m, 0, tid);
-          zn = z1;
-        }
       }
       {   // rows of tile t + 2 (indices in hand), indices of tile t + 3, query rows of tile t + 1
         const T *Kb, *Vb;

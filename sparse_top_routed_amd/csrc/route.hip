@@ -396,6 +396,195 @@ __global__ __launch_bounds__(256) void route_fast_kernel(const T* __restrict__ Q
   }
 }
 
+// Fast router for m > 64: a workgroup takes TPW query tiles at once (their query
+// fragments and top lists stay in registers) and streams the landmark blocks
+// through LDS once for all of them, so each block is staged once per TPW tiles.
+// Deciding a query is as in route_fast_kernel's list path: certain, band
+// re-scored in fp64 when the list holds it, else queued (to the end of this
+// workgroup when TAIL, else to the exact kernel).
+template <typename T, int D, int TM, int TPW, bool TAIL>
+__global__ __launch_bounds__(256) void route_multi_kernel(const T* __restrict__ Q, const void* __restrict__ qtop,
+                                                          const double* __restrict__ qt64,
+                                                          const float* __restrict__ qtnorm, int32_t* __restrict__ E,
+                                                          uint32_t* __restrict__ counters,
+                                                          uint32_t* __restrict__ rflag, int N, int m, int s,
+                                                          double gamma, int qtiles) {
+  using TL = Tiles<T, D>;
+  constexpr bool BF = TL::BF;
+  __shared__ __align__(16) T Ks0[TL::KTILE];
+  __shared__ __align__(16) T Ks1[BF ? TL::KTILE : 8];
+  __shared__ float s_red[4];
+  __shared__ int s_nq;
+  __shared__ int s_q[TAIL ? TPW * kQueryTile : 1];
+  __shared__ double s_x[TAIL ? 4 * (kRouteLdsMaxM + D) : 1];
+  const int z = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
+  const int t0 = blockIdx.x * TPW;
+  const T* plane0 = BF ? (const T*)((const uint16_t*)qtop + (size_t)z * 2 * m * D) : (const T*)((const float*)qtop + (size_t)z * m * D);
+  const T* plane1 = BF ? plane0 + (size_t)m * D : plane0;
+  const double* qt64z = qt64 + (size_t)z * m * D;
+
+  // query fragments of the TPW tiles (tiles past the end repeat the last row)
+  uint4 qb[TPW][1][D / 32];
+  float qf[TPW][D / 4];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int q = min((t0 + tt) * kQueryTile + 16 * w + r, N - 1);
+    const T* qrow = Q + ((size_t)z * N + q) * D;
+    if constexpr (BF) {
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) qb[tt][0][ks] = ld16(qrow + 32 * ks + 8 * g);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < D / 4; ++ks) qf[tt][ks] = qrow[4 * ks + g];
+    }
+  }
+  float qtm = 0.f;
+  for (int i = tid; i < m; i += 256) qtm = fmaxf(qtm, qtnorm[(size_t)z * m + i]);
+  qtm = wave_max(qtm);
+  if (lane == 0) s_red[w] = qtm;
+  if (tid == 0) s_nq = 0;
+
+  float tv[TPW][TM];
+  int ti[TPW][TM];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) { tv[tt][j] = -INFINITY; ti[tt][j] = 0x7FFFFFFF; }
+  for (int lb0 = 0; lb0 < m; lb0 += kKeyBlock) {
+    __syncthreads();   // readers of the previous block are done
+    const int nvalid = min(kKeyBlock, m - lb0);
+    stage_rows<T, D>(Ks0, TL::KSTR, [&](int rr) { return plane0 + (size_t)(lb0 + rr) * D; }, nvalid, tid);
+    if constexpr (BF)
+      stage_rows<T, D>(Ks1, TL::KSTR, [&](int rr) { return plane1 + (size_t)(lb0 + rr) * D; }, nvalid, tid);
+    __syncthreads();
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      f32x4 acc[4];
+      if constexpr (BF)
+        qk_bf16<D, 2, 1>((const uint16_t*)Ks0, (const uint16_t*)Ks1, qb[tt], acc, lane);
+      else
+        qk_f32<D>((const float*)Ks0, qf[tt], acc, lane);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int li = lb0 + 16 * kt + 4 * g + j;   // past m: -inf never enters the list
+          list_insert_ordered<TM>(tv[tt], ti[tt], li < m ? acc[kt][j] : -INFINITY, li);
+        }
+    }
+  }
+  const double qtmax = (double)fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int q = (t0 + tt) * kQueryTile + 16 * w + r;
+    const bool q_ok = (t0 + tt) < qtiles && q < N;
+    const T* qrow = Q + ((size_t)z * N + min(q, N - 1)) * D;
+#pragma unroll
+    for (int sh = 16; sh <= 32; sh <<= 1) {
+      float ov[TM];
+      int oi[TM];
+#pragma unroll
+      for (int j = 0; j < TM; ++j) { ov[j] = __shfl_xor(tv[tt][j], sh, WAVE); oi[j] = __shfl_xor(ti[tt][j], sh, WAVE); }
+#pragma unroll
+      for (int j = 0; j < TM; ++j) list_insert<TM>(tv[tt], ti[tt], ov[j], oi[j]);
+    }
+    float sq = 0.f;
+    if constexpr (BF) {
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const uint16_t* h = (const uint16_t*)&qb[tt][0][ks];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { const float x = bf16_to_f32(h[e]); sq = fmaf(x, x, sq); }
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < D / 4; ++ks) sq = fmaf(qf[tt][ks], qf[tt][ks], sq);
+    }
+    const float qn = sqrtf(quad_sum(sq)) * 1.0001f;
+    const double Eq = gamma * (double)qn * qtmax;
+    float v_s = -INFINITY, v_s1 = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      if (j == s - 1) v_s = tv[tt][j];
+      if (j == s) v_s1 = tv[tt][j];
+    }
+    const double That = (double)v_s, lo = That - 2.0 * Eq, hi = That + 2.0 * Eq;
+    const bool certain = s >= m || (double)v_s - (double)v_s1 > 2.0 * Eq;
+    int32_t* Eq_out = E + ((size_t)z * N + min(q, N - 1)) * s;
+    if (q_ok && g == 0 && certain) {
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+        if (j < s) Eq_out[j] = ti[tt][j];
+    }
+    const bool unc = q_ok && !certain;
+    if (!__any(unc)) continue;
+    int c_in = 0;
+#pragma unroll
+    for (int j = 0; j < TM; ++j) c_in += (j < s && (double)tv[tt][j] > hi) ? 1 : 0;
+    const int need = s - c_in;
+    if (unc && g == 0) {
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+        if (j < c_in) Eq_out[j] = ti[tt][j];
+    }
+    const bool refine = unc && (m <= TM || (double)tv[tt][TM - 1] < lo);
+    if (unc && !refine && g == 0) {
+      if (TAIL) {
+        s_q[atomicAdd(&s_nq, 1)] = q;
+      } else {
+        const uint32_t pos = atomicAdd(&counters[0], 1u);
+        rflag[pos] = (uint32_t)(z * N + q);
+      }
+    }
+    if (__any(refine)) {
+      double s64[TM];
+      bool band[TM];
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        const double v = (double)tv[tt][j];
+        band[j] = refine && ti[tt][j] < m && v >= lo && v <= hi;
+        const double* qr = qt64z + (size_t)(band[j] ? ti[tt][j] : 0) * D;
+        double part = 0.0;
+        if constexpr (BF) {
+#pragma unroll
+          for (int ks = 0; ks < D / 32; ++ks) {
+            const uint16_t* h = (const uint16_t*)&qb[tt][0][ks];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part = fma(qr[32 * ks + 8 * g + e], (double)bf16_to_f32(h[e]), part);
+          }
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < D / 4; ++ks) part = fma(qr[4 * ks + g], (double)qf[tt][ks], part);
+        }
+        part += __shfl_xor(part, 16, WAVE);
+        s64[j] = part + __shfl_xor(part, 32, WAVE);
+      }
+      if (refine && g == 0) {
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+          if (!band[j]) continue;
+          int rank = 0;
+#pragma unroll
+          for (int f = 0; f < TM; ++f)
+            rank += (band[f] && ((s64[f] > s64[j]) | ((s64[f] == s64[j]) & (ti[tt][f] < ti[tt][j])))) ? 1 : 0;
+          if (rank < need) Eq_out[c_in + rank] = ti[tt][j];
+        }
+      }
+    }
+  }
+  if constexpr (TAIL) {   // this workgroup's queued queries, one wave each
+    __syncthreads();
+    const int nq = s_nq;
+    double* r64 = s_x + w * (kRouteLdsMaxM + D);
+    for (int e = w; e < nq; e += 4) {
+      const int q = s_q[e];
+      exact_route_wave<T, D, 16>(Q + ((size_t)z * N + q) * D, qt64z, m, s, E + ((size_t)z * N + q) * s, r64,
+                                 r64 + kRouteLdsMaxM, lane);
+    }
+  }
+}
+
 // Exact routing kernel: one wave per query (up to four per workgroup), for the
 // queries the fast kernel queued or for all queries when `list` is NULL (s > 6).
 template <typename T, int D>
@@ -419,17 +608,25 @@ __global__ __launch_bounds__(256) void route_exact_kernel(const T* __restrict__ 
 // Where the queries the fast kernel cannot settle are finished: m <= 64 in the
 // fast kernel itself (all scores at hand); up to kRouteLdsMaxM at the end of each
 // query tile of the fast kernel; beyond that by the exact kernel.
-template <typename T, int D, int TM>
+template <typename T, int D, int TM, bool RES>
 static hipError_t route_fast_launch(const Plan& p, const void* Q, char* ws, hipStream_t st) {
-  const bool res = p.m <= kKeyBlock, tail = !res && p.m <= kRouteLdsMaxM;
-  const int tpw = res ? 4 : 1;   // several query tiles per workgroup when the landmarks stay staged
-  const dim3 grid((p.qtiles + tpw - 1) / tpw, p.BH);
-  auto kern = res ? route_fast_kernel<T, D, TM, true, false>
-                  : (tail ? route_fast_kernel<T, D, TM, false, true> : route_fast_kernel<T, D, TM, false, false>);
-  hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, (const T*)Q, (const void*)(ws + p.ws.qtop),
-                     (const double*)(ws + p.ws.qt64), (const float*)(ws + p.ws.qtnorm), (int32_t*)(ws + p.ws.E),
-                     (uint32_t*)(ws + p.ws.counters), (uint32_t*)(ws + p.ws.rflag), p.N, p.m, p.s, p.gamma_qk,
-                     p.qtiles, tpw);
+  if constexpr (RES) {
+    const int tpw = 4;   // several query tiles per workgroup: the landmarks stay staged
+    hipLaunchKernelGGL((route_fast_kernel<T, D, TM, true, false>), dim3((p.qtiles + tpw - 1) / tpw, p.BH), dim3(256), 0,
+                       st, (const T*)Q, (const void*)(ws + p.ws.qtop), (const double*)(ws + p.ws.qt64),
+                       (const float*)(ws + p.ws.qtnorm), (int32_t*)(ws + p.ws.E), (uint32_t*)(ws + p.ws.counters),
+                       (uint32_t*)(ws + p.ws.rflag), p.N, p.m, p.s, p.gamma_qk, p.qtiles, tpw);
+  } else {
+    // landmark blocks streamed once per TPW query tiles (fewer when the query
+    // fragments of all TPW tiles would crowd the registers)
+    constexpr int TPW = (sizeof(T) == 2 && D == 64) ? 4 : 2;
+    // the rare queries the lists cannot settle go to the exact kernel (an in-kernel
+    // exact pass would cost every workgroup its registers)
+    hipLaunchKernelGGL((route_multi_kernel<T, D, TM, TPW, false>), dim3((p.qtiles + TPW - 1) / TPW, p.BH), dim3(256), 0, st, (const T*)Q,
+                       (const void*)(ws + p.ws.qtop), (const double*)(ws + p.ws.qt64), (const float*)(ws + p.ws.qtnorm),
+                       (int32_t*)(ws + p.ws.E), (uint32_t*)(ws + p.ws.counters), (uint32_t*)(ws + p.ws.rflag), p.N,
+                       p.m, p.s, p.gamma_qk, p.qtiles);
+  }
   return hipGetLastError();
 }
 
@@ -438,14 +635,23 @@ static hipError_t route_launch(const Plan& p, const void* Q, char* ws, hipStream
   hipError_t e = hipSuccess;
   const bool fast = p.s <= kRouteFastMaxS;
   if (fast) {
-    // lists of s + 1 entries: enough to certify the set (m <= 64 re-scores the
-    // band from the scores in registers; larger m queues what the list cannot settle)
-    if (p.s == 1) e = route_fast_launch<T, D, 2>(p, Q, ws, st);
-    else if (p.s == 2) e = route_fast_launch<T, D, 3>(p, Q, ws, st);
-    else if (p.s <= 4) e = route_fast_launch<T, D, 5>(p, Q, ws, st);
-    else e = route_fast_launch<T, D, 7>(p, Q, ws, st);
+    // m <= 64: lists of s + 1 entries certify the set, and the band is re-scored
+    // from the scores in registers. Larger m: lists of s + 2, so that the band
+    // of an uncertain query usually ends inside the list and is re-scored
+    // there; the rest is queued.
+    if (p.m <= kKeyBlock) {
+      if (p.s == 1) e = route_fast_launch<T, D, 2, true>(p, Q, ws, st);
+      else if (p.s == 2) e = route_fast_launch<T, D, 3, true>(p, Q, ws, st);
+      else if (p.s <= 4) e = route_fast_launch<T, D, 5, true>(p, Q, ws, st);
+      else e = route_fast_launch<T, D, 7, true>(p, Q, ws, st);
+    } else {
+      if (p.s == 1) e = route_fast_launch<T, D, 3, false>(p, Q, ws, st);
+      else if (p.s == 2) e = route_fast_launch<T, D, 4, false>(p, Q, ws, st);
+      else if (p.s <= 4) e = route_fast_launch<T, D, 6, false>(p, Q, ws, st);
+      else e = route_fast_launch<T, D, 8, false>(p, Q, ws, st);
+    }
     if (e != hipSuccess) return e;
-    if (p.m <= kRouteLdsMaxM) return hipSuccess;
+    if (p.m <= kKeyBlock) return hipSuccess;   // settled in the fast kernel
   }
   const int total = p.BH * p.N;
   const int nw = (size_t)4 * (p.m + p.d) * 8 <= 65536 ? 4 : 1;   // LDS: m scores + the query row per wave

@@ -17,7 +17,6 @@ constexpr int kTopkMaxGroups = 4096;  // group maxima per score row that the thr
 constexpr int kTopkMaxCap = 4096;     // candidates per row the select kernel holds (larger k: exact fallback)
 constexpr int kTopkGeneralWaves = 64; // waves (each with an fp64 score row of scratch) of the fallback kernel
 constexpr int kRouteFastMaxS = 6;     // the router keeps per-lane top lists up to this s
-constexpr int kRouteLdsMaxM = 512;    // up to this m, queries the fast router cannot settle are finished in it
 
 // Workspace offsets (bytes) of every intermediate buffer.
 struct Layout {

@@ -3,15 +3,15 @@
 // subset of the deformable experts without giving the rule; this dot-product
 // top-s is the reading taken).
 //
-// Fast kernel (s <= 6): a workgroup takes 64 queries (16 per wave); landmark
-// blocks of 64 are staged in LDS and multiplied on MFMA (bf16: Q~ as hi + lo
-// parts, so the scores have a proven error E_q = gamma |q| max|q~|). Each lane
-// keeps a sorted top list of its landmarks; the four lanes of a query merge
-// theirs. If the s-th and (s+1)-th scores are more than 2E_q apart the set is
-// certain; otherwise the entries within 2E_q of the s-th score are re-scored in
-// fp64 (when the list provably holds all of them), or the query is queued for
-// the exact kernel, which scores all m landmarks in fp64 and ranks them. For
-// s > 6 every query goes through the exact kernel.
+// Fast kernels (s <= 6): 16 queries per wave; landmark blocks of 64 are staged
+// in LDS and multiplied on MFMA (bf16: Q~ as hi + lo parts, so the scores have a
+// proven error E_q = gamma |q| max|q~|). Each lane keeps a sorted top list of its
+// landmarks; the four lanes of a query merge theirs. If the s-th and (s+1)-th
+// scores are more than 2E_q apart the set is certain; otherwise the entries
+// within 2E_q of the s-th score are re-scored in fp64, or (m > 64, band longer
+// than the list) the query is queued for the exact kernel, which scores all m
+// landmarks in fp64 and ranks them. For s > 6 every query goes through the
+// exact kernel.
 #include "attn_core.h"
 
 namespace mita {
@@ -134,13 +134,10 @@ __device__ __forceinline__ void exact_route_wave(const T* qrow, const double* qt
   wave_sync();
 }
 
-// Fast router. RES: m <= 64, so the landmark block is staged once for all the
-// workgroup's query tiles and each query's m scores are still in registers when
-// its set is decided: band members are then re-scored in fp64 right there.
-// Otherwise the landmark blocks stream through LDS per tile, each lane keeps a
-// top list, and a query whose band reaches past the list end is queued: to the
-// end of this workgroup (TAIL) or to the exact kernel.
-template <typename T, int D, int TM, bool RES, bool TAIL>
+// Fast router for m <= 64: the landmark block is staged once for all the
+// workgroup's query tiles, and each query's m scores are still in registers
+// when its set is decided: band members are re-scored in fp64 right there.
+template <typename T, int D, int TM>
 __global__ __launch_bounds__(256) void route_fast_kernel(const T* __restrict__ Q, const void* __restrict__ qtop,
                                                          const double* __restrict__ qt64,
                                                          const float* __restrict__ qtnorm, int32_t* __restrict__ E,
@@ -151,9 +148,6 @@ __global__ __launch_bounds__(256) void route_fast_kernel(const T* __restrict__ Q
   __shared__ __align__(16) T Ks0[TL::KTILE];
   __shared__ __align__(16) T Ks1[BF ? TL::KTILE : 8];
   __shared__ float s_red[4];
-  __shared__ int s_nq;
-  __shared__ int s_q[TAIL ? kQueryTile : 1];                   // queries left for the exact routine
-  __shared__ double s_x[TAIL ? 4 * (kRouteLdsMaxM + D) : 1];   // per wave: m scores + the query row
   const int z = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
   const int t0 = blockIdx.x * tpw, t1 = min(qtiles, t0 + tpw);
   const T* plane0 = BF ? (const T*)((const uint16_t*)qtop + (size_t)z * 2 * m * D) : (const T*)((const float*)qtop + (size_t)z * m * D);
@@ -185,26 +179,13 @@ __global__ __launch_bounds__(256) void route_fast_kernel(const T* __restrict__ Q
   load_q(qb_n, qf_n, qrow_of(t0));
   float qtm = 0.f;
   for (int i = tid; i < m; i += 256) qtm = fmaxf(qtm, qtnorm[(size_t)z * m + i]);
-  if (RES) stage(0);
+  stage(0);
   qtm = wave_max(qtm);
   if (lane == 0) s_red[w] = qtm;
-  if (tid == 0) s_nq = 0;
   __syncthreads();
   const double qtmax = (double)fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
 
   for (int t = t0; t < t1; ++t) {
-    if (!RES && TAIL && t > t0) {   // finish the previous tile's queued queries (one wave each)
-      __syncthreads();
-      const int nq = s_nq;
-      double* r64 = s_x + w * (kRouteLdsMaxM + D);
-      for (int e = w; e < nq; e += 4) {
-        const int q = s_q[e];
-        exact_route_wave<T, D, 16>(Q + ((size_t)z * N + q) * D, qt64z, m, s, E + ((size_t)z * N + q) * s, r64,
-                                   r64 + kRouteLdsMaxM, lane);
-      }
-      __syncthreads();
-      if (tid == 0) s_nq = 0;
-    }
     const int q = t * kQueryTile + 16 * w + r;
     const bool q_ok = q < N;
     if constexpr (BF) {
@@ -222,11 +203,6 @@ __global__ __launch_bounds__(256) void route_fast_kernel(const T* __restrict__ Q
     for (int j = 0; j < TM; ++j) { tv[j] = -INFINITY; ti[j] = 0x7FFFFFFF; }
     f32x4 acc[4];
     for (int lb0 = 0; lb0 < m; lb0 += kKeyBlock) {
-      if (!RES) {
-        __syncthreads();   // readers of the previous block are done
-        stage(lb0);
-        __syncthreads();
-      }
       if constexpr (BF)
         qk_bf16<D, 2, 1>((const uint16_t*)Ks0, (const uint16_t*)Ks1, qb, acc, lane);
       else
@@ -309,89 +285,45 @@ __global__ __launch_bounds__(256) void route_fast_kernel(const T* __restrict__ Q
       part += __shfl_xor(part, 16, WAVE);
       return part + __shfl_xor(part, 32, WAVE);
     };
-    if constexpr (RES) {
-      // every score of the query is in acc (lanes of the quad hold 16 each):
-      // the band members are re-scored one by one, quad-uniformly
-      uint32_t mk = 0;
+    // every score of the query is in acc (lanes of the quad hold 16 each):
+    // the band members are re-scored one by one, quad-uniformly
+    uint32_t mk = 0;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int li = 16 * kt + 4 * g + j;
-          const double v = (double)acc[kt][j];
-          mk |= (unc && li < m && v >= lo && v <= hi) ? 1u << (4 * kt + j) : 0u;
-        }
-      uint64_t qm = 0;
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) qm |= (uint64_t)__shfl(mk, r + 16 * gg, WAVE) << (16 * gg);
-      double bv[TM];
-      int bi[TM];
-#pragma unroll
-      for (int j = 0; j < TM; ++j) { bv[j] = -INFINITY; bi[j] = 0x7FFFFFFF; }
-      while (qm) {   // same trip count on the four lanes of a query
-        const int bit = __builtin_ctzll(qm);
-        qm &= qm - 1;
-        const int b = bit & 15, li = 16 * (b >> 2) + 4 * (bit >> 4) + (b & 3);
-        double v = part64(li);
-        int i = li;
-#pragma unroll
-        for (int j = 0; j < TM; ++j) {   // insert by (score desc, id asc)
-          const bool better = (v > bv[j]) | ((v == bv[j]) & (i < bi[j]));
-          const double ov = bv[j];
-          const int oi = bi[j];
-          bv[j] = better ? v : ov;
-          bi[j] = better ? i : oi;
-          v = better ? ov : v;
-          i = better ? oi : i;
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int li = 16 * kt + 4 * g + j;
+        const double v = (double)acc[kt][j];
+        mk |= (unc && li < m && v >= lo && v <= hi) ? 1u << (4 * kt + j) : 0u;
       }
-      if (unc && g == 0) {
+    uint64_t qm = 0;
 #pragma unroll
-        for (int j = 0; j < TM; ++j)
-          if (j < need) Eq_out[c_in + j] = bi[j];
-      }
-    } else {
-      // the list holds the whole band when its last entry lies below it
-      const bool refine = unc && (m <= TM || (double)tv[TM - 1] < lo);
-      if (unc && !refine && g == 0) {
-        if (TAIL) {
-          s_q[atomicAdd(&s_nq, 1)] = q;
-        } else {
-          const uint32_t pos = atomicAdd(&counters[0], 1u);
-          rflag[pos] = (uint32_t)(z * N + q);
-        }
-      }
-      if (__any(refine)) {
-        double s64[TM];
-        bool band[TM];
+    for (int gg = 0; gg < 4; ++gg) qm |= (uint64_t)__shfl(mk, r + 16 * gg, WAVE) << (16 * gg);
+    double bv[TM];
+    int bi[TM];
 #pragma unroll
-        for (int j = 0; j < TM; ++j) {
-          const double v = (double)tv[j];
-          band[j] = refine && ti[j] < m && v >= lo && v <= hi;
-          s64[j] = part64(band[j] ? ti[j] : 0);
-        }
-        if (refine && g == 0) {
+    for (int j = 0; j < TM; ++j) { bv[j] = -INFINITY; bi[j] = 0x7FFFFFFF; }
+    while (qm) {   // same trip count on the four lanes of a query
+      const int bit = __builtin_ctzll(qm);
+      qm &= qm - 1;
+      const int b = bit & 15, li = 16 * (b >> 2) + 4 * (bit >> 4) + (b & 3);
+      double v = part64(li);
+      int i = li;
 #pragma unroll
-          for (int j = 0; j < TM; ++j) {
-            if (!band[j]) continue;
-            int rank = 0;
-#pragma unroll
-            for (int f = 0; f < TM; ++f)
-              rank += (band[f] && ((s64[f] > s64[j]) | ((s64[f] == s64[j]) & (ti[f] < ti[j])))) ? 1 : 0;
-            if (rank < need) Eq_out[c_in + rank] = ti[j];
-          }
-        }
+      for (int j = 0; j < TM; ++j) {   // insert by (score desc, id asc)
+        const bool better = (v > bv[j]) | ((v == bv[j]) & (i < bi[j]));
+        const double ov = bv[j];
+        const int oi = bi[j];
+        bv[j] = better ? v : ov;
+        bi[j] = better ? i : oi;
+        v = better ? ov : v;
+        i = better ? oi : i;
       }
     }
-  }
-  if constexpr (!RES && TAIL) {   // the last tile's queued queries
-    __syncthreads();
-    const int nq = s_nq;
-    double* r64 = s_x + w * (kRouteLdsMaxM + D);
-    for (int e = w; e < nq; e += 4) {
-      const int q = s_q[e];
-      exact_route_wave<T, D, 16>(Q + ((size_t)z * N + q) * D, qt64z, m, s, E + ((size_t)z * N + q) * s, r64,
-                                 r64 + kRouteLdsMaxM, lane);
+    if (unc && g == 0) {
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+        if (j < need) Eq_out[c_in + j] = bi[j];
     }
   }
 }
@@ -399,10 +331,9 @@ __global__ __launch_bounds__(256) void route_fast_kernel(const T* __restrict__ Q
 // Fast router for m > 64: a workgroup takes TPW query tiles at once (their query
 // fragments and top lists stay in registers) and streams the landmark blocks
 // through LDS once for all of them, so each block is staged once per TPW tiles.
-// Deciding a query is as in route_fast_kernel's list path: certain, band
-// re-scored in fp64 when the list holds it, else queued (to the end of this
-// workgroup when TAIL, else to the exact kernel).
-template <typename T, int D, int TM, int TPW, bool TAIL>
+// A query is certain, or its band is re-scored in fp64 when the list holds it,
+// or it is queued for the exact kernel.
+template <typename T, int D, int TM, int TPW>
 __global__ __launch_bounds__(256) void route_multi_kernel(const T* __restrict__ Q, const void* __restrict__ qtop,
                                                           const double* __restrict__ qt64,
                                                           const float* __restrict__ qtnorm, int32_t* __restrict__ E,
@@ -414,9 +345,6 @@ __global__ __launch_bounds__(256) void route_multi_kernel(const T* __restrict__ 
   __shared__ __align__(16) T Ks0[TL::KTILE];
   __shared__ __align__(16) T Ks1[BF ? TL::KTILE : 8];
   __shared__ float s_red[4];
-  __shared__ int s_nq;
-  __shared__ int s_q[TAIL ? TPW * kQueryTile : 1];
-  __shared__ double s_x[TAIL ? 4 * (kRouteLdsMaxM + D) : 1];
   const int z = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
   const int t0 = blockIdx.x * TPW;
   const T* plane0 = BF ? (const T*)((const uint16_t*)qtop + (size_t)z * 2 * m * D) : (const T*)((const float*)qtop + (size_t)z * m * D);
@@ -442,7 +370,6 @@ __global__ __launch_bounds__(256) void route_multi_kernel(const T* __restrict__ 
   for (int i = tid; i < m; i += 256) qtm = fmaxf(qtm, qtnorm[(size_t)z * m + i]);
   qtm = wave_max(qtm);
   if (lane == 0) s_red[w] = qtm;
-  if (tid == 0) s_nq = 0;
 
   float tv[TPW][TM];
   int ti[TPW][TM];
@@ -530,12 +457,8 @@ __global__ __launch_bounds__(256) void route_multi_kernel(const T* __restrict__ 
     }
     const bool refine = unc && (m <= TM || (double)tv[tt][TM - 1] < lo);
     if (unc && !refine && g == 0) {
-      if (TAIL) {
-        s_q[atomicAdd(&s_nq, 1)] = q;
-      } else {
-        const uint32_t pos = atomicAdd(&counters[0], 1u);
-        rflag[pos] = (uint32_t)(z * N + q);
-      }
+      const uint32_t pos = atomicAdd(&counters[0], 1u);
+      rflag[pos] = (uint32_t)(z * N + q);
     }
     if (__any(refine)) {
       double s64[TM];
@@ -573,16 +496,6 @@ __global__ __launch_bounds__(256) void route_multi_kernel(const T* __restrict__ 
       }
     }
   }
-  if constexpr (TAIL) {   // this workgroup's queued queries, one wave each
-    __syncthreads();
-    const int nq = s_nq;
-    double* r64 = s_x + w * (kRouteLdsMaxM + D);
-    for (int e = w; e < nq; e += 4) {
-      const int q = s_q[e];
-      exact_route_wave<T, D, 16>(Q + ((size_t)z * N + q) * D, qt64z, m, s, E + ((size_t)z * N + q) * s, r64,
-                                 r64 + kRouteLdsMaxM, lane);
-    }
-  }
 }
 
 // Exact routing kernel: one wave per query (up to four per workgroup), for the
@@ -605,14 +518,14 @@ __global__ __launch_bounds__(256) void route_exact_kernel(const T* __restrict__ 
   }
 }
 
-// Where the queries the fast kernel cannot settle are finished: m <= 64 in the
-// fast kernel itself (all scores at hand); up to kRouteLdsMaxM at the end of each
-// query tile of the fast kernel; beyond that by the exact kernel.
+// m <= 64: every query is settled in route_fast_kernel (all its scores at hand).
+// Larger m: route_multi_kernel, with the queries its lists cannot settle queued
+// for the exact kernel.
 template <typename T, int D, int TM, bool RES>
 static hipError_t route_fast_launch(const Plan& p, const void* Q, char* ws, hipStream_t st) {
   if constexpr (RES) {
     const int tpw = 4;   // several query tiles per workgroup: the landmarks stay staged
-    hipLaunchKernelGGL((route_fast_kernel<T, D, TM, true, false>), dim3((p.qtiles + tpw - 1) / tpw, p.BH), dim3(256), 0,
+    hipLaunchKernelGGL((route_fast_kernel<T, D, TM>), dim3((p.qtiles + tpw - 1) / tpw, p.BH), dim3(256), 0,
                        st, (const T*)Q, (const void*)(ws + p.ws.qtop), (const double*)(ws + p.ws.qt64),
                        (const float*)(ws + p.ws.qtnorm), (int32_t*)(ws + p.ws.E), (uint32_t*)(ws + p.ws.counters),
                        (uint32_t*)(ws + p.ws.rflag), p.N, p.m, p.s, p.gamma_qk, p.qtiles, tpw);
@@ -622,7 +535,7 @@ static hipError_t route_fast_launch(const Plan& p, const void* Q, char* ws, hipS
     constexpr int TPW = (sizeof(T) == 2 && D == 64) ? 4 : 2;
     // the rare queries the lists cannot settle go to the exact kernel (an in-kernel
     // exact pass would cost every workgroup its registers)
-    hipLaunchKernelGGL((route_multi_kernel<T, D, TM, TPW, false>), dim3((p.qtiles + TPW - 1) / TPW, p.BH), dim3(256), 0, st, (const T*)Q,
+    hipLaunchKernelGGL((route_multi_kernel<T, D, TM, TPW>), dim3((p.qtiles + TPW - 1) / TPW, p.BH), dim3(256), 0, st, (const T*)Q,
                        (const void*)(ws + p.ws.qtop), (const double*)(ws + p.ws.qt64), (const float*)(ws + p.ws.qtnorm),
                        (int32_t*)(ws + p.ws.E), (uint32_t*)(ws + p.ws.counters), (uint32_t*)(ws + p.ws.rflag), p.N,
                        p.m, p.s, p.gamma_qk, p.qtiles);

@@ -39,6 +39,22 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
   return (uint16_t)(__float_as_uint(f) >> 16);
 }
 
+// ---------------------------------------------------------------- XCD placement
+// Workgroups of a 1D grid go round-robin to the 8 XCDs (each with its own L2).
+// Work item (lt, c, z) of this workgroup for a landmark-tile x key-chunk x slice
+// problem such that the lm_tiles workgroups sharing one key chunk run on one
+// XCD and read the chunk through its L2 once. Grid: 8 ceil(nsplit BH / 8)
+// lm_tiles workgroups; returns false for the padding ones.
+__device__ __forceinline__ bool chunk_item(int lm_tiles, int nsplit, int BH, int& lt, int& c, int& z) {
+  const int b = blockIdx.x, xcd = b & 7, j = b >> 3;
+  lt = j % lm_tiles;
+  const int G = (j / lm_tiles) * 8 + xcd;
+  if (G >= nsplit * BH) return false;
+  c = G % nsplit;
+  z = G / nsplit;
+  return true;
+}
+
 // ---------------------------------------------------------------- order keys
 // Monotone map of float32 onto uint32: a < b (as floats) iff key(a) < key(b).
 __device__ __forceinline__ uint32_t f32_key(float x) {

@@ -4,7 +4,7 @@
 // the deformable experts, so one pass produces both).
 //
 // Flash-style: a workgroup takes 64 landmarks (16 per wave) and one chunk of
-// keys, streams the chunk through LDS 64 keys at a time (the next block is
+// keys (the workgroups sharing a chunk are placed on one XCD), streams the chunk through LDS 64 keys at a time (the next block is
 // fetched into registers while the current one computes) and keeps an online
 // softmax. A second kernel merges the chunks' partial softmaxes into V~. The
 // scores themselves do not go to memory: only maxima of groups of 16 (one
@@ -26,13 +26,14 @@ __global__ __launch_bounds__(256) void landmark_kernel(const T* __restrict__ K, 
                                                        const void* __restrict__ qtop, float* __restrict__ S,
                                                        float* __restrict__ lpart, float* __restrict__ kmax,
                                                        float* __restrict__ bmax, int N, int m, int lchunk, int nsplit,
-                                                       int gq, int nbg, float sl2e) {
+                                                       int gq, int nbg, int lm_tiles, int BH, float sl2e) {
   using TL = Tiles<T, D>;
   constexpr bool BF = TL::BF;
   __shared__ __align__(16) T Ks[TL::KTILE];
   __shared__ __align__(16) T Vs[TL::VTILE];
   __shared__ float kred[4];
-  const int lt = blockIdx.x, c = blockIdx.y, z = blockIdx.z;
+  int lt, c, z;
+  if (!chunk_item(lm_tiles, nsplit, BH, lt, c, z)) return;   // workgroup-uniform
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
   const int lm = lt * kLandmarkTile + 16 * w + r;
   const bool lm_ok = lm < m;
@@ -203,10 +204,10 @@ template <typename T, int D>
 static hipError_t landmark_launch(const Plan& p, const void* K, const void* V, char* ws, float* S_out,
                                   hipStream_t st) {
   const float sl2e = (float)(1.4426950408889634 / sqrt((double)D));
-  dim3 grid(p.lm_tiles, p.nsplit, p.BH);
-  hipLaunchKernelGGL((landmark_kernel<T, D>), grid, dim3(256), 0, st, (const T*)K, (const T*)V,
+  const int grid = 8 * ((p.nsplit * p.BH + 7) / 8) * p.lm_tiles;   // see chunk_item
+  hipLaunchKernelGGL((landmark_kernel<T, D>), dim3(grid), dim3(256), 0, st, (const T*)K, (const T*)V,
                      (const void*)(ws + p.ws.qtop), S_out, (float*)(ws + p.ws.lpart), (float*)(ws + p.ws.kmax),
-                     (float*)(ws + p.ws.bmax), p.N, p.m, p.lchunk, p.nsplit, p.gq, p.nbg, sl2e);
+                     (float*)(ws + p.ws.bmax), p.N, p.m, p.lchunk, p.nsplit, p.gq, p.nbg, p.lm_tiles, p.BH, sl2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rows = p.BH * p.m;

@@ -136,11 +136,12 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void topk_cand_kernel(const T* __restrict__ K, const void* __restrict__ qtop,
                                                         const uint32_t* __restrict__ thr, uint2* __restrict__ cand,
                                                         uint32_t* __restrict__ ccnt, int N, int m, int lchunk,
-                                                        int nsplit, int capc) {
+                                                        int nsplit, int capc, int lm_tiles, int BH) {
   using TL = Tiles<T, D>;
   constexpr bool BF = TL::BF;
   __shared__ __align__(16) T Ks[TL::KTILE];
-  const int lt = blockIdx.x, c = blockIdx.y, z = blockIdx.z;
+  int lt, c, z;
+  if (!chunk_item(lm_tiles, nsplit, BH, lt, c, z)) return;   // workgroup-uniform
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
   const int lm = lt * kLandmarkTile + 16 * w + r;
   const bool lm_ok = lm < m;
@@ -480,9 +481,10 @@ static hipError_t topk_launch(const Plan& p, const void* K, char* ws, hipStream_
     else if (p.nbg <= 1024) th(topk_thresh_kernel<16>);
     else th(topk_thresh_kernel<64>);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((topk_cand_kernel<T, D>), dim3(p.lm_tiles, p.nsplit, p.BH), dim3(256), 0, st, (const T*)K,
+    const int cgrid = 8 * ((p.nsplit * p.BH + 7) / 8) * p.lm_tiles;   // see chunk_item
+    hipLaunchKernelGGL((topk_cand_kernel<T, D>), dim3(cgrid), dim3(256), 0, st, (const T*)K,
                        (const void*)(ws + p.ws.qtop), (const uint32_t*)(ws + p.ws.thr), (uint2*)(ws + p.ws.cand),
-                       (uint32_t*)(ws + p.ws.ccnt), p.N, p.m, p.lchunk, p.nsplit, p.capc);
+                       (uint32_t*)(ws + p.ws.ccnt), p.N, p.m, p.lchunk, p.nsplit, p.capc, p.lm_tiles, p.BH);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     auto sel = [&](auto kern, int wpb) {
       hipLaunchKernelGGL(kern, dim3((rows + wpb - 1) / wpb), dim3(64 * wpb), 0, st, (const uint2*)(ws + p.ws.cand),

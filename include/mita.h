@@ -22,7 +22,8 @@
  *   - Tensors are device pointers, row-major and contiguous: Q, K, V and out are
  *     [B, H, N, d] with d fastest, all of the dtype named in the shape (bf16 as
  *     raw 16-bit patterns, or fp32). The caller allocates and owns every buffer;
- *     the library keeps no pointer after a call returns and allocates nothing.
+ *     the library keeps no pointer after a call returns and allocates no device
+ *     memory (mita_forward keeps one side stream and two events per device).
  *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
  *     asynchronously; the call returns without synchronising. Device faults show
  *     up at the caller's next synchronisation.
@@ -74,7 +75,12 @@ size_t mita_workspace_bytes(const mita_shape* shape, int m, int k, int s);
  * k tokens and s routed experts per query. Requires 1 <= m <= N, 1 <= k <= N,
  * 1 <= s <= m. `out` has the input dtype ([B, H, N, d]); bf16 results are
  * rounded to nearest even. Equivalent to calling mita_pool, mita_landmark,
- * mita_topk, mita_route and mita_gather in that order on the same workspace. */
+ * mita_topk, mita_route and mita_gather in that order on the same workspace,
+ * except that routing (step 4, which needs only step 1) runs concurrently with
+ * steps 2 and 3 on a side stream: per device the library keeps one stream
+ * (default priority) and two events, created on the first call, and joins the
+ * side stream back into `stream` before step 5 (so the call stays ordered on
+ * `stream`, and may be captured into a graph). No device memory is allocated. */
 mita_status mita_forward(const void* Q, const void* K, const void* V, int m, int k, int s, void* out,
                          const mita_shape* shape, void* workspace, size_t workspace_bytes, void* stream);
 

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "plan.h"
 
@@ -245,6 +246,43 @@ mita_status mita_gather(const void* Q, const void* K, const void* V, int m, int 
   return hip_status(launch_gather(P, Q, K, V, out, (char*)workspace, (hipStream_t)stream), "gather");
 }
 
+}  // extern "C"
+
+namespace {
+
+// Per device: one side stream (default priority) and two events, created on the
+// first forward call on that device, so that routing (which needs only step 1)
+// runs concurrently with steps 2 and 3. The mutex keeps each call's fork and
+// join together when several host threads share the device.
+struct SideStream {
+  std::mutex mu;
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+std::mutex g_side_init;
+
+mita_status side_stream(SideStream** out) {
+  int dev = 0;
+  mita_status st;
+  if ((st = hip_status(hipGetDevice(&dev), "hipGetDevice")) != MITA_OK) return st;
+  if (dev < 0 || dev >= kMaxDevices) { set_error("device id out of range"); return MITA_ERR_UNSUPPORTED; }
+  SideStream& sd = g_side[dev];
+  std::lock_guard<std::mutex> lk(g_side_init);
+  if (!sd.stream) {
+    if ((st = hip_status(hipStreamCreateWithFlags(&sd.stream, hipStreamNonBlocking), "side stream")) != MITA_OK) return st;
+    if ((st = hip_status(hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming), "fork event")) != MITA_OK) return st;
+    if ((st = hip_status(hipEventCreateWithFlags(&sd.join, hipEventDisableTiming), "join event")) != MITA_OK) return st;
+  }
+  *out = &sd;
+  return MITA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 mita_status mita_forward(const void* Q, const void* K, const void* V, int m, int k, int s, void* out,
                          const mita_shape* shape, void* workspace, size_t workspace_bytes, void* stream) {
   Plan P;
@@ -255,12 +293,22 @@ mita_status mita_forward(const void* Q, const void* K, const void* V, int m, int
     return st;
   hipStream_t hs = (hipStream_t)stream;
   char* ws = (char*)workspace;
+  SideStream* sd = nullptr;
+  if ((st = side_stream(&sd)) != MITA_OK) return st;
+  std::lock_guard<std::mutex> lk(sd->mu);
+  hipStream_t rs = sd->stream;
   if ((st = hip_status(launch_pool(P, Q, ws, hs), "pool")) != MITA_OK) return st;
+  // fork: routing (+ bucketing) on the side stream, steps 2-3 on the caller's
+  if ((st = hip_status(hipEventRecord(sd->fork, hs), "fork")) != MITA_OK) return st;
+  if ((st = hip_status(hipStreamWaitEvent(rs, sd->fork, 0), "fork wait")) != MITA_OK) return st;
+  if ((st = hip_status(launch_clear(P, ws, rs), "clear")) != MITA_OK) return st;
+  if ((st = hip_status(launch_route(P, Q, ws, rs), "route")) != MITA_OK) return st;
+  if ((st = hip_status(launch_bucket(P, ws, rs), "bucket")) != MITA_OK) return st;
+  if ((st = hip_status(hipEventRecord(sd->join, rs), "join")) != MITA_OK) return st;
   if ((st = hip_status(launch_landmark(P, K, V, ws, nullptr, hs), "landmark")) != MITA_OK) return st;
   if ((st = hip_status(launch_topk(P, K, ws, hs), "topk")) != MITA_OK) return st;
-  if ((st = hip_status(launch_clear(P, ws, hs), "clear")) != MITA_OK) return st;
-  if ((st = hip_status(launch_route(P, Q, ws, hs), "route")) != MITA_OK) return st;
-  if ((st = hip_status(launch_bucket(P, ws, hs), "bucket")) != MITA_OK) return st;
+  // join: the output step needs both branches
+  if ((st = hip_status(hipStreamWaitEvent(hs, sd->join, 0), "join wait")) != MITA_OK) return st;
   return hip_status(launch_gather(P, Q, K, V, out, ws, hs), "gather");
 }
 

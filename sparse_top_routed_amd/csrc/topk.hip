@@ -251,30 +251,50 @@ __global__ __launch_bounds__(64 * WPB) void topk_select_kernel(const uint2* __re
     if (lane == 0) glist[1 + atomicAdd(&glist[0], 1u)] = (uint32_t)row;
   };
 
-  // gather the lists; any overflow, or more than CAP in all, goes to the fallback
-  // chunk offsets (exclusive sums of the counts) go to LDS, in the band list's space
+  // gather the lists; any overflow, or more than CAP in all, goes to the fallback;
+  // chunk offsets: exclusive sums of the counts
   uint32_t total = 0;
-  bool over = false;
-  for (int c0 = 0; c0 < nsplit; c0 += 64) {
-    const int c = c0 + lane;
-    const uint32_t n = c < nsplit ? cnt[c] : 0u;
-    over |= n > (uint32_t)capc;
-    uint32_t tot;
-    const uint32_t ex = wave_excl_scan(n, tot);
-    if (c < nsplit && c < BAND) blist[c] = total + ex;
-    total += tot;
-  }
-  total = __builtin_amdgcn_readfirstlane(total);   // wave-uniform: keep the loops below scalar
-  if (__any(over) || total > (uint32_t)CAP || nsplit > BAND) {
-    fallback();
-    return;
-  }
-  wave_sync();
-  // candidate j: chunk c with off_c <= j < off_{c+1} (offsets ascend; few chunks)
-  for (uint32_t j = lane; j < total; j += 64) {
-    int c = 0;
-    while (c + 1 < nsplit && blist[c + 1] <= j) ++c;
-    cs[j] = segs[(size_t)c * capc + (j - blist[c])];
+  if (nsplit <= 64) {   // one chunk per lane; offsets stay in registers
+    const uint32_t n = lane < nsplit ? cnt[lane] : 0u;
+    const uint32_t off = wave_excl_scan(n, total);
+    total = __builtin_amdgcn_readfirstlane(total);   // wave-uniform: keep the loops below scalar
+    if (__any(n > (uint32_t)capc) || total > (uint32_t)CAP) {
+      fallback();
+      return;
+    }
+    // candidate j: chunk c with off_c <= j < off_{c+1} (offsets ascend)
+    for (uint32_t j = lane; j < total; j += 64) {
+      int c = 0;
+      uint32_t oc = 0;
+      for (int i = 1; i < nsplit; ++i) {
+        const uint32_t oi = __builtin_amdgcn_readlane(off, i);
+        c = oi <= j ? i : c;
+        oc = oi <= j ? oi : oc;
+      }
+      cs[j] = segs[(size_t)c * capc + (j - oc)];
+    }
+  } else {   // many chunks: offsets in LDS (the band list's space, free until later)
+    bool over = false;
+    for (int c0 = 0; c0 < nsplit; c0 += 64) {
+      const int c = c0 + lane;
+      const uint32_t n = c < nsplit ? cnt[c] : 0u;
+      over |= n > (uint32_t)capc;
+      uint32_t tot;
+      const uint32_t ex = wave_excl_scan(n, tot);
+      if (c < nsplit && c < BAND) blist[c] = total + ex;
+      total += tot;
+    }
+    total = __builtin_amdgcn_readfirstlane(total);
+    if (__any(over) || total > (uint32_t)CAP || nsplit > BAND) {
+      fallback();
+      return;
+    }
+    wave_sync();
+    for (uint32_t j = lane; j < total; j += 64) {
+      int c = 0;
+      while (c + 1 < nsplit && blist[c + 1] <= j) ++c;
+      cs[j] = segs[(size_t)c * capc + (j - blist[c])];
+    }
   }
   wave_sync();
   const double E = row_bound(qtnorm, kmax, nsplit, row, z, gamma, lane);

@@ -15,9 +15,7 @@
 // carry ~16 more bits than a bf16 Q~ would; fp32 inputs use the fp32 MFMA.
 // The workgroups of landmark tile 0 also record max_n |K_n|_2 per chunk, which
 // bounds the score error for the exact top-k of step 3.
-#include <type_traits>
-
-#include "attn_core.h"
+#include "sweep.h"
 
 namespace mita {
 
@@ -28,7 +26,6 @@ __global__ __launch_bounds__(256) void landmark_kernel(const T* __restrict__ K, 
                                                        float* __restrict__ bmax, int N, int m, int lchunk, int nsplit,
                                                        int gq, int nbg, int lm_tiles, int BH, float sl2e) {
   using TL = Tiles<T, D>;
-  constexpr bool BF = TL::BF;
   __shared__ __align__(16) T Ks[TL::KTILE];
   __shared__ __align__(16) T Vs[TL::VTILE];
   __shared__ float kred[4];
@@ -39,102 +36,16 @@ __global__ __launch_bounds__(256) void landmark_kernel(const T* __restrict__ K, 
   const bool lm_ok = lm < m;
   const int lmc = lm_ok ? lm : m - 1;   // padding lanes compute on a real landmark, never write
   const int k0 = c * lchunk, k1 = min(N, k0 + lchunk);
-  const T* Kz = K + (size_t)z * N * D;
-  const T* Vz = V + (size_t)z * N * D;
 
-  // first key/value block into registers, then the landmark fragments
-  RowRegs<T, D> KR;
-  std::conditional_t<BF, VtRegs<D>, RowRegs<T, D>> VR;
-  KR.load([&](int rr) { return Kz + (size_t)(k0 + rr) * D; }, min(kKeyBlock, k1 - k0), tid);
-  VR.load([&](int rr) { return Vz + (size_t)(k0 + rr) * D; }, min(kKeyBlock, k1 - k0), tid);
-  uint4 qb[2][D / 32];
-  float qf[D / 4];
-  if constexpr (BF) {
-    const uint16_t* qt = (const uint16_t*)qtop;
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks)
-        qb[p][ks] = *(const uint4*)(qt + ((size_t)(z * 2 + p) * m + lmc) * D + 32 * ks + 8 * g);
-  } else {
-    const float* qt = (const float*)qtop;
-#pragma unroll
-    for (int ks = 0; ks < D / 4; ++ks) qf[ks] = qt[((size_t)z * m + lmc) * D + 4 * ks + g];
-  }
-
-  float mrun = -INFINITY, lrun = 0.f, kmx = 0.f;
-  f32x4 o[D / 16];
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  LmFrag<T, D> qfr;
+  qfr.load(qtop, z, m, lmc, g);
+  LmState<D> st;
+  st.init();
+  float kmx = 0.f;
   float* Srow = S ? S + ((size_t)z * m + lmc) * N : nullptr;
   float* Brow = bmax + ((size_t)z * m + lmc) * nbg;
-  const bool vec_store = (N & 3) == 0;
-  const int last_kb = k0 + ((k1 - k0 - 1) / kKeyBlock) * kKeyBlock;
-
-  for (int kb = k0; kb < k1; kb += kKeyBlock) {
-    const int nvalid = min(kKeyBlock, k1 - kb);
-    KR.store(Ks, TL::KSTR, tid);
-    if constexpr (BF) VR.store((uint16_t*)Vs, tid); else VR.store(Vs, TL::VSTR, tid);
-    __syncthreads();
-    {   // prefetch the next block (the last block again at the end: no branch)
-      const int nb = min(kb + kKeyBlock, last_kb);
-      const int nv = min(kKeyBlock, k1 - nb);
-      KR.load([&](int rr) { return Kz + (size_t)(nb + rr) * D; }, nv, tid);
-      VR.load([&](int rr) { return Vz + (size_t)(nb + rr) * D; }, nv, tid);
-    }
-
-    if (lt == 0) {  // squared norms of the staged keys: 4 threads per row
-      const int row = tid >> 2, part = tid & 3;
-      const T* kr = Ks + row * TL::KSTR + part * (D / 4);
-      float sq = 0.f;
-#pragma unroll
-      for (int e = 0; e < D / 4; ++e) {
-        float x;
-        if constexpr (BF) x = bf16_to_f32(kr[e]); else x = kr[e];
-        sq = fmaf(x, x, sq);
-      }
-      sq += __shfl_xor(sq, 1, WAVE);
-      sq += __shfl_xor(sq, 2, WAVE);
-      kmx = fmaxf(kmx, sq);
-    }
-
-    f32x4 acc[4];
-    if constexpr (BF)
-      qk_bf16<D, 1, 2>((const uint16_t*)Ks, nullptr, qb, acc, lane);
-    else
-      qk_f32<D>((const float*)Ks, qf, acc, lane);
-
-    {   // group maxima for the top-k threshold: one lane's 16 scores, or the block's 64
-      float gm = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) gm = fmaxf(gm, kb + 16 * kt + 4 * g + j < k1 ? acc[kt][j] : -INFINITY);
-      if (gq == 64) gm = quad_max(gm);
-      const int blk = kb / kKeyBlock;
-      if (lm_ok && (gq == 16 || g == 0)) Brow[gq == 16 ? 4 * blk + g : blk] = gm;
-    }
-    if (Srow && lm_ok) {   // the scores themselves only when asked for
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const int key = kb + 16 * kt + 4 * g;
-        if (vec_store && key + 3 < k1) {
-          *(float4*)(Srow + key) = make_float4(acc[kt][0], acc[kt][1], acc[kt][2], acc[kt][3]);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (key + j < k1) Srow[key + j] = acc[kt][j];
-        }
-      }
-    }
-    const float alpha = online_softmax(acc, nvalid, sl2e, mrun, lrun, lane);
-    rescale<D>(o, alpha);
-    if constexpr (BF)
-      pv_bf16<D>((const uint16_t*)Vs, acc, o, lane);
-    else
-      pv_f32<D>((const float*)Vs, acc, o, lane);
-    __syncthreads();
-  }
+  shared_expert_sweep<T, D>(K + (size_t)z * N * D, V + (size_t)z * N * D, k0, k1, qfr, Ks, Vs, lt == 0, kmx, Brow,
+                            gq, Srow, (N & 3) == 0, lm_ok, sl2e, st, tid);
 
   if (lt == 0) {
     kmx = wave_max(kmx);
@@ -146,13 +57,13 @@ __global__ __launch_bounds__(256) void landmark_kernel(const T* __restrict__ K, 
     }
   }
   // partial softmax of this chunk: [max, sum, pad, pad, acc[D]] per landmark
-  lrun = quad_sum(lrun);
+  const float lrun = quad_sum(st.lrun);
   if (lm_ok) {
     float* P = lpart + (((size_t)z * m + lm) * nsplit + c) * (D + 4);
-    if (g == 0) *(float2*)P = make_float2(mrun, lrun);
+    if (g == 0) *(float2*)P = make_float2(st.mrun, lrun);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
-      *(float4*)(P + 4 + 16 * dt + 4 * g) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+      *(float4*)(P + 4 + 16 * dt + 4 * g) = make_float4(st.o[dt][0], st.o[dt][1], st.o[dt][2], st.o[dt][3]);
   }
 }
 

@@ -20,7 +20,7 @@
 //      scores of the whole row and an 8-bit radix select on their order keys.
 // Every token that could be in the exact top-k is a candidate: anything within
 // 2E of T is at least tau - 2E.
-#include "attn_core.h"
+#include "sweep.h"
 
 namespace mita {
 
@@ -86,33 +86,19 @@ __device__ __forceinline__ void band_keys(double Tf, double E, uint32_t& hiKey, 
 }
 
 // ---------------------------------------------------------------- 1. threshold
-// One wave per row (four rows per workgroup); the row's group maxima (at most
-// 64 PV) sit in registers, lane l holding maxima l, 64 + l, ...
+// Candidate threshold of one row (as an order key; 0: none, every score is a
+// candidate) from its nbg group maxima, lane l holding maxima l, 64 + l, ...
+// (order keys, 0 past nbg): tau = the k-th largest maximum by a bit search
+// (ballots: one compare per register, the counting on the scalar unit), then
+// tau - 2E rounded down.
 template <int PV>
-__global__ __launch_bounds__(256) void topk_thresh_kernel(const float* __restrict__ bmax,
-                                                          const float* __restrict__ qtnorm,
-                                                          const float* __restrict__ kmax, int nsplit,
-                                                          uint32_t* __restrict__ thr, uint32_t* __restrict__ glist,
-                                                          int nbg, int m, int k, double gamma, int rows) {
-  const int tid = threadIdx.x, lane = tid & 63, row = blockIdx.x * 4 + (tid >> 6);
-  if (blockIdx.x == 0 && tid == 0) glist[0] = 0u;   // no fallback rows yet
-  if (row >= rows) return;
-  const int z = row / m;
-  const float* br = bmax + (size_t)row * nbg;
-  uint32_t v[PV];
-#pragma unroll
-  for (int p = 0; p < PV; ++p) {
-    const int i = 64 * p + lane;
-    const float x = br[max(0, min(i, nbg - 1))];   // nbg = 0: no threshold, the load stays in bounds
-    v[p] = i < nbg ? f32_key(x) : 0u;
-  }
-  const double E = row_bound(qtnorm, kmax, nsplit, row, z, gamma, lane);
-  uint32_t key = 0u;   // 0: no threshold, every score is a candidate
+__device__ __forceinline__ uint32_t thresh_key(const uint32_t (&v)[PV], int nbg, int k, double E) {
+  uint32_t key = 0u;
   if (nbg >= k) {
-    uint32_t pfx = 0u;   // the k-th largest group-maximum key, bit by bit
+    uint32_t pfx = 0u;
     for (int b = 31; b >= 0; --b) {
       const uint32_t cand = pfx | (1u << b);
-      uint32_t c = 0;   // ballots: one compare per register, the counting on the scalar unit
+      uint32_t c = 0;
 #pragma unroll
       for (int p = 0; p < PV; ++p) c += ballot_count(v[p] >= cand);
       if (c >= (uint32_t)k) pfx = cand;
@@ -123,22 +109,48 @@ __global__ __launch_bounds__(256) void topk_thresh_kernel(const float* __restric
       key = t > -INFINITY ? max(1u, f32_key(round_down_f32(t))) : 0u;
     }
   }
+  return key;
+}
+
+// Loads a row's group maxima as order keys (lane l: maxima l, 64 + l, ...).
+template <int PV>
+__device__ __forceinline__ void load_group_keys(const float* br, int nbg, int lane, uint32_t (&v)[PV]) {
+#pragma unroll
+  for (int p = 0; p < PV; ++p) {
+    const int i = 64 * p + lane;
+    const float x = br[max(0, min(i, nbg - 1))];   // nbg = 0: no threshold, the load stays in bounds
+    v[p] = i < nbg ? f32_key(x) : 0u;
+  }
+}
+
+// One wave per row (four rows per workgroup); the row's group maxima (at most
+// 64 PV) sit in registers.
+template <int PV>
+__global__ __launch_bounds__(256) void topk_thresh_kernel(const float* __restrict__ bmax,
+                                                          const float* __restrict__ qtnorm,
+                                                          const float* __restrict__ kmax, int nsplit,
+                                                          uint32_t* __restrict__ thr, uint32_t* __restrict__ glist,
+                                                          int nbg, int m, int k, double gamma, int rows) {
+  const int tid = threadIdx.x, lane = tid & 63, row = blockIdx.x * 4 + (tid >> 6);
+  if (blockIdx.x == 0 && tid == 0) glist[0] = 0u;   // no fallback rows yet
+  if (row >= rows) return;
+  const int z = row / m;
+  uint32_t v[PV];
+  load_group_keys<PV>(bmax + (size_t)row * nbg, nbg, lane, v);
+  const double E = row_bound(qtnorm, kmax, nsplit, row, z, gamma, lane);
+  const uint32_t key = thresh_key<PV>(v, nbg, k, E);
   if (lane == 0) thr[row] = key;
 }
 
 // ---------------------------------------------------------------- 2. candidates
 // Same workgroup shape and MFMA sequence as the shared-expert kernel (64
-// landmarks x one key chunk, 16 landmarks per wave), K only. A lane holds 16
-// scores of one landmark per 64-key block: keys 16 kt + 4 g + j. Candidates go
-// out in index order: per kt, the four lanes of a landmark take consecutive
-// slots by an exclusive count over g.
+// landmarks x one key chunk, 16 landmarks per wave), K only.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void topk_cand_kernel(const T* __restrict__ K, const void* __restrict__ qtop,
                                                         const uint32_t* __restrict__ thr, uint2* __restrict__ cand,
                                                         uint32_t* __restrict__ ccnt, int N, int m, int lchunk,
                                                         int nsplit, int capc, int lm_tiles, int BH) {
   using TL = Tiles<T, D>;
-  constexpr bool BF = TL::BF;
   __shared__ __align__(16) T Ks[TL::KTILE];
   int lt, c, z;
   if (!chunk_item(lm_tiles, nsplit, BH, lt, c, z)) return;   // workgroup-uniform
@@ -147,76 +159,14 @@ __global__ __launch_bounds__(256) void topk_cand_kernel(const T* __restrict__ K,
   const bool lm_ok = lm < m;
   const int lmc = lm_ok ? lm : m - 1;
   const int k0 = c * lchunk, k1 = min(N, k0 + lchunk);
-  const T* Kz = K + (size_t)z * N * D;
   const size_t row = (size_t)z * m + lmc;
-
-  RowRegs<T, D> KR;
-  KR.load([&](int rr) { return Kz + (size_t)(k0 + rr) * D; }, min(kKeyBlock, k1 - k0), tid);
-  uint4 qb[2][D / 32];
-  float qf[D / 4];
-  if constexpr (BF) {
-    const uint16_t* qt = (const uint16_t*)qtop;
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks)
-        qb[p][ks] = ld16(qt + ((size_t)(z * 2 + p) * m + lmc) * D + 32 * ks + 8 * g);
-  } else {
-    const float* qt = (const float*)qtop;
-#pragma unroll
-    for (int ks = 0; ks < D / 4; ++ks) qf[ks] = qt[((size_t)z * m + lmc) * D + 4 * ks + g];
-  }
+  LmFrag<T, D> qfr;
+  qfr.load(qtop, z, m, lmc, g);
   const uint32_t tk = thr[row];
   const float tf = tk ? key_f32(tk) : -INFINITY;   // compare the scores themselves (same order)
-  uint2* seg = cand + (row * nsplit + c) * (size_t)capc;
-  uint32_t base = 0;   // candidates of this landmark so far (same on its four lanes)
-  const int last_kb = k0 + ((k1 - k0 - 1) / kKeyBlock) * kKeyBlock;
-
-  for (int kb = k0; kb < k1; kb += kKeyBlock) {
-    KR.store(Ks, TL::KSTR, tid);
-    __syncthreads();
-    {
-      const int nb = min(kb + kKeyBlock, last_kb);
-      KR.load([&](int rr) { return Kz + (size_t)(nb + rr) * D; }, min(kKeyBlock, k1 - nb), tid);
-    }
-    f32x4 acc[4];
-    if constexpr (BF)
-      qk_bf16<D, 1, 2>((const uint16_t*)Ks, nullptr, qb, acc, lane);
-    else
-      qk_f32<D>((const float*)Ks, qf, acc, lane);
-    // per kt: this lane's candidate count in a byte of one word
-    uint32_t flags = 0, packed = 0;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bool p = (kb + 16 * kt + 4 * g + j < k1) & (acc[kt][j] >= tf);
-        flags |= p ? 1u << (4 * kt + j) : 0u;
-        packed += p ? 1u << (8 * kt) : 0u;
-      }
-    const uint32_t p0 = __shfl(packed, r, WAVE), p1 = __shfl(packed, r + 16, WAVE);
-    const uint32_t p2 = __shfl(packed, r + 32, WAVE), p3 = __shfl(packed, r + 48, WAVE);
-    const uint32_t tot = p0 + p1 + p2 + p3;   // no byte exceeds 16: no carries
-    const uint32_t ex = (g > 0 ? p0 : 0u) + (g > 1 ? p1 : 0u) + (g > 2 ? p2 : 0u);
-    if (flags && lm_ok) {
-      uint32_t run = base;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        uint32_t pos = run + ((ex >> (8 * kt)) & 255u);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (flags & (1u << (4 * kt + j))) {
-            if (pos < (uint32_t)capc) seg[pos] = make_uint2(f32_key(acc[kt][j]), (uint32_t)(kb + 16 * kt + 4 * g + j));
-            ++pos;
-          }
-        }
-        run += (tot >> (8 * kt)) & 255u;
-      }
-    }
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) base += (tot >> (8 * kt)) & 255u;
-    __syncthreads();
-  }
+  uint32_t base = 0;
+  candidate_sweep<T, D>(K + (size_t)z * N * D, k0, k1, qfr, Ks, tf, cand + (row * nsplit + c) * (size_t)capc, capc,
+                        lm_ok, base, tid);
   if (lm_ok && g == 0) ccnt[row * nsplit + c] = min(base, (uint32_t)capc + 1u);
 }
 

@@ -32,6 +32,10 @@ SMALL = [
     # s = 1 with one key block per expert (k, m <= 64): the one-pass output kernel
     small("one_block_f32_d128", B=2, H=1, N=700, d=128, grid_w=700, pool_w=50, k=33, s=1),
     small("one_block_bf16_d128", B=1, H=3, N=4096, d=128, grid_w=4096, pool_w=64, k=64, s=1, dtype="bf16"),
+    # fp32 over several key chunks; several landmark tiles per slice on a 2D grid
+    small("chunked_f32", B=1, H=2, N=5000, grid_w=5000, pool_w=20, k=80, s=2),
+    small("tiles_2d_bf16", B=1, H=2, N=64 * 64, grid_h=64, grid_w=64, pool_h=10, pool_w=10, k=64, s=2,
+          dtype="bf16"),
 ]
 
 

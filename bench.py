@@ -71,11 +71,11 @@ def sources_sha256(step: str) -> str:
     return h.hexdigest()
 
 
-def stored_traffic(step: str, workload: str):
+def stored_traffic(step: str, workload: str, kernel: str):
     """HBM bytes per launch of the step's dominant kernel, from the rocprofv3
     FETCH_SIZE / WRITE_SIZE summary under profiles/, or None when there is none
     or the kernel's sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAMES[step]}_{workload}_traffic.md")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -187,6 +187,10 @@ def main() -> int:
     per = {n: acc[n] / a.steps for n in names}
     nbytes = step_bytes(w)
     dom = max(per, key=per.get)
+    kname = KERNEL_NAMES[dom]
+    if dom == "gather" and not (w.s == 1 and w.k <= 64 and w.m <= 64):
+        # the one-pass kernel serves s = 1 with k, m <= 64 only
+        kname = "gather_kernel" if w.s == 1 else "gather_kernel+combine_kernel"
     achieved = nbytes[dom] / (per[dom] * 1e-3) / 1e9
     if a.breakdown:
         for n in names:
@@ -207,9 +211,9 @@ def main() -> int:
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "m": w.m, "k": w.k, "s": w.s,
                    "grid": [w.grid_h, w.grid_w], "pool": [w.pool_h, w.pool_w]},
-        "roofline": {"bound": "hbm", "kernel": KERNEL_NAMES[dom], "achieved": achieved, "peak": HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": stored_traffic(dom, w.name), "algorithmic_bytes": nbytes[dom]},
+                     "traffic": stored_traffic(dom, w.name, kname), "algorithmic_bytes": nbytes[dom]},
         "step_ms": per,
     }
     if not a.no_cpu:

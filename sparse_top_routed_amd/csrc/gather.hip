@@ -303,9 +303,13 @@ __device__ __forceinline__ void load_rows(KVRegs<T, D, 1>& R, const RowIdx<T, D>
   }
 }
 
-// Persistent expert-grouped attention. Workgroup b walks the tile-table entries
-// [b C, (b + 1) C) (slice-major, so consecutive tiles mostly share a slice):
-// it lists the real tiles in LDS and streams their 64-key routed blocks
+// Persistent expert-grouped attention. The tile table (slice-major, the tiles
+// of one expert adjacent) is cut into one contiguous run per group of gs
+// workgroups; the gs members of a group sit on one XCD (workgroups go
+// round-robin to the 8 XCDs) and each takes every gs-th entry of the run, so
+// they work on neighbouring tiles of the same expert at the same time and that
+// expert's gathered rows come from the XCD's L2 after the first read. Each
+// workgroup lists its real tiles in LDS and streams their 64-key routed blocks
 // (block j = tile j / B, keys 64 (j % B), B = ceil(k / 64)). While block j
 // computes, the rows of block j + 1 (their indices already in registers) and the
 // indices of block j + 2 are in flight, so no prefetch waits on a dependent
@@ -318,21 +322,26 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ Q, co
                                                      const void* __restrict__ qtop, const void* __restrict__ vtop,
                                                      T* __restrict__ out, float* __restrict__ pacc,
                                                      float* __restrict__ pml, int N, int m, int k, int s,
-                                                     int max_tiles, long total, int chunk, float sl2e) {
+                                                     int max_tiles, long total, long gchunk, int gs, float sl2e) {
   using TL = Tiles<T, D>;
   constexpr bool BF = TL::BF;
   constexpr int KP = BF ? 2 : 1;
   __shared__ GatherLds<T, D, FUSED> sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
   const int rowi = 16 * w + r;
-  const long c0 = (long)blockIdx.x * chunk, c1 = min(total, c0 + chunk);
+  const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3, gpx = (int)(gridDim.x >> 3) / gs;
+  if (jx >= gpx * gs) return;   // workgroup-uniform
+  const int grp = xcd * gpx + jx / gs, jj = jx % gs;
+  // this workgroup's entries: g0 + jj + gs e, e = 0 .. nent - 1
+  const long g0 = (long)grp * gchunk, g1 = min(total, g0 + gchunk);
+  const long nent = g1 - g0 > jj ? (g1 - g0 - jj + gs - 1) / gs : 0;
   const bool resident = FUSED && m <= kKeyBlock;
   const int B = (k + kKeyBlock - 1) / kKeyBlock;
 
-  for (long base = c0; base < c1; base += 256) {
+  for (long base = 0; base < nent; base += 256) {
     // list the real tiles of this batch of entries
-    const long ent = base + tid;
-    const int4 te = ent < c1 ? tiles[ent] : make_int4(-1, 0, 0, 0);
+    const long e = base + tid, ent = g0 + jj + gs * e;
+    const int4 te = e < nent ? tiles[ent] : make_int4(-1, 0, 0, 0);
     const uint32_t f = te.x >= 0 ? 1u : 0u;
     uint32_t nt;
     const uint32_t pos = block_incl_scan(f, sm.wtot, nt) - f;
@@ -731,12 +740,13 @@ static hipError_t gather_launch(const Plan& p, const void* Q, const void* K, con
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_f, gather_kernel<T, D, true>, 256, 0) != hipSuccess) occ_f = 1;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_p, gather_kernel<T, D, false>, 256, 0) != hipSuccess) occ_p = 1;
   }
-  // persistent grid: one resident workgroup per slot, each walking a contiguous chunk
+  // persistent grid: one resident workgroup per slot, in groups of gs on one XCD,
+  // each group walking a contiguous run of the tile table
   const long total = (long)p.max_tiles * p.BH;
   const int slots = n_cu * std::max(1, p.s == 1 ? occ_f : occ_p);
-  const int groups = (int)std::min<long>(total, slots);
-  const int chunk = (int)((total + groups - 1) / groups);
-  const int grid = (int)((total + chunk - 1) / chunk);
+  const int gsz = std::max(1, std::min(8, slots / 8));
+  const int grid = std::max(8 * gsz, slots / (8 * gsz) * 8 * gsz);
+  const long gchunk = (total + grid / gsz - 1) / (grid / gsz);
   // the one-pass kernel where its double-buffered LDS fits a workgroup
   constexpr bool one_pass_fits = sizeof(Gather1Lds<T, D>) <= 160 * 1024;
   if constexpr (one_pass_fits) if (p.s == 1 && p.k <= kKeyBlock && p.m <= kKeyBlock) {
@@ -756,13 +766,13 @@ static hipError_t gather_launch(const Plan& p, const void* Q, const void* K, con
     hipLaunchKernelGGL((gather_kernel<T, D, true>), dim3(grid), dim3(256), 0, st, (const T*)Q, (const T*)K, (const T*)V,
                        (const int32_t*)(ws + p.ws.I), (const int4*)(ws + p.ws.tiles), (const int32_t*)(ws + p.ws.perm),
                        (const void*)(ws + p.ws.qtop), vtop, (T*)out, (float*)nullptr, (float*)nullptr, p.N, p.m, p.k,
-                       p.s, p.max_tiles, total, chunk, sl2e);
+                       p.s, p.max_tiles, total, gchunk, gsz, sl2e);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((gather_kernel<T, D, false>), dim3(grid), dim3(256), 0, st, (const T*)Q, (const T*)K, (const T*)V,
                      (const int32_t*)(ws + p.ws.I), (const int4*)(ws + p.ws.tiles), (const int32_t*)(ws + p.ws.perm),
                      (const void*)(ws + p.ws.qtop), vtop, (T*)out, (float*)(ws + p.ws.pacc), (float*)(ws + p.ws.pml),
-                     p.N, p.m, p.k, p.s, p.max_tiles, total, chunk, sl2e);
+                     p.N, p.m, p.k, p.s, p.max_tiles, total, gchunk, gsz, sl2e);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((combine_kernel<T, D>), dim3(p.qtiles, p.BH), dim3(256), 0, st, (const T*)Q,
                      (const void*)(ws + p.ws.qtop), vtop, (const float*)(ws + p.ws.pacc), (const float*)(ws + p.ws.pml),

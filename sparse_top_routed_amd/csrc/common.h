@@ -151,6 +151,15 @@ __device__ __forceinline__ uint32_t wave_max_uniform(uint32_t x) {
              max((uint32_t)__builtin_amdgcn_readlane(x, 32), (uint32_t)__builtin_amdgcn_readlane(x, 48)));
 }
 
+__device__ __forceinline__ uint32_t wave_min_uniform(uint32_t x) {
+  x = min(x, dpp_u32<0xB1>(x));
+  x = min(x, dpp_u32<0x4E>(x));
+  x = min(x, dpp_u32<0x141>(x));
+  x = min(x, dpp_u32<0x140>(x));
+  return min(min((uint32_t)__builtin_amdgcn_readlane(x, 0), (uint32_t)__builtin_amdgcn_readlane(x, 16)),
+             min((uint32_t)__builtin_amdgcn_readlane(x, 32), (uint32_t)__builtin_amdgcn_readlane(x, 48)));
+}
+
 // Inclusive prefix sum over the 256 threads of a block, in thread order.
 __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wtot, uint32_t& total) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;

@@ -6,7 +6,8 @@
 // Flash-style: a workgroup takes 64 landmarks (16 per wave) and one chunk of
 // keys (the workgroups sharing a chunk are placed on one XCD), streams the chunk through LDS 64 keys at a time (the next block is
 // fetched into registers while the current one computes) and keeps an online
-// softmax. A second kernel merges the chunks' partial softmaxes into V~. The
+// softmax. A second kernel merges the chunks' partial softmaxes into V~ (and,
+// from the group maxima below, sets step 3's candidate thresholds). The
 // scores themselves do not go to memory: only maxima of groups of 16 (one
 // lane's share of a block) or 64 (a block) per landmark, from which step 3 sets
 // a threshold that its candidates must reach (written out in full only on
@@ -67,50 +68,6 @@ __global__ __launch_bounds__(256) void landmark_kernel(const T* __restrict__ K, 
   }
 }
 
-// Merge the chunks' partial softmaxes of each landmark into V~: four threads
-// per landmark, d/4 columns each. (A "last chunk merges" scheme inside the
-// kernel above would need device-scope fences, which write back the L2 of the
-// XCD for every workgroup: far dearer than this launch.)
-template <int D>
-__global__ __launch_bounds__(256) void landmark_merge_kernel(const float* __restrict__ lpart, float* __restrict__ vt32,
-                                                             uint16_t* __restrict__ vt16, int rows, int nsplit) {
-  constexpr int CW = D / 4;
-  const int t = blockIdx.x * 256 + threadIdx.x, row = t >> 2, col = (t & 3) * CW;
-  if (row >= rows) return;
-  const float* Pr = lpart + (size_t)row * nsplit * (D + 4);
-  float M = -INFINITY;
-#pragma unroll 4
-  for (int cc = 0; cc < nsplit; ++cc) M = fmaxf(M, Pr[(size_t)cc * (D + 4)]);
-  float L = 0.f;
-  float4 av[CW / 4];
-#pragma unroll
-  for (int e = 0; e < CW / 4; ++e) av[e] = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 2
-  for (int cc = 0; cc < nsplit; ++cc) {
-    const float* Pc = Pr + (size_t)cc * (D + 4);
-    const float2 ml = *(const float2*)Pc;
-    const float f = __builtin_amdgcn_exp2f(ml.x - M);
-    L = fmaf(f, ml.y, L);
-#pragma unroll
-    for (int e = 0; e < CW / 4; ++e) {
-      const float4 x = *(const float4*)(Pc + 4 + col + 4 * e);
-      av[e].x = fmaf(f, x.x, av[e].x);
-      av[e].y = fmaf(f, x.y, av[e].y);
-      av[e].z = fmaf(f, x.z, av[e].z);
-      av[e].w = fmaf(f, x.w, av[e].w);
-    }
-  }
-  const float inv = 1.f / L;
-  float* o32 = vt32 + (size_t)row * D + col;
-  uint16_t* o16 = vt16 + (size_t)row * D + col;
-#pragma unroll
-  for (int e = 0; e < CW / 4; ++e) {
-    const float4 v = make_float4(av[e].x * inv, av[e].y * inv, av[e].z * inv, av[e].w * inv);
-    *(float4*)(o32 + 4 * e) = v;
-    *(uint2*)(o16 + 4 * e) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
-  }
-}
-
 template <typename T, int D>
 static hipError_t landmark_launch(const Plan& p, const void* K, const void* V, char* ws, float* S_out,
                                   hipStream_t st) {
@@ -121,11 +78,9 @@ static hipError_t landmark_launch(const Plan& p, const void* K, const void* V, c
                      (float*)(ws + p.ws.bmax), p.N, p.m, p.lchunk, p.nsplit, p.gq, p.nbg, p.lm_tiles, p.BH, sl2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int rows = p.BH * p.m;
-  hipLaunchKernelGGL((landmark_merge_kernel<D>), dim3((rows * 4 + 255) / 256), dim3(256), 0, st,
-                     (const float*)(ws + p.ws.lpart), (float*)(ws + p.ws.vt32), (uint16_t*)(ws + p.ws.vt16), rows,
-                     p.nsplit);
-  return hipGetLastError();
+  // the chunks' partial softmaxes merged into V~, and the candidate thresholds of
+  // step 3 from the group maxima (merge_thresh_kernel, with the top-k kernels)
+  return launch_merge_thresh(p, ws, st);
 }
 
 hipError_t launch_landmark(const Plan& p, const void* K, const void* V, char* ws, float* S_out, hipStream_t st) {

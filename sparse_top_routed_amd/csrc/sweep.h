@@ -176,21 +176,24 @@ __device__ __forceinline__ void candidate_sweep(const T* Kz, int k0, int k1, con
     const uint32_t p2 = __shfl(packed, r + 32, WAVE), p3 = __shfl(packed, r + 48, WAVE);
     const uint32_t tot = p0 + p1 + p2 + p3;   // no byte exceeds 16: no carries
     const uint32_t ex = (g > 0 ? p0 : 0u) + (g > 1 ? p1 : 0u) + (g > 2 ? p2 : 0u);
-    if (flags && lm_ok) {
-      uint32_t run = base;
+    // slot of the lane's first candidate of each kt (one byte per kt): the
+    // landmark's candidates of earlier kt, then those of lanes with smaller g;
+    // the byte sums stay below 256
+    const uint32_t first = ex + (tot << 8) + (tot << 16) + (tot << 24);
+    // one pass per candidate of the lane (few: most scores are below the
+    // threshold), in (kt, j) order, i.e. in key order
+    uint32_t fl = lm_ok ? flags : 0u;
+    while (fl) {
+      const int bit = __builtin_ctz(fl);
+      fl &= fl - 1u;
+      const int kt = bit >> 2;
+      const uint32_t pos = base + ((first >> (8 * kt)) & 255u) +
+                           (uint32_t)__builtin_popcount(flags & ((1u << bit) - 1u) & (0xFu << (4 * kt)));
+      float x = acc[0][0];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        uint32_t pos = run + ((ex >> (8 * kt)) & 255u);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (flags & (1u << (4 * kt + j))) {
-            if (pos < (uint32_t)capc)
-              seg[pos] = make_uint2(f32_key(acc[kt][j]), (uint32_t)(kb + 16 * kt + 4 * g + j));
-            ++pos;
-          }
-        }
-        run += (tot >> (8 * kt)) & 255u;
-      }
+      for (int b = 1; b < 16; ++b) x = bit == b ? acc[b >> 2][b & 3] : x;
+      if (pos < (uint32_t)capc)
+        seg[pos] = make_uint2(f32_key(x), (uint32_t)(kb + 16 * kt + 4 * g + (bit & 3)));
     }
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) base += (tot >> (8 * kt)) & 255u;

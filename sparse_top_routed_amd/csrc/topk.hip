@@ -6,9 +6,10 @@
 // groups of 16 or 64 approximate scores; every group maximum is itself a score,
 // so the k-th largest of them, tau, is a lower bound of the row's k-th largest
 // approximate score T. Then:
-//   1. threshold kernel: tau per row by a bit search over the group maxima;
-//      the candidate threshold is tau - 2E (E_i = gamma |q~_i| max|K|, the proven
-//      bound on an approximate score's error), rounded down;
+//   1. threshold (at the end of step 2, with the shared-expert merge): tau per
+//      row by a bit search over the group maxima; the candidate threshold is
+//      tau - 2E (E_i = gamma |q~_i| max|K|, the proven bound on an approximate
+//      score's error), rounded down;
 //   2. candidate kernel: recomputes the approximate scores exactly as step 2 did
 //      (same MFMA sequence on the same operands, so the same bits) and writes
 //      every score at or above the threshold, with its token id, in index
@@ -85,24 +86,51 @@ __device__ __forceinline__ void band_keys(double Tf, double E, uint32_t& hiKey, 
   loKey = (Tf - 2.0 * E > -INFINITY) ? max(1u, f32_key(round_down_f32(Tf - 2.0 * E))) : 1u;
 }
 
+// The k-th largest of a wave's order keys (lane's keys in v[0..ns), 0 = absent;
+// at least k present), by a bit search from the top: the largest P with at
+// least k keys >= P. Every present key lies between the wave's smallest and
+// largest, so the bits those two share are settled at once. With lowbit > 0
+// the bits below lowbit stay 0: the result is then a lower bound of the k-th
+// largest key that differs from it only in those bits.
+template <int PV>
+__device__ __forceinline__ uint32_t kth_largest_key(const uint32_t (&v)[PV], int ns, uint32_t k, int lowbit) {
+  uint32_t hi = 0u, lo = 0xFFFFFFFFu;
+#pragma unroll
+  for (int p = 0; p < PV; ++p)
+    if (p < ns) {
+      hi = max(hi, v[p]);
+      lo = min(lo, v[p] ? v[p] : 0xFFFFFFFFu);
+    }
+  hi = wave_max_uniform(hi);
+  lo = wave_min_uniform(lo);
+  const uint32_t low_mask = (1u << lowbit) - 1u;
+  if (hi == lo) return hi & ~low_mask;
+  const int top = 31 - __builtin_clz(hi ^ lo);   // highest bit where the keys can differ
+  uint32_t pfx = top == 31 ? 0u : hi & ~((2u << top) - 1u);
+  for (int b = top; b >= lowbit; --b) {
+    const uint32_t cand = pfx | (1u << b);
+    uint32_t c = 0;
+#pragma unroll
+    for (int p = 0; p < PV; ++p)
+      if (p < ns) c += ballot_count(v[p] >= cand);
+    if (c >= k) pfx = cand;
+  }
+  return pfx;
+}
+
 // ---------------------------------------------------------------- 1. threshold
 // Candidate threshold of one row (as an order key; 0: none, every score is a
 // candidate) from its nbg group maxima, lane l holding maxima l, 64 + l, ...
 // (order keys, 0 past nbg): tau = the k-th largest maximum by a bit search
-// (ballots: one compare per register, the counting on the scalar unit), then
-// tau - 2E rounded down.
+// (ballots: one compare per register, the counting on the scalar unit) that
+// leaves the 12 lowest key bits at 0 (a lower bound of it, within 2^-11 of it
+// relative: the threshold only has to be low enough), then tau - 2E rounded
+// down.
 template <int PV>
 __device__ __forceinline__ uint32_t thresh_key(const uint32_t (&v)[PV], int nbg, int k, double E) {
   uint32_t key = 0u;
   if (nbg >= k) {
-    uint32_t pfx = 0u;
-    for (int b = 31; b >= 0; --b) {
-      const uint32_t cand = pfx | (1u << b);
-      uint32_t c = 0;
-#pragma unroll
-      for (int p = 0; p < PV; ++p) c += ballot_count(v[p] >= cand);
-      if (c >= (uint32_t)k) pfx = cand;
-    }
+    const uint32_t pfx = kth_largest_key<PV>(v, PV, (uint32_t)k, 12);
     const float tau = key_f32(pfx);
     if (tau > -INFINITY && tau < INFINITY) {
       const double t = (double)tau - 2.0 * E;
@@ -123,20 +151,51 @@ __device__ __forceinline__ void load_group_keys(const float* br, int nbg, int la
   }
 }
 
-// One wave per row (four rows per workgroup); the row's group maxima (at most
-// 64 PV) sit in registers.
-template <int PV>
-__global__ __launch_bounds__(256) void topk_thresh_kernel(const float* __restrict__ bmax,
-                                                          const float* __restrict__ qtnorm,
-                                                          const float* __restrict__ kmax, int nsplit,
-                                                          uint32_t* __restrict__ thr, uint32_t* __restrict__ glist,
-                                                          int nbg, int m, int k, double gamma, int rows) {
+// End of step 2 and start of step 3, one wave per score row (four rows per
+// workgroup): the chunks' partial softmaxes of landmark i are merged into V~_i
+// (lane l: columns l, l + 64, ...), and the row's candidate threshold is set
+// from its group maxima (at most 64 PV, in registers). Merging here, where each
+// row's maxima are read anyway, saves a launch between the two steps.
+template <int D, int PV>
+__global__ __launch_bounds__(256) void merge_thresh_kernel(const float* __restrict__ lpart,
+                                                           float* __restrict__ vt32, uint16_t* __restrict__ vt16,
+                                                           const float* __restrict__ bmax,
+                                                           const float* __restrict__ qtnorm,
+                                                           const float* __restrict__ kmax, int nsplit,
+                                                           uint32_t* __restrict__ thr, int nbg, int m, int k,
+                                                           double gamma, int rows) {
+  constexpr int CW = D / 64;
   const int tid = threadIdx.x, lane = tid & 63, row = blockIdx.x * 4 + (tid >> 6);
-  if (blockIdx.x == 0 && tid == 0) glist[0] = 0u;   // no fallback rows yet
-  if (row >= rows) return;
+  if (row >= rows) return;   // wave-uniform
   const int z = row / m;
   uint32_t v[PV];
   load_group_keys<PV>(bmax + (size_t)row * nbg, nbg, lane, v);
+
+  // partials [max, sum, pad, pad, acc[D]] per chunk
+  const float* Pr = lpart + (size_t)row * nsplit * (D + 4);
+  float M = -INFINITY;
+  for (int c = lane; c < nsplit; c += 64) M = fmaxf(M, Pr[(size_t)c * (D + 4)]);
+  M = wave_max(M);
+  float L = 0.f, acc[CW];
+#pragma unroll
+  for (int e = 0; e < CW; ++e) acc[e] = 0.f;
+#pragma unroll 2
+  for (int c = 0; c < nsplit; ++c) {
+    const float* Pc = Pr + (size_t)c * (D + 4);
+    const float2 ml = *(const float2*)Pc;
+    const float f = __builtin_amdgcn_exp2f(ml.x - M);
+    L = fmaf(f, ml.y, L);
+#pragma unroll
+    for (int e = 0; e < CW; ++e) acc[e] = fmaf(f, Pc[4 + lane + 64 * e], acc[e]);
+  }
+  const float inv = 1.f / L;
+#pragma unroll
+  for (int e = 0; e < CW; ++e) {
+    const float x = acc[e] * inv;
+    vt32[(size_t)row * D + lane + 64 * e] = x;
+    vt16[(size_t)row * D + lane + 64 * e] = f32_to_bf16(x);
+  }
+
   const double E = row_bound(qtnorm, kmax, nsplit, row, z, gamma, lane);
   const uint32_t key = thresh_key<PV>(v, nbg, k, E);
   if (lane == 0) thr[row] = key;
@@ -148,10 +207,12 @@ __global__ __launch_bounds__(256) void topk_thresh_kernel(const float* __restric
 template <typename T, int D>
 __global__ __launch_bounds__(256) void topk_cand_kernel(const T* __restrict__ K, const void* __restrict__ qtop,
                                                         const uint32_t* __restrict__ thr, uint2* __restrict__ cand,
-                                                        uint32_t* __restrict__ ccnt, int N, int m, int lchunk,
-                                                        int nsplit, int capc, int lm_tiles, int BH) {
+                                                        uint32_t* __restrict__ ccnt, uint32_t* __restrict__ glist,
+                                                        int N, int m, int lchunk, int nsplit, int capc, int lm_tiles,
+                                                        int BH) {
   using TL = Tiles<T, D>;
   __shared__ __align__(16) T Ks[TL::KTILE];
+  if (blockIdx.x == 0 && threadIdx.x == 0) glist[0] = 0u;   // no fallback rows yet (the select kernel adds them)
   int lt, c, z;
   if (!chunk_item(lm_tiles, nsplit, BH, lt, c, z)) return;   // workgroup-uniform
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
@@ -208,7 +269,7 @@ __global__ __launch_bounds__(64 * WPB) void topk_select_kernel(const uint2* __re
     const uint32_t n = lane < nsplit ? cnt[lane] : 0u;
     const uint32_t off = wave_excl_scan(n, total);
     total = __builtin_amdgcn_readfirstlane(total);   // wave-uniform: keep the loops below scalar
-    if (__any(n > (uint32_t)capc) || total > (uint32_t)CAP) {
+    if (__any(n > (uint32_t)capc) || total > (uint32_t)CAP || total < (uint32_t)k) {
       fallback();
       return;
     }
@@ -235,7 +296,7 @@ __global__ __launch_bounds__(64 * WPB) void topk_select_kernel(const uint2* __re
       total += tot;
     }
     total = __builtin_amdgcn_readfirstlane(total);
-    if (__any(over) || total > (uint32_t)CAP || nsplit > BAND) {
+    if (__any(over) || total > (uint32_t)CAP || total < (uint32_t)k || nsplit > BAND) {
       fallback();
       return;
     }
@@ -256,15 +317,7 @@ __global__ __launch_bounds__(64 * WPB) void topk_select_kernel(const uint2* __re
     ck[sl] = (sl < ns && j < total) ? cs[j].x : 0u;
   }
   // exact k-th largest candidate key
-  uint32_t that = 0;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t tst = that | (1u << b);
-    uint32_t c = 0;
-#pragma unroll
-    for (int sl = 0; sl < SL; ++sl)
-      if (sl < ns) c += ballot_count(ck[sl] >= tst);
-    if (c >= (uint32_t)k) that = tst;
-  }
+  const uint32_t that = kth_largest_key<SL>(ck, ns, (uint32_t)k, 0);
   uint32_t hiKey, loKey;
   band_keys((double)key_f32(that), E, hiKey, loKey);
   uint32_t cin = 0, nb = 0;
@@ -438,23 +491,12 @@ static hipError_t topk_launch(const Plan& p, const void* K, char* ws, hipStream_
   const int rows = p.BH * p.m;
   uint32_t* glist = (uint32_t*)(ws + p.ws.glist);
   hipError_t e = hipSuccess;
-  const bool thresholds = p.cap > 0 && p.nbg <= kTopkMaxGroups;
   if (p.cap > 0) {
-    // thresholds (rows of more than kTopkMaxGroups group maxima: none, every score a candidate)
-    const dim3 tg((rows + 3) / 4);
-    auto th = [&](auto kern) {
-      hipLaunchKernelGGL(kern, tg, dim3(256), 0, st, (const float*)(ws + p.ws.bmax), (const float*)(ws + p.ws.qtnorm),
-                         (const float*)(ws + p.ws.kmax), p.nsplit, (uint32_t*)(ws + p.ws.thr), glist,
-                         thresholds ? p.nbg : 0, p.m, p.k, p.gamma_qk, rows);
-    };
-    if (!thresholds || p.nbg <= 256) th(topk_thresh_kernel<4>);
-    else if (p.nbg <= 1024) th(topk_thresh_kernel<16>);
-    else th(topk_thresh_kernel<64>);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // candidates against the thresholds the landmark step set (merge_thresh_kernel)
     const int cgrid = 8 * ((p.nsplit * p.BH + 7) / 8) * p.lm_tiles;   // see chunk_item
     hipLaunchKernelGGL((topk_cand_kernel<T, D>), dim3(cgrid), dim3(256), 0, st, (const T*)K,
                        (const void*)(ws + p.ws.qtop), (const uint32_t*)(ws + p.ws.thr), (uint2*)(ws + p.ws.cand),
-                       (uint32_t*)(ws + p.ws.ccnt), p.N, p.m, p.lchunk, p.nsplit, p.capc, p.lm_tiles, p.BH);
+                       (uint32_t*)(ws + p.ws.ccnt), glist, p.N, p.m, p.lchunk, p.nsplit, p.capc, p.lm_tiles, p.BH);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     auto sel = [&](auto kern, int wpb) {
       hipLaunchKernelGGL(kern, dim3((rows + wpb - 1) / wpb), dim3(64 * wpb), 0, st, (const uint2*)(ws + p.ws.cand),
@@ -477,6 +519,28 @@ static hipError_t topk_launch(const Plan& p, const void* K, char* ws, hipStream_
                      (const double*)(ws + p.ws.qt64), (const T*)K, (int32_t*)(ws + p.ws.I), (const uint32_t*)glist,
                      (double*)(ws + p.ws.gscr), p.N, p.m, p.k);
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t merge_thresh_launch(const Plan& p, char* ws, hipStream_t st) {
+  const int rows = p.BH * p.m;
+  // rows of more than kTopkMaxGroups group maxima, or k beyond the select kernel:
+  // no threshold (every score a candidate, or every row to the fallback)
+  const int nbg = (p.cap > 0 && p.nbg <= kTopkMaxGroups) ? p.nbg : 0;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((rows + 3) / 4), dim3(256), 0, st, (const float*)(ws + p.ws.lpart),
+                       (float*)(ws + p.ws.vt32), (uint16_t*)(ws + p.ws.vt16), (const float*)(ws + p.ws.bmax),
+                       (const float*)(ws + p.ws.qtnorm), (const float*)(ws + p.ws.kmax), p.nsplit,
+                       (uint32_t*)(ws + p.ws.thr), nbg, p.m, p.k, p.gamma_qk, rows);
+  };
+  if (nbg <= 256) go(merge_thresh_kernel<D, 4>);
+  else if (nbg <= 1024) go(merge_thresh_kernel<D, 16>);
+  else go(merge_thresh_kernel<D, 64>);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_thresh(const Plan& p, char* ws, hipStream_t st) {
+  return p.d == 64 ? merge_thresh_launch<64>(p, ws, st) : merge_thresh_launch<128>(p, ws, st);
 }
 
 hipError_t launch_topk(const Plan& p, const void* K, char* ws, hipStream_t st) {

@@ -6,46 +6,49 @@
 // Fast kernels (s <= 6): 16 queries per wave; landmark blocks of 64 are staged
 // in LDS and multiplied on MFMA (bf16: Q~ as hi + lo parts, so the scores have a
 // proven error E_q = gamma |q| max|q~|). Each lane keeps a sorted top list of its
-// landmarks; the four lanes of a query merge theirs. If the s-th and (s+1)-th
-// scores are more than 2E_q apart the set is certain; otherwise the entries
-// within 2E_q of the s-th score are re-scored in fp64, or (m > 64, band longer
-// than the list) the query is queued for the exact kernel, which scores all m
-// landmarks in fp64 and ranks them. For s > 6 every query goes through the
-// exact kernel.
+// landmarks' scores (m <= 64: the scores alone, which stay in registers; m > 64:
+// keys that carry the landmark id); the four lanes of a query merge theirs. If
+// the s-th and (s+1)-th scores are more than 2E_q apart the set is certain;
+// otherwise the entries within 2E_q of the s-th score are re-scored in fp64, or
+// (m > 64, band longer than the list) the query is queued for the exact kernel,
+// which scores all m landmarks in fp64 and ranks them. For s > 6 every query
+// goes through the exact kernel. The order of the s ids within a query's list
+// is not specified.
 #include "attn_core.h"
 
 namespace mita {
 
-// Insert into a descending top list. Within a lane the landmarks arrive in
-// increasing id, so an equal later value must stay below: strict comparison.
+// Descending top lists kept with three-input medians: inserting x into
+// t[0] >= t[1] >= ... makes the new t[j] the median of the old t[j - 1], t[j]
+// and x (t[0]: the maximum), one instruction per entry, all independent.
 template <int TM>
-__device__ __forceinline__ void list_insert_ordered(float (&tv)[TM], int (&ti)[TM], float v, int i) {
+__device__ __forceinline__ void top_insert(float (&t)[TM], float x) {
 #pragma unroll
-  for (int j = 0; j < TM; ++j) {
-    const bool better = v > tv[j];
-    const float ov = tv[j];
-    const int oi = ti[j];
-    tv[j] = better ? v : ov;
-    ti[j] = better ? i : oi;
-    v = better ? ov : v;
-    i = better ? oi : i;
-  }
+  for (int j = TM - 1; j >= 1; --j) t[j] = __builtin_amdgcn_fmed3f(t[j - 1], t[j], x);
+  t[0] = fmaxf(t[0], x);
+}
+__device__ __forceinline__ uint32_t med3_u32(uint32_t a, uint32_t b, uint32_t c) {
+  return max(min(a, b), min(max(a, b), c));
+}
+template <int TM>
+__device__ __forceinline__ void top_insert(uint32_t (&t)[TM], uint32_t x) {
+#pragma unroll
+  for (int j = TM - 1; j >= 1; --j) t[j] = med3_u32(t[j - 1], t[j], x);
+  t[0] = max(t[0], x);
 }
 
-// Same with ties broken by the lower id (merging lists of different lanes).
-template <int TM>
-__device__ __forceinline__ void list_insert(float (&tv)[TM], int (&ti)[TM], float v, int i) {
-#pragma unroll
-  for (int j = 0; j < TM; ++j) {
-    const bool better = (v > tv[j]) | ((v == tv[j]) & (i < ti[j]));   // bitwise: no short-circuit branches
-    const float ov = tv[j];
-    const int oi = ti[j];
-    tv[j] = better ? v : ov;
-    ti[j] = better ? i : oi;
-    v = better ? ov : v;
-    i = better ? oi : i;
-  }
-}
+// Landmark score as a sortable key that carries its landmark id: the order key
+// of the score with its low ib bits replaced by imask - id (imask = 2^ib - 1 >=
+// m - 1), so keys are distinct, a higher score wins and, among scores equal
+// after the truncation, the lower id wins. Real keys are never 0.
+struct RouteKey {
+  uint32_t imask;
+  __device__ __forceinline__ uint32_t make(float v, int li) const { return (f32_key(v) & ~imask) | (imask - li); }
+  __device__ __forceinline__ int id(uint32_t k) const { return (int)(imask - (k & imask)); }
+  // bounds of the score a key stands for
+  __device__ __forceinline__ double lo(uint32_t k) const { return (double)key_f32(k & ~imask); }
+  __device__ __forceinline__ double hi(uint32_t k) const { return (double)key_f32(k | imask); }
+};
 
 template <typename T>
 __device__ __forceinline__ double load_f64(const T* p, int c) {
@@ -197,12 +200,11 @@ __global__ __launch_bounds__(256) void route_fast_kernel(const T* __restrict__ Q
     }
     load_q(qb_n, qf_n, qrow_of(min(t + 1, t1 - 1)));   // next tile's rows in flight
 
-    float tv[TM];
-    int ti[TM];
+    float tv[TM];   // the TM largest scores of the lane, then of the query
 #pragma unroll
-    for (int j = 0; j < TM; ++j) { tv[j] = -INFINITY; ti[j] = 0x7FFFFFFF; }
+    for (int j = 0; j < TM; ++j) tv[j] = -INFINITY;
     f32x4 acc[4];
-    for (int lb0 = 0; lb0 < m; lb0 += kKeyBlock) {
+    for (int lb0 = 0; lb0 < m; lb0 += kKeyBlock) {   // one block (m <= 64)
       if constexpr (BF)
         qk_bf16<D, 2, 1>((const uint16_t*)Ks0, (const uint16_t*)Ks1, qb, acc, lane);
       else
@@ -211,18 +213,18 @@ __global__ __launch_bounds__(256) void route_fast_kernel(const T* __restrict__ Q
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int li = lb0 + 16 * kt + 4 * g + j;   // past m: -inf never enters the list
-          list_insert_ordered<TM>(tv, ti, li < m ? acc[kt][j] : -INFINITY, li);
+          const int li = lb0 + 16 * kt + 4 * g + j;   // past m: -inf
+          if (li >= m) acc[kt][j] = -INFINITY;
+          top_insert<TM>(tv, acc[kt][j]);
         }
     }
 #pragma unroll
     for (int sh = 16; sh <= 32; sh <<= 1) {
       float ov[TM];
-      int oi[TM];
 #pragma unroll
-      for (int j = 0; j < TM; ++j) { ov[j] = __shfl_xor(tv[j], sh, WAVE); oi[j] = __shfl_xor(ti[j], sh, WAVE); }
+      for (int j = 0; j < TM; ++j) ov[j] = __shfl_xor(tv[j], sh, WAVE);
 #pragma unroll
-      for (int j = 0; j < TM; ++j) list_insert<TM>(tv, ti, ov[j], oi[j]);
+      for (int j = 0; j < TM; ++j) top_insert<TM>(tv, ov[j]);
     }
 
     float sq = 0.f;
@@ -239,7 +241,7 @@ __global__ __launch_bounds__(256) void route_fast_kernel(const T* __restrict__ Q
     }
     const float qn = sqrtf(quad_sum(sq)) * 1.0001f;
     const double Eq = gamma * (double)qn * qtmax;
-    // s-th and (s+1)-th entries without dynamic register indexing
+    // s-th and (s+1)-th scores without dynamic register indexing
     float v_s = -INFINITY, v_s1 = -INFINITY;
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
@@ -248,25 +250,46 @@ __global__ __launch_bounds__(256) void route_fast_kernel(const T* __restrict__ Q
     }
     const double That = (double)v_s, lo = That - 2.0 * Eq, hi = That + 2.0 * Eq;
     const bool certain = s >= m || (double)v_s - (double)v_s1 > 2.0 * Eq;
-    int32_t* Eq_out = E + ((size_t)z * N + min(q, N - 1)) * s;
-    if (q_ok && g == 0 && certain) {
-#pragma unroll
-      for (int j = 0; j < TM; ++j)
-        if (j < s) Eq_out[j] = ti[j];
-    }
     const bool unc = q_ok && !certain;
+    int32_t* Eq_out = E + ((size_t)z * N + min(q, N - 1)) * s;
+    // Landmarks of the query in a mask over its quad (bit 16 g' + 4 kt + j: lane
+    // g' of the quad, score acc[kt][j]) and written to Eq_out[base ..] by one
+    // lane per member. Certain: the s scores >= v_s (more than 2 E_q above the
+    // rest, so no tie at the boundary). Uncertain: those above the band are in,
+    // the band is re-scored in fp64.
+    auto quad_mask = [&](auto pred) {   // the query's scores that satisfy pred
+      uint32_t mk = 0;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mk |= pred(acc[kt][j]) ? 1u << (4 * kt + j) : 0u;
+      uint64_t qm = 0;
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) qm |= (uint64_t)__shfl(mk, r + 16 * gg, WAVE) << (16 * gg);
+      return qm;
+    };
+    auto landmark_of = [](int bit) { const int b = bit & 15; return 16 * (b >> 2) + 4 * (bit >> 4) + (b & 3); };
+    auto write_mask = [&](uint64_t qm, int base) {   // same trip count on the four lanes of a query
+      int pos = base;
+      while (qm) {
+        const int bit = __builtin_ctzll(qm);
+        qm &= qm - 1;
+        if (g == 0) Eq_out[pos] = landmark_of(bit);
+        ++pos;
+      }
+      return pos;
+    };
+    {
+      const bool take = q_ok && certain;
+      const uint64_t qm = quad_mask([&](float v) { return take && v >= v_s; });
+      write_mask(qm, 0);
+    }
     if (!__any(unc)) continue;
 
     // entries above the band are in for sure; the band is ranked in fp64
-    int c_in = 0;
-#pragma unroll
-    for (int j = 0; j < TM; ++j) c_in += (j < s && (double)tv[j] > hi) ? 1 : 0;
+    const uint64_t in_m = quad_mask([&](float v) { return unc && (double)v > hi; });
+    const int c_in = write_mask(in_m, 0);
     const int need = s - c_in;
-    if (unc && g == 0) {
-#pragma unroll
-      for (int j = 0; j < TM; ++j)
-        if (j < c_in) Eq_out[j] = ti[j];
-    }
     // fp64 partial dot of this lane's share of the query with landmark li
     auto part64 = [&](int li) {
       const double* qr = qt64z + (size_t)li * D;
@@ -287,18 +310,7 @@ __global__ __launch_bounds__(256) void route_fast_kernel(const T* __restrict__ Q
     };
     // every score of the query is in acc (lanes of the quad hold 16 each):
     // the band members are re-scored one by one, quad-uniformly
-    uint32_t mk = 0;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int li = 16 * kt + 4 * g + j;
-        const double v = (double)acc[kt][j];
-        mk |= (unc && li < m && v >= lo && v <= hi) ? 1u << (4 * kt + j) : 0u;
-      }
-    uint64_t qm = 0;
-#pragma unroll
-    for (int gg = 0; gg < 4; ++gg) qm |= (uint64_t)__shfl(mk, r + 16 * gg, WAVE) << (16 * gg);
+    uint64_t qm = quad_mask([&](float v) { return unc && (double)v >= lo && (double)v <= hi; });
     double bv[TM];
     int bi[TM];
 #pragma unroll
@@ -306,9 +318,8 @@ __global__ __launch_bounds__(256) void route_fast_kernel(const T* __restrict__ Q
     while (qm) {   // same trip count on the four lanes of a query
       const int bit = __builtin_ctzll(qm);
       qm &= qm - 1;
-      const int b = bit & 15, li = 16 * (b >> 2) + 4 * (bit >> 4) + (b & 3);
-      double v = part64(li);
-      int i = li;
+      double v = part64(landmark_of(bit));
+      int i = landmark_of(bit);
 #pragma unroll
       for (int j = 0; j < TM; ++j) {   // insert by (score desc, id asc)
         const bool better = (v > bv[j]) | ((v == bv[j]) & (i < bi[j]));
@@ -371,12 +382,12 @@ __global__ __launch_bounds__(256) void route_multi_kernel(const T* __restrict__ 
   qtm = wave_max(qtm);
   if (lane == 0) s_red[w] = qtm;
 
-  float tv[TPW][TM];
-  int ti[TPW][TM];
+  const RouteKey rk{(2u << (31 - __builtin_clz((uint32_t)(m - 1)))) - 1u};   // m > 64: imask >= m - 1
+  uint32_t tk[TPW][TM];   // the TM largest keys of the lane, then of the query
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
-    for (int j = 0; j < TM; ++j) { tv[tt][j] = -INFINITY; ti[tt][j] = 0x7FFFFFFF; }
+    for (int j = 0; j < TM; ++j) tk[tt][j] = 0u;
   for (int lb0 = 0; lb0 < m; lb0 += kKeyBlock) {
     __syncthreads();   // readers of the previous block are done
     const int nvalid = min(kKeyBlock, m - lb0);
@@ -395,8 +406,8 @@ __global__ __launch_bounds__(256) void route_multi_kernel(const T* __restrict__ 
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int li = lb0 + 16 * kt + 4 * g + j;   // past m: -inf never enters the list
-          list_insert_ordered<TM>(tv[tt], ti[tt], li < m ? acc[kt][j] : -INFINITY, li);
+          const int li = lb0 + 16 * kt + 4 * g + j;   // past m: key 0 never enters the list
+          top_insert<TM>(tk[tt], li < m ? rk.make(acc[kt][j], li) : 0u);
         }
     }
   }
@@ -409,12 +420,11 @@ __global__ __launch_bounds__(256) void route_multi_kernel(const T* __restrict__ 
     const T* qrow = Q + ((size_t)z * N + min(q, N - 1)) * D;
 #pragma unroll
     for (int sh = 16; sh <= 32; sh <<= 1) {
-      float ov[TM];
-      int oi[TM];
+      uint32_t ok[TM];
 #pragma unroll
-      for (int j = 0; j < TM; ++j) { ov[j] = __shfl_xor(tv[tt][j], sh, WAVE); oi[j] = __shfl_xor(ti[tt][j], sh, WAVE); }
+      for (int j = 0; j < TM; ++j) ok[j] = __shfl_xor(tk[tt][j], sh, WAVE);
 #pragma unroll
-      for (int j = 0; j < TM; ++j) list_insert<TM>(tv[tt], ti[tt], ov[j], oi[j]);
+      for (int j = 0; j < TM; ++j) top_insert<TM>(tk[tt], ok[j]);
     }
     float sq = 0.f;
     if constexpr (BF) {
@@ -430,32 +440,36 @@ __global__ __launch_bounds__(256) void route_multi_kernel(const T* __restrict__ 
     }
     const float qn = sqrtf(quad_sum(sq)) * 1.0001f;
     const double Eq = gamma * (double)qn * qtmax;
-    float v_s = -INFINITY, v_s1 = -INFINITY;
+    // s-th and (s+1)-th keys without dynamic register indexing; each key bounds
+    // its score from both sides, so the s-th score lies in [lo(k_s), hi(k_s)]
+    uint32_t k_s = 0u, k_s1 = 0u;
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
-      if (j == s - 1) v_s = tv[tt][j];
-      if (j == s) v_s1 = tv[tt][j];
+      if (j == s - 1) k_s = tk[tt][j];
+      if (j == s) k_s1 = tk[tt][j];
     }
-    const double That = (double)v_s, lo = That - 2.0 * Eq, hi = That + 2.0 * Eq;
-    const bool certain = s >= m || (double)v_s - (double)v_s1 > 2.0 * Eq;
+    const double lo = rk.lo(k_s) - 2.0 * Eq, hi = rk.hi(k_s) + 2.0 * Eq;
+    const bool certain = s >= m || rk.lo(k_s) - rk.hi(k_s1) > 2.0 * Eq;
     int32_t* Eq_out = E + ((size_t)z * N + min(q, N - 1)) * s;
     if (q_ok && g == 0 && certain) {
 #pragma unroll
       for (int j = 0; j < TM; ++j)
-        if (j < s) Eq_out[j] = ti[tt][j];
+        if (j < s) Eq_out[j] = rk.id(tk[tt][j]);
     }
     const bool unc = q_ok && !certain;
     if (!__any(unc)) continue;
+    // in for sure: keys whose lowest possible score is above the band (they lead the list)
     int c_in = 0;
 #pragma unroll
-    for (int j = 0; j < TM; ++j) c_in += (j < s && (double)tv[tt][j] > hi) ? 1 : 0;
+    for (int j = 0; j < TM; ++j) c_in += (j < s && rk.lo(tk[tt][j]) > hi) ? 1 : 0;
     const int need = s - c_in;
     if (unc && g == 0) {
 #pragma unroll
       for (int j = 0; j < TM; ++j)
-        if (j < c_in) Eq_out[j] = ti[tt][j];
+        if (j < c_in) Eq_out[j] = rk.id(tk[tt][j]);
     }
-    const bool refine = unc && (m <= TM || (double)tv[tt][TM - 1] < lo);
+    // the list holds the whole band when its last key's highest possible score is below it
+    const bool refine = unc && rk.hi(tk[tt][TM - 1]) < lo;
     if (unc && !refine && g == 0) {
       const uint32_t pos = atomicAdd(&counters[0], 1u);
       rflag[pos] = (uint32_t)(z * N + q);
@@ -463,11 +477,12 @@ __global__ __launch_bounds__(256) void route_multi_kernel(const T* __restrict__ 
     if (__any(refine)) {
       double s64[TM];
       bool band[TM];
+      int tid_[TM];
 #pragma unroll
       for (int j = 0; j < TM; ++j) {
-        const double v = (double)tv[tt][j];
-        band[j] = refine && ti[tt][j] < m && v >= lo && v <= hi;
-        const double* qr = qt64z + (size_t)(band[j] ? ti[tt][j] : 0) * D;
+        tid_[j] = rk.id(tk[tt][j]);
+        band[j] = refine && j >= c_in && tk[tt][j] != 0u && rk.hi(tk[tt][j]) >= lo;
+        const double* qr = qt64z + (size_t)(band[j] ? tid_[j] : 0) * D;
         double part = 0.0;
         if constexpr (BF) {
 #pragma unroll
@@ -490,8 +505,8 @@ __global__ __launch_bounds__(256) void route_multi_kernel(const T* __restrict__ 
           int rank = 0;
 #pragma unroll
           for (int f = 0; f < TM; ++f)
-            rank += (band[f] && ((s64[f] > s64[j]) | ((s64[f] == s64[j]) & (ti[tt][f] < ti[tt][j])))) ? 1 : 0;
-          if (rank < need) Eq_out[c_in + rank] = ti[tt][j];
+            rank += (band[f] && ((s64[f] > s64[j]) | ((s64[f] == s64[j]) & (tid_[f] < tid_[j])))) ? 1 : 0;
+          if (rank < need) Eq_out[c_in + rank] = tid_[j];
         }
       }
     }

@@ -94,6 +94,59 @@ __global__ __launch_bounds__(256) void bucket_scatter_kernel(const int32_t* __re
     if (ex[u] >= 0) pz[h[m + ex[u]] + rank[u]] = start + tid + 256 * u;
 }
 
+// The whole counting sort of one slice in one workgroup, for slices of at most
+// 256 PER (query, slot) pairs: bucket sizes by LDS atomics (each pair keeps the
+// rank its atomic returned), their exclusive scan, the tile table and the
+// scatter. Ranks within a bucket follow the atomics' order; every query of a
+// tile is computed on its own, so the output does not depend on it.
+template <int PER>
+__global__ __launch_bounds__(256) void bucket_slice_kernel(const int32_t* __restrict__ E, uint32_t* __restrict__ boff,
+                                                           int4* __restrict__ tiles, int32_t* __restrict__ perm,
+                                                           int Ns, int m, int max_tiles) {
+  extern __shared__ uint32_t h[];   // [0, m): bucket sizes, [m, 2m): bucket offsets
+  __shared__ uint32_t wtot[4];
+  const int z = blockIdx.x, tid = threadIdx.x;
+  for (int i = tid; i < m; i += 256) h[i] = 0;
+  __syncthreads();
+  const int32_t* Ez = E + (size_t)z * Ns;
+  int ex[PER];
+  uint32_t rank[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = tid + 256 * u;
+    ex[u] = e < Ns ? Ez[e] : -1;
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    if ((unsigned)ex[u] >= (unsigned)m) ex[u] = -1;
+    rank[u] = ex[u] >= 0 ? atomicAdd(&h[ex[u]], 1u) : 0u;
+  }
+  __syncthreads();
+  const int per = (m + 255) / 256, i0 = min(m, tid * per), i1 = min(m, i0 + per);
+  uint32_t sc = 0, st = 0;
+  for (int i = i0; i < i1; ++i) { sc += h[i]; st += (h[i] + kQueryTile - 1) / kQueryTile; }
+  uint32_t totc, tott;
+  uint32_t oc = block_incl_scan(sc, wtot, totc) - sc;
+  uint32_t ot = block_incl_scan(st, wtot, tott) - st;
+  uint32_t* bo = boff + (size_t)z * (m + 1);
+  int4* tz = tiles + (size_t)z * max_tiles;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t c = h[i];
+    bo[i] = oc;
+    h[m + i] = oc;
+    for (uint32_t r = 0; r < c; r += kQueryTile, ++ot)
+      tz[ot] = make_int4(i, (int)r, (int)min((uint32_t)kQueryTile, c - r), (int)(oc + r));
+    oc += c;
+  }
+  if (tid == 0) bo[m] = totc;
+  for (int t = (int)tott + tid; t < max_tiles; t += 256) tz[t] = make_int4(-1, 0, 0, 0);
+  __syncthreads();
+  int32_t* pz = perm + (size_t)z * Ns;
+#pragma unroll
+  for (int u = 0; u < PER; ++u)
+    if (ex[u] >= 0) pz[h[m + ex[u]] + rank[u]] = tid + 256 * u;
+}
+
 // Query fragments of one query row (zeros when the row is absent).
 template <typename T, int D>
 struct QFrag {
@@ -707,6 +760,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Q, c
 // Counting sort of the (query, slot) pairs by expert and the tile table.
 hipError_t launch_bucket(const Plan& p, char* ws, hipStream_t st) {
   const int Ns = p.N * p.s;
+  if (Ns <= 256 * kBucketSlicePer && (size_t)p.m * 8 <= 64 * 1024) {   // one workgroup per slice
+    hipLaunchKernelGGL(bucket_slice_kernel<kBucketSlicePer>, dim3(p.BH), dim3(256), (size_t)p.m * 8, st,
+                       (const int32_t*)(ws + p.ws.E), (uint32_t*)(ws + p.ws.boff), (int4*)(ws + p.ws.tiles),
+                       (int32_t*)(ws + p.ws.perm), Ns, p.m, p.max_tiles);
+    return hipGetLastError();
+  }
   const int nclear = (int)((p.ws.bcursor + (size_t)p.BH * p.m * 4 - p.ws.bcount) / 4);
   hipLaunchKernelGGL(clear_kernel, dim3(std::min(1024, (nclear + 255) / 256)), dim3(256), 0, st,
                      (uint32_t*)(ws + p.ws.bcount), nclear);
@@ -787,8 +846,10 @@ hipError_t launch_gather(const Plan& p, const void* Q, const void* K, const void
   return p.d == 64 ? gather_launch<float, 64>(p, Q, K, V, out, ws, st) : gather_launch<float, 128>(p, Q, K, V, out, ws, st);
 }
 
-// Route-step counter block (queued-query count) is cleared before routing.
+// Route-step counter block (queued-query count) is cleared before routing; only
+// the fast router for m > 64 queues queries.
 hipError_t launch_clear(const Plan& p, char* ws, hipStream_t st) {
+  if (!(p.s <= kRouteFastMaxS && p.m > kKeyBlock)) return hipSuccess;
   hipLaunchKernelGGL(clear_kernel, dim3(1), dim3(256), 0, st, (uint32_t*)(ws + p.ws.counters), 64);
   return hipGetLastError();
 }

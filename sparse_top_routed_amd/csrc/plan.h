@@ -16,6 +16,7 @@ constexpr int kQueryTile = 64;        // queries per workgroup in the router, ga
 constexpr int kTopkMaxGroups = 4096;  // group maxima per score row that the threshold kernel ranks
 constexpr int kTopkMaxCap = 4096;     // candidates per row the select kernel holds (larger k: exact fallback)
 constexpr int kTopkGeneralWaves = 64; // waves (each with an fp64 score row of scratch) of the fallback kernel
+constexpr int kBucketSlicePer = 16;   // pairs per thread of the one-workgroup counting sort (slices of <= 4096 pairs)
 constexpr int kRouteFastMaxS = 6;     // the router keeps per-lane top lists up to this s
 
 // Workspace offsets (bytes) of every intermediate buffer.

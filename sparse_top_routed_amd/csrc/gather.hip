@@ -549,9 +549,11 @@ __device__ __forceinline__ void block_scores(const T* k0, const T* k1, const QFr
 // s = 1 with k <= 64 and m <= 64: every tile is one routed block plus the
 // slice's landmark block, so the softmax over the m + k keys is taken in one
 // pass (no running rescale). Same persistent walk as gather_kernel; the routed
-// blocks are double-buffered in LDS, so each tile needs one barrier. Rows of
-// tile t + 2, expert indices of tile t + 3, query rows of tile t + 1 and query
-// ids of tile t + 2 are in flight while tile t computes.
+// blocks are double-buffered in LDS, so each tile needs one barrier. While tile
+// t computes, the rows of tiles t + 2 and t + 3 (two register sets), the expert
+// indices of tile t + 4, the query rows of tiles t + 1 and t + 2 and the query
+// ids of tile t + 3 are in flight: three workgroups' LDS would not fit in a CU,
+// so the two resident ones hide the gathers' latency with depth instead.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void gather1_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                       const T* __restrict__ V, const int32_t* __restrict__ I,
@@ -613,40 +615,47 @@ __global__ __launch_bounds__(256) void gather1_kernel(const T* __restrict__ Q, c
       if constexpr (BF) R.v.store((uint16_t*)sm.rv[b], tid); else R.v.store(sm.rv[b], TL::VSTR, tid);
     };
 
-    // prologue: tile 0's rows straight to buffer 0, tile 1's rows in registers,
-    // tile 2's indices in flight
+    // prologue: tile 0's rows straight to buffer 0, tile 1's rows in RA, tile
+    // 2's in RB, tile 3's indices in flight; query rows of tiles 0 and 1
     RowIdx<T, D> ix;
-    KVRegs<T, D, 1> RR;
+    KVRegs<T, D, 1> RA, RB;
     {
       const T *Kb, *Vb;
       ix.load(expert(0), k, 0, tid);
       slice_kv(0, Kb, Vb);
-      load_rows<T, D>(RR, ix, Kb, Vb, tid);
+      load_rows<T, D>(RA, ix, Kb, Vb, tid);
       ix.load(expert(1), k, 0, tid);
-      store_rows(RR, 0);
+      store_rows(RA, 0);
       slice_kv(1, Kb, Vb);
-      load_rows<T, D>(RR, ix, Kb, Vb, tid);
+      load_rows<T, D>(RA, ix, Kb, Vb, tid);
       ix.load(expert(2), k, 0, tid);
+      slice_kv(2, Kb, Vb);
+      load_rows<T, D>(RB, ix, Kb, Vb, tid);
+      ix.load(expert(3), k, 0, tid);
     }
-    int q = qid(0), q_n = qid(1), q_nn = q_n;
-    QFrag<T, D> qf;
+    int q = qid(0), q_n = qid(1), q_nn = qid(2), q_n3 = q_nn;
+    QFrag<T, D> qf, qf_n;
     qf.load(Q + ((size_t)sm.tz[0] * N + q) * D, g);
-    QFrag<T, D> qf_n = qf;
+    qf_n.load(Q + ((size_t)sm.tz[min(1, last)] * N + q_n) * D, g);
+    QFrag<T, D> qf_nn = qf_n;
     int zl = -1;   // slice in the landmark buffer
 
-    // one barrier per tile: at iteration t the rows of tile t + 1 go to the other
-    // buffer, whose last readers (tile t - 1) finished before the barrier
-    for (int t = 0; t < (int)nt; ++t) {
+    // one barrier per tile: at iteration t the rows of tile t + 1 (in Rc) go to
+    // the other buffer, whose last readers (tile t - 1) finished before the
+    // barrier; Rc then takes the rows of tile t + 3, while Rn holds tile t + 2's
+    auto tile_step = [&](int t, KVRegs<T, D, 1>& Rc) {
       const int4 cur = sm.tile[t];
       const int zc = sm.tz[t];
       if (t > 0) {
         q = q_n;
         q_n = q_nn;
+        q_nn = q_n3;
         qf = qf_n;
+        qf_n = qf_nn;
       }
-      q_nn = qid(t + 2);
+      q_n3 = qid(t + 3);
       __syncthreads();
-      store_rows(RR, (t + 1) & 1);
+      store_rows(Rc, (t + 1) & 1);
       if (zc != zl) {   // a new slice: its landmark block (uniform branch)
         KVRegs<T, D, KP> LR;
         load_landmarks<T, D>(LR, qtop, vtop, zc, m, 0, tid);
@@ -654,12 +663,12 @@ __global__ __launch_bounds__(256) void gather1_kernel(const T* __restrict__ Q, c
         zl = zc;
         __syncthreads();
       }
-      {   // rows of tile t + 2 (indices in hand), indices of tile t + 3, query rows of tile t + 1
+      {   // rows of tile t + 3 (indices in hand), indices of tile t + 4, query rows of tile t + 2
         const T *Kb, *Vb;
-        slice_kv(t + 2, Kb, Vb);
-        load_rows<T, D>(RR, ix, Kb, Vb, tid);
-        ix.load(expert(t + 3), k, 0, tid);
-        qf_n.load(Q + ((size_t)sm.tz[min(t + 1, last)] * N + q_n) * D, g);
+        slice_kv(t + 3, Kb, Vb);
+        load_rows<T, D>(Rc, ix, Kb, Vb, tid);
+        ix.load(expert(t + 4), k, 0, tid);
+        qf_nn.load(Q + ((size_t)sm.tz[min(t + 2, last)] * N + q_nn) * D, g);
       }
       if (16 * w < cur.z) {   // wave has live rows (uniform)
         const int b = t & 1;
@@ -699,6 +708,10 @@ __global__ __launch_bounds__(256) void gather1_kernel(const T* __restrict__ Q, c
             store4<T>(orow + 16 * dt + 4 * g, o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
         }
       }
+    };
+    for (int t = 0; t < (int)nt; t += 2) {   // two steps per trip: the register sets swap roles
+      tile_step(t, RA);
+      if (t + 1 < (int)nt) tile_step(t + 1, RB);
     }
     __syncthreads();   // the tile list is rewritten by the next batch
   }

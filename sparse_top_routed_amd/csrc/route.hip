@@ -342,10 +342,12 @@ __global__ __launch_bounds__(256) void route_fast_kernel(const T* __restrict__ Q
 // Fast router for m > 64: a workgroup takes TPW query tiles at once (their query
 // fragments and top lists stay in registers) and streams the landmark blocks
 // through LDS once for all of them, so each block is staged once per TPW tiles.
+// Held to three waves per SIMD: the gathers of Q rows need the occupancy more
+// than the few registers that spill.
 // A query is certain, or its band is re-scored in fp64 when the list holds it,
 // or it is queued for the exact kernel.
 template <typename T, int D, int TM, int TPW>
-__global__ __launch_bounds__(256) void route_multi_kernel(const T* __restrict__ Q, const void* __restrict__ qtop,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void route_multi_kernel(const T* __restrict__ Q, const void* __restrict__ qtop,
                                                           const double* __restrict__ qt64,
                                                           const float* __restrict__ qtnorm, int32_t* __restrict__ E,
                                                           uint32_t* __restrict__ counters,
@@ -395,13 +397,42 @@ __global__ __launch_bounds__(256) void route_multi_kernel(const T* __restrict__ 
     if constexpr (BF)
       stage_rows<T, D>(Ks1, TL::KSTR, [&](int rr) { return plane1 + (size_t)(lb0 + rr) * D; }, nvalid, tid);
     __syncthreads();
+    // scores of all TPW tiles at once: each landmark fragment read from LDS
+    // serves every tile right away (nothing to keep live across tiles)
+    f32x4 acct[TPW][4];
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) acct[tt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (BF) {
+      constexpr int KSTR = TL::KSTR;
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const int off = (16 * kt + r) * KSTR + 32 * ks + 8 * g;
+          const uint4 a0 = *(const uint4*)((const uint16_t*)Ks0 + off);
+          const uint4 a1 = *(const uint4*)((const uint16_t*)Ks1 + off);
+#pragma unroll
+          for (int tt = 0; tt < TPW; ++tt) {
+            acct[tt][kt] = mma_bf16(a0, qb[tt][0][ks], acct[tt][kt]);
+            acct[tt][kt] = mma_bf16(a1, qb[tt][0][ks], acct[tt][kt]);
+          }
+        }
+    } else {
+      constexpr int KSTR = TL::KSTR;
+#pragma unroll
+      for (int ks = 0; ks < D / 4; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const float a = ((const float*)Ks0)[(16 * kt + r) * KSTR + 4 * ks + g];
+#pragma unroll
+          for (int tt = 0; tt < TPW; ++tt) acct[tt][kt] = mma_f32(a, qf[tt][ks], acct[tt][kt]);
+        }
+    }
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
-      f32x4 acc[4];
-      if constexpr (BF)
-        qk_bf16<D, 2, 1>((const uint16_t*)Ks0, (const uint16_t*)Ks1, qb[tt], acc, lane);
-      else
-        qk_f32<D>((const float*)Ks0, qf[tt], acc, lane);
+      const f32x4 (&acc)[4] = acct[tt];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll

@@ -570,7 +570,7 @@ __global__ __launch_bounds__(256) void route_exact_kernel(const T* __restrict__ 
 template <typename T, int D, int TM, bool RES>
 static hipError_t route_fast_launch(const Plan& p, const void* Q, char* ws, hipStream_t st) {
   if constexpr (RES) {
-    const int tpw = 4;   // several query tiles per workgroup: the landmarks stay staged
+    const int tpw = 8;   // several query tiles per workgroup: the landmarks stay staged
     hipLaunchKernelGGL((route_fast_kernel<T, D, TM>), dim3((p.qtiles + tpw - 1) / tpw, p.BH), dim3(256), 0,
                        st, (const T*)Q, (const void*)(ws + p.ws.qtop), (const double*)(ws + p.ws.qt64),
                        (const float*)(ws + p.ws.qtnorm), (int32_t*)(ws + p.ws.E), (uint32_t*)(ws + p.ws.counters),

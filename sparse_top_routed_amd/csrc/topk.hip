@@ -168,25 +168,44 @@ __global__ __launch_bounds__(256) void merge_thresh_kernel(const float* __restri
   const int tid = threadIdx.x, lane = tid & 63, row = blockIdx.x * 4 + (tid >> 6);
   if (row >= rows) return;   // wave-uniform
   const int z = row / m;
+  // every independent load first: the group maxima, the error-bound inputs and
+  // the first chunks' partials [max, sum, pad, pad, acc[D]]
   uint32_t v[PV];
   load_group_keys<PV>(bmax + (size_t)row * nbg, nbg, lane, v);
-
-  // partials [max, sum, pad, pad, acc[D]] per chunk
+  float kmx = 0.f;
+  for (int c = lane; c < nsplit; c += 64) kmx = fmaxf(kmx, kmax[(size_t)z * nsplit + c]);
+  const float qn = qtnorm[row];
   const float* Pr = lpart + (size_t)row * nsplit * (D + 4);
+  constexpr int CB = 8;   // chunks in flight
+  float2 ml[CB];
+  float a[CB][CW];
+  auto fetch = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const float* Pc = Pr + (size_t)min(c0 + u, nsplit - 1) * (D + 4);
+      ml[u] = *(const float2*)Pc;
+#pragma unroll
+      for (int e = 0; e < CW; ++e) a[u][e] = Pc[4 + lane + 64 * e];
+    }
+  };
+  fetch(0);
   float M = -INFINITY;
   for (int c = lane; c < nsplit; c += 64) M = fmaxf(M, Pr[(size_t)c * (D + 4)]);
   M = wave_max(M);
   float L = 0.f, acc[CW];
 #pragma unroll
   for (int e = 0; e < CW; ++e) acc[e] = 0.f;
-#pragma unroll 2
-  for (int c = 0; c < nsplit; ++c) {
-    const float* Pc = Pr + (size_t)c * (D + 4);
-    const float2 ml = *(const float2*)Pc;
-    const float f = __builtin_amdgcn_exp2f(ml.x - M);
-    L = fmaf(f, ml.y, L);
+  for (int c0 = 0; c0 < nsplit; c0 += CB) {
+    if (c0 > 0) fetch(c0);
 #pragma unroll
-    for (int e = 0; e < CW; ++e) acc[e] = fmaf(f, Pc[4 + lane + 64 * e], acc[e]);
+    for (int u = 0; u < CB; ++u) {
+      if (c0 + u < nsplit) {
+        const float f = __builtin_amdgcn_exp2f(ml[u].x - M);
+        L = fmaf(f, ml[u].y, L);
+#pragma unroll
+        for (int e = 0; e < CW; ++e) acc[e] = fmaf(f, a[u][e], acc[e]);
+      }
+    }
   }
   const float inv = 1.f / L;
 #pragma unroll
@@ -196,7 +215,7 @@ __global__ __launch_bounds__(256) void merge_thresh_kernel(const float* __restri
     vt16[(size_t)row * D + lane + 64 * e] = f32_to_bf16(x);
   }
 
-  const double E = row_bound(qtnorm, kmax, nsplit, row, z, gamma, lane);
+  const double E = gamma * (double)qn * (double)wave_max(kmx);
   const uint32_t key = thresh_key<PV>(v, nbg, k, E);
   if (lane == 0) thr[row] = key;
 }

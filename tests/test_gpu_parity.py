@@ -36,6 +36,8 @@ SMALL = [
     small("chunked_f32", B=1, H=2, N=5000, grid_w=5000, pool_w=20, k=80, s=2),
     small("tiles_2d_bf16", B=1, H=2, N=64 * 64, grid_h=64, grid_w=64, pool_h=10, pool_w=10, k=64, s=2,
           dtype="bf16"),
+    # s = 1 with k > 64 and d = 128: the general kernel with the landmark part fused
+    small("fused_bf16_d128", B=1, H=2, N=3000, d=128, grid_w=3000, pool_w=30, k=100, s=1, dtype="bf16"),
 ]
 
 

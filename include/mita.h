@@ -96,7 +96,8 @@ mita_status mita_pool(const void* Q, int m, int k, int s, const mita_shape* shap
 
 /* Step 2 (shared expert). Vt_out: fp32 [B, H, m, d], the shared expert V~
  * (copied from the workspace). The m x N score rows q~_i . K_n are not kept; the
- * step leaves maxima of groups of them for step 3. S_out, when not NULL, is a
+ * step leaves maxima of groups of them and, derived from those, each row's
+ * candidate threshold for step 3. S_out, when not NULL, is a
  * device buffer (fp32 [B, H, m, N], 16-byte aligned) that the kernel fills with
  * the unscaled scores as computed on the GPU (fp32 accumulation), for checking. */
 mita_status mita_landmark(const void* K, const void* V, int m, int k, int s, const mita_shape* shape,
@@ -113,9 +114,9 @@ mita_status mita_topk(const void* K, int m, int k, int s, const mita_shape* shap
                       size_t workspace_bytes, int32_t* I_out, void* stream);
 
 /* Step 4 (routing). E_out: int32 [B, H, N, s], the routed landmarks of each
- * query, ordered by decreasing score. The set is exact in the same sense as
- * step 3; the order among the s entries follows the fp32 scores. Also groups
- * the (query, expert) pairs by expert (a counting sort) for step 5. */
+ * query. The set is exact in the same sense as step 3; the order among a
+ * query's s entries is not specified (it does not change the output). Also
+ * groups the (query, expert) pairs by expert (a counting sort) for step 5. */
 mita_status mita_route(const void* Q, int m, int k, int s, const mita_shape* shape, void* workspace,
                        size_t workspace_bytes, int32_t* E_out, void* stream);
 

@@ -38,6 +38,16 @@ SMALL = [
           dtype="bf16"),
     # s = 1 with k > 64 and d = 128: the general kernel with the landmark part fused
     small("fused_bf16_d128", B=1, H=2, N=3000, d=128, grid_w=3000, pool_w=30, k=100, s=1, dtype="bf16"),
+    # m > 64 with s = 1: router lists of order keys carrying the landmark id, and the
+    # general kernel streaming the landmark blocks (not resident)
+    small("landmarks100_s1", B=1, H=2, N=5000, grid_w=5000, pool_w=100, k=64, s=1, dtype="bf16"),
+    # fp32 with m > 64 (the router's fp32 MFMA path with key lists)
+    small("f32_m80", B=1, H=2, N=4000, grid_w=4000, pool_w=80, k=50, s=2),
+    # k > 1024: no candidate pass, every row selected from fp64 scores of the whole row
+    small("k1100_fallback", B=1, H=1, N=3000, grid_w=3000, pool_w=8, k=1100, s=1, dtype="bf16"),
+    # more than 4096 group maxima per row (groups of 16 since k > N / 256): no candidate
+    # threshold, so every row overflows its lists and goes to the fp64 fallback
+    small("no_threshold", B=1, H=1, N=70000, grid_w=70000, pool_w=8, k=300, s=1, dtype="bf16"),
 ]
 
 

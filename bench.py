@@ -30,7 +30,7 @@ def step_bytes(w) -> dict:
     BH, N, d, m, k, s = w.slices, w.N, w.d, w.m, w.k, w.s
     tok = BH * N * d * e
     nblk = -(-N // 64)
-    nbg = nblk * (1 if nblk >= 4 * k else 4)   # group maxima per score row (groups of 64 or 16 scores)
+    nbg = nblk * (1 if nblk >= 4 * k else (4 if 4 * nblk >= k else 16))   # group maxima per row (64, 16 or 4 scores)
     return {
         "pool": tok + BH * m * d * (8 + 4 + 4),
         # K and V read once, group maxima of the score rows written once
@@ -113,6 +113,35 @@ def cpu_baseline(w, Q, K, V, budget_s: float = 12.0) -> dict:
                       f"fp64 numpy, BLAS limited to 1 thread, {el:.1f} s"}
 
 
+def sweep(w, Qd, Kd, Vd, steps: int, warmup: int) -> int:
+    """Forward throughput for each (m, k, s) setting of synth.SWEEP on the same
+    inputs; per-setting parity is covered by the GPU tests."""
+    import torch
+
+    import synth
+    from sparse_top_routed_amd import mita
+
+    st = torch.cuda.current_stream()
+    for v in synth.sweep_workloads(w.name):
+        call = mita.Mita.create(Qd, v.m, v.k, v.s, grid=(v.grid_h, v.grid_w), pool=(v.pool_h, v.pool_w))
+        out = torch.empty_like(Qd)
+        for _ in range(warmup):
+            call.forward(Qd, Kd, Vd, out)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(st)
+        for _ in range(steps):
+            call.forward(Qd, Kd, Vd, out)
+        t1.record(st)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        print(json.dumps({"workload": v.name, "m": v.m, "k": v.k, "s": v.s, "ms_per_step": ms,
+                          "value": v.slices * v.N / (ms * 1e-3), "unit": "query-tokens/s",
+                          "keys_per_query": v.m + v.k * v.s}), flush=True)
+        del call, out
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,6 +154,9 @@ def main() -> int:
                     help="also run 3 elementwise copies of 512 MiB (read and write 2^29 bytes each), the "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
     ap.add_argument("--print-sha", action="store_true", help="print the dominant kernels' source hashes and exit")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the forward pass over the inference-time (m, k, s) settings of synth.SWEEP on the "
+                         "workload's inputs (one JSON line per setting) instead of the benchmark line")
     a = ap.parse_args()
     if a.print_sha:
         for step in KERNEL_SOURCES:
@@ -150,6 +182,8 @@ def main() -> int:
         return torch.from_numpy(x).cuda()
 
     Qd, Kd, Vd = dev(Q), dev(K), dev(V)
+    if a.sweep:
+        return sweep(w, Qd, Kd, Vd, a.steps, a.warmup)
     call = mita.Mita.create(Qd, w.m, w.k, w.s, grid=(w.grid_h, w.grid_w), pool=(w.pool_h, w.pool_w))
     out = torch.empty_like(Qd)
     for _ in range(a.warmup):

@@ -63,9 +63,15 @@ mita_status make_plan(const mita_shape* shape, int m, int k, int s, Plan* p, con
   // Top-k select: group maxima of the scores give each row a candidate threshold.
   {
     const int64_t nblk = (sh.N + kKeyBlock - 1) / kKeyBlock;
-    P.gq = nblk >= 4 * (int64_t)k ? 64 : 16;
+    // groups as large as leave at least k of them (4 k for groups of 64, so the
+    // threshold is close), but no smaller than 4 scores
+    P.gq = nblk >= 4 * (int64_t)k ? 64 : (4 * nblk >= k ? 16 : 4);
     P.nbg = (int)(nblk * (kKeyBlock / P.gq));
-    int64_t cap = std::max<int64_t>(256, 4 * (int64_t)k);
+    // With a threshold the candidates are about k per row (room for 4k); a row
+    // with fewer group maxima than k (or more than the threshold search takes)
+    // has none, so all its N scores are candidates
+    const bool thresholded = P.nbg >= k && P.nbg <= kTopkMaxGroups;
+    int64_t cap = thresholded ? std::max<int64_t>(256, 4 * (int64_t)k) : std::max<int64_t>(256, sh.N);
     cap = (cap + 63) / 64 * 64;
     int64_t pw = 256;
     while (pw < cap) pw *= 2;   // the select kernel is instantiated for powers of two
@@ -101,7 +107,10 @@ mita_status make_plan(const mita_shape* shape, int m, int k, int s, Plan* p, con
   L.cand = take(bh * m * P.nsplit * (size_t)P.capc * 8);
   L.ccnt = take(bh * m * P.nsplit * 4);
   L.glist = take((bh * m + 1) * 4);
-  L.gscr = take((size_t)kTopkGeneralWaves * N * 8);
+  // fallback rows: one fp64 score row of scratch per wave, ~64 MiB in all
+  P.gwaves = (int)std::min<int64_t>(kTopkGeneralWavesMax,
+                                    std::max<int64_t>(kTopkGeneralWaves, ((int64_t)64 << 20) / ((int64_t)N * 8)));
+  L.gscr = take((size_t)P.gwaves * N * 8);
   L.I = take(bh * m * (size_t)k * 4);
   L.E = take(bh * N * s * 4);
   // counters: everything from here to `perm` is cleared before routing

@@ -15,7 +15,8 @@ constexpr int kKeyBlock = 64;         // keys per LDS block in the attention ker
 constexpr int kQueryTile = 64;        // queries per workgroup in the router, gather and combine kernels
 constexpr int kTopkMaxGroups = 4096;  // group maxima per score row that the threshold kernel ranks
 constexpr int kTopkMaxCap = 4096;     // candidates per row the select kernel holds (larger k: exact fallback)
-constexpr int kTopkGeneralWaves = 64; // waves (each with an fp64 score row of scratch) of the fallback kernel
+constexpr int kTopkGeneralWaves = 64; // fewest waves (each with an fp64 score row of scratch) of the fallback kernel
+constexpr int kTopkGeneralWavesMax = 4096;
 constexpr int kBucketSlicePer = 16;   // pairs per thread of the one-workgroup counting sort (slices of <= 4096 pairs)
 constexpr int kRouteFastMaxS = 6;     // the router keeps per-lane top lists up to this s
 
@@ -28,12 +29,12 @@ struct Layout {
   size_t kmax;      // f32 [BH, nsplit]   upper bound of max_n |K_n|_2 per key chunk
   size_t vt32;      // f32 [BH, m, d]     shared expert V~
   size_t vt16;      // bf16 [BH, m, d]    V~ rounded to bf16 (MFMA operand)
-  size_t bmax;      // f32 [BH * m, nbg]  maxima of groups of approximate scores q~_i . K_n
+  size_t bmax;      // f32 [BH * m, nbg]  maxima of groups of 4, 16 or 64 approximate scores q~_i . K_n
   size_t thr;       // u32 [BH * m]       order key of the candidate threshold of each score row
   size_t cand;      // u32x2 [BH * m, nsplit, capc] candidates (order key, token id) per key chunk
   size_t ccnt;      // u32 [BH * m, nsplit] candidates per chunk (capc + 1: overflow)
   size_t glist;     // u32 [BH * m + 1]   rows for the exact fallback, count first
-  size_t gscr;      // f64 [kTopkGeneralWaves, N] fp64 score rows of the fallback
+  size_t gscr;      // f64 [gwaves, N] fp64 score rows of the fallback
   size_t I;         // i32 [BH, m, k]     expert token sets, ascending
   size_t E;         // i32 [BH, N, s]     routed experts per query
   size_t counters;  // u32 block cleared at the start of routing (below)
@@ -60,9 +61,10 @@ struct Plan {
   int lchunk;       // keys per workgroup (multiple of kKeyBlock)
   int nsplit;       // ceil(N / lchunk)
   // top-k select
-  int gq;           // scores per group maximum: 16 (one lane's share of a key block) or 64 (a whole block)
+  int gq;           // scores per group maximum: 4 (a lane's share of one 16-key tile), 16 (its share of a key block) or 64 (a block)
   int nbg;          // group maxima per row: ceil(N / 64) * 64 / gq
   int cap;          // candidates per row the select kernel holds (multiple of 64, or 0: fallback for all rows)
+  int gwaves;       // waves of the fallback kernel (64 .. 4096, ~64 MiB of score rows)
   int capc;         // candidate slots per (row, key chunk): min(lchunk, cap)
   // router and output
   int qtiles;       // ceil(N / kQueryTile)

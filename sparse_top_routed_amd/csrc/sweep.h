@@ -58,8 +58,9 @@ struct LmState {
 };
 
 // Shared-expert sweep over keys [k0, k1) (k1 > k0): online softmax of the
-// scores against V, the maxima of groups of gq (16: one lane's share of a
-// block; 64: a block) scores into Brow[group] (the global group index), the
+// scores against V, the maxima of groups of gq (4: a lane's share of one 16-key
+// tile; 16: its share of a block; 64: a block) scores into Brow[group] (the
+// global group index), the
 // scores into Srow when it is not null, and, when `norms`, the largest squared
 // key norm seen into kmx (per thread; reduce over the workgroup).
 template <typename T, int D>
@@ -106,15 +107,23 @@ __device__ __forceinline__ void shared_expert_sweep(const T* Kz, const T* Vz, in
     f32x4 acc[4];
     qfr.scores(Ks, acc, lane);
 
-    {   // group maxima for the top-k threshold: one lane's 16 scores, or the block's 64
-      float gm = -INFINITY;
+    {   // group maxima for the top-k threshold: one lane's 4 scores of one kt (gq = 4),
+        // its 16 scores (gq = 16), or the block's 64
+      float gk[4];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < 4; ++kt) {
+        gk[kt] = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) gm = fmaxf(gm, kb + 16 * kt + 4 * g + j < k1 ? acc[kt][j] : -INFINITY);
-      if (gq == 64) gm = quad_max(gm);
+        for (int j = 0; j < 4; ++j) gk[kt] = fmaxf(gk[kt], kb + 16 * kt + 4 * g + j < k1 ? acc[kt][j] : -INFINITY);
+      }
       const int blk = kb / kKeyBlock;
-      if (lm_ok && (gq == 16 || g == 0)) Brow[gq == 16 ? 4 * blk + g : blk] = gm;
+      if (gq == 4) {
+        if (lm_ok) *(float4*)(Brow + 16 * blk + 4 * g) = make_float4(gk[0], gk[1], gk[2], gk[3]);
+      } else {
+        float gm = fmaxf(fmaxf(gk[0], gk[1]), fmaxf(gk[2], gk[3]));
+        if (gq == 64) gm = quad_max(gm);
+        if (lm_ok && (gq == 16 || g == 0)) Brow[gq == 16 ? 4 * blk + g : blk] = gm;
+      }
     }
     if (Srow && lm_ok) {   // the scores themselves only when asked for
 #pragma unroll

@@ -534,7 +534,7 @@ static hipError_t topk_launch(const Plan& p, const void* K, char* ws, hipStream_
     hipLaunchKernelGGL(topk_all_rows_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, glist, rows);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((topk_general_kernel<T, D>), dim3(kTopkGeneralWaves), dim3(64), 0, st,
+  hipLaunchKernelGGL((topk_general_kernel<T, D>), dim3(p.gwaves), dim3(64), 0, st,
                      (const double*)(ws + p.ws.qt64), (const T*)K, (int32_t*)(ws + p.ws.I), (const uint32_t*)glist,
                      (double*)(ws + p.ws.gscr), p.N, p.m, p.k);
   return hipGetLastError();

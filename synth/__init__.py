@@ -69,6 +69,31 @@ WORKLOADS: Dict[str, Workload] = {
 }
 
 
+# Inference-time settings of (m, k, s) on the ViT-B-like inputs: the pages note
+# that a model can be run with more landmarks or larger experts than it was
+# trained with. m comes from the pooling grid of the 56 x 56 tokens (4x4, 7x7,
+# 8x8, 14x14); every other field stays that of "vit_b".
+SWEEP: Tuple[Tuple[int, int, int, int], ...] = (
+    # (pool_h, pool_w, k, s)
+    (4, 4, 64, 1),
+    (7, 7, 64, 1),
+    (8, 8, 32, 1),
+    (8, 8, 64, 1),
+    (8, 8, 128, 1),
+    (8, 8, 256, 1),
+    (8, 8, 64, 2),
+    (8, 8, 64, 4),
+    (14, 14, 64, 1),
+    (14, 14, 128, 2),
+)
+
+
+def sweep_workloads(base: str = "vit_b") -> Sequence[Workload]:
+    """The SWEEP settings applied to a base workload."""
+    w = WORKLOADS[base]
+    return [w.with_(name=f"{base}_m{ph * pw}_k{k}_s{s}", pool_h=ph, pool_w=pw, k=k, s=s) for ph, pw, k, s in SWEEP]
+
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16 (round to nearest, ties to even); return uint16 bits."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)

@@ -43,12 +43,30 @@ SMALL = [
     small("landmarks100_s1", B=1, H=2, N=5000, grid_w=5000, pool_w=100, k=64, s=1, dtype="bf16"),
     # fp32 with m > 64 (the router's fp32 MFMA path with key lists)
     small("f32_m80", B=1, H=2, N=4000, grid_w=4000, pool_w=80, k=50, s=2),
-    # k > 1024: no candidate pass, every row selected from fp64 scores of the whole row
-    small("k1100_fallback", B=1, H=1, N=3000, grid_w=3000, pool_w=8, k=1100, s=1, dtype="bf16"),
+    # fewer group maxima per row than k: no threshold, all N scores are candidates of
+    # the select kernel (N <= 4096) ...
+    small("k1100_all_candidates", B=1, H=1, N=3000, grid_w=3000, pool_w=8, k=1100, s=1, dtype="bf16"),
+    # ... or, past its capacity, every row is selected from fp64 scores of the whole row
+    small("k1100_fallback", B=1, H=2, N=5000, grid_w=5000, pool_w=8, k=1100, s=1, dtype="bf16"),
     # more than 4096 group maxima per row (groups of 16 since k > N / 256): no candidate
     # threshold, so every row overflows its lists and goes to the fp64 fallback
     small("no_threshold", B=1, H=1, N=70000, grid_w=70000, pool_w=8, k=300, s=1, dtype="bf16"),
 ]
+
+
+# The inference-time (m, k, s) settings that bench.py --sweep times, on two
+# slices of the ViT-B-like inputs.
+SWEEP = [w.with_(B=1, H=2) for w in synth.sweep_workloads("vit_b")]
+
+
+@pytest.mark.parametrize("w", SWEEP, ids=lambda w: w.name)
+def test_sweep_settings(w, lib):
+    say(f"[sweep] {w.name}")
+    Q, K, V = synth.make_inputs(w)
+    gpu = run_gpu_steps(w, Q, K, V, lib, want_s=False)
+    for z in range(w.slices):
+        st = check_slice(w, Q, K, V, gpu, z, check_s=False)
+        say(f"  slice {z}: {st}")
 
 
 @pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)

@@ -113,7 +113,29 @@ def cpu_baseline(w, Q, K, V, budget_s: float = 12.0) -> dict:
                       f"fp64 numpy, BLAS limited to 1 thread, {el:.1f} s"}
 
 
-def sweep(w, Qd, Kd, Vd, steps: int, warmup: int) -> int:
+def step_times(call, Qd, Kd, Vd, out, steps: int) -> dict:
+    """Mean time (ms) of each step entry point, the launches of one forward run one
+    step at a time, bracketed by events on the stream the kernels run on."""
+    import torch
+
+    st = torch.cuda.current_stream()
+    names = ["pool", "landmark", "topk", "route", "gather"]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    acc = dict.fromkeys(names, 0.0)
+    for _ in range(steps):
+        ev[0].record(st)
+        call.pool(Qd); ev[1].record(st)
+        call.landmark(Kd, Vd); ev[2].record(st)
+        call.topk(Kd); ev[3].record(st)
+        call.route(Qd); ev[4].record(st)
+        call.gather(Qd, Kd, Vd, out); ev[5].record(st)
+        torch.cuda.synchronize()
+        for i, n in enumerate(names):
+            acc[n] += ev[i].elapsed_time(ev[i + 1])
+    return {n: acc[n] / steps for n in names}
+
+
+def sweep(w, Qd, Kd, Vd, steps: int, warmup: int, breakdown: bool) -> int:
     """Forward throughput for each (m, k, s) setting of synth.SWEEP on the same
     inputs; per-setting parity is covered by the GPU tests."""
     import torch
@@ -135,9 +157,11 @@ def sweep(w, Qd, Kd, Vd, steps: int, warmup: int) -> int:
         t1.record(st)
         torch.cuda.synchronize()
         ms = t0.elapsed_time(t1) / steps
-        print(json.dumps({"workload": v.name, "m": v.m, "k": v.k, "s": v.s, "ms_per_step": ms,
-                          "value": v.slices * v.N / (ms * 1e-3), "unit": "query-tokens/s",
-                          "keys_per_query": v.m + v.k * v.s}), flush=True)
+        res = {"workload": v.name, "m": v.m, "k": v.k, "s": v.s, "ms_per_step": ms,
+               "value": v.slices * v.N / (ms * 1e-3), "unit": "query-tokens/s", "keys_per_query": v.m + v.k * v.s}
+        if breakdown:
+            res["step_ms"] = step_times(call, Qd, Kd, Vd, out, steps)
+        print(json.dumps(res), flush=True)
         del call, out
     return 0
 
@@ -183,7 +207,7 @@ def main() -> int:
 
     Qd, Kd, Vd = dev(Q), dev(K), dev(V)
     if a.sweep:
-        return sweep(w, Qd, Kd, Vd, a.steps, a.warmup)
+        return sweep(w, Qd, Kd, Vd, a.steps, a.warmup, a.breakdown)
     call = mita.Mita.create(Qd, w.m, w.k, w.s, grid=(w.grid_h, w.grid_w), pool=(w.pool_h, w.pool_w))
     out = torch.empty_like(Qd)
     for _ in range(a.warmup):
@@ -203,22 +227,9 @@ def main() -> int:
     ms = t0.elapsed_time(t1) / a.steps
     tokens = w.slices * w.N
 
-    # per-step times: the same launches as forward, one step entry point at a time,
-    # bracketed by events on the stream the kernels run on
+    # per-step times: the same launches as forward, one step entry point at a time
     names = ["pool", "landmark", "topk", "route", "gather"]
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-    acc = dict.fromkeys(names, 0.0)
-    for _ in range(a.steps):
-        ev[0].record(st)
-        call.pool(Qd); ev[1].record(st)
-        call.landmark(Kd, Vd); ev[2].record(st)
-        call.topk(Kd); ev[3].record(st)
-        call.route(Qd); ev[4].record(st)
-        call.gather(Qd, Kd, Vd, out); ev[5].record(st)
-        torch.cuda.synchronize()
-        for i, n in enumerate(names):
-            acc[n] += ev[i].elapsed_time(ev[i + 1])
-    per = {n: acc[n] / a.steps for n in names}
+    per = step_times(call, Qd, Kd, Vd, out, a.steps)
     nbytes = step_bytes(w)
     dom = max(per, key=per.get)
     kname = KERNEL_NAMES[dom]

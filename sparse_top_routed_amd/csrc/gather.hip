@@ -228,7 +228,8 @@ __device__ __forceinline__ void load_routed(KVRegs<T, D, 1>& R, const T* Kz, con
 }
 
 // Attention over the m landmark pairs (keys Q~, values V~), block 0 already in
-// registers (R). Block-uniform call; ends with the LDS tiles free again.
+// registers (R). The next block is fetched into R while the current one
+// computes. Block-uniform call; ends with the LDS tiles free again.
 template <typename T, int D>
 __device__ __forceinline__ void attend_landmarks(AttnLds<T, D>& sm, KVRegs<T, D, sizeof(T) == 2 ? 2 : 1>& R,
                                                  const QFrag<T, D>& qf, const void* qtop, const void* vtop, int z,
@@ -237,9 +238,9 @@ __device__ __forceinline__ void attend_landmarks(AttnLds<T, D>& sm, KVRegs<T, D,
   constexpr int KP = sizeof(T) == 2 ? 2 : 1;
   const int lane = tid & 63;
   for (int lb0 = 0; lb0 < m; lb0 += kKeyBlock) {
-    if (lb0 > 0) load_landmarks<T, D>(R, qtop, vtop, z, m, lb0, tid);
     R.store(sm, tid);
     __syncthreads();
+    if (lb0 + kKeyBlock < m) load_landmarks<T, D>(R, qtop, vtop, z, m, lb0 + kKeyBlock, tid);   // block-uniform
     attend_block<T, D, KP>(sm, qf, min(kKeyBlock, m - lb0), sl2e, mrun, lrun, o, lane, wave_live);
     __syncthreads();
   }

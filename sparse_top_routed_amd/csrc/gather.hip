@@ -719,6 +719,9 @@ __global__ __launch_bounds__(256) void gather1_kernel(const T* __restrict__ Q, c
 }
 
 // s > 1: landmark part for 64 consecutive queries, merged with their s partials.
+// The partial softmaxes seed the online-softmax state (reference max, sum and
+// unnormalised output), so their loads overlap those of the query rows and the
+// first landmark block; the landmark blocks then continue the same softmax.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Q, const void* __restrict__ qtop,
                                                       const void* __restrict__ vtop, const float* __restrict__ pacc,
@@ -728,32 +731,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Q, c
   const int z = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
   const int q = blockIdx.x * kQueryTile + 16 * w + r;
   const bool ok = q < N;
+  const int qc = ok ? q : N - 1;
   QFrag<T, D> qf;
-  qf.load(Q + ((size_t)z * N + (ok ? q : N - 1)) * D, g);
-  float mrun = -INFINITY, lrun = 0.f;
+  qf.load(Q + ((size_t)z * N + qc) * D, g);
+  KVRegs<T, D, sizeof(T) == 2 ? 2 : 1> LR;
+  load_landmarks<T, D>(LR, qtop, vtop, z, m, 0, tid);
+  // seed: M = the largest partial reference; o, l = the partials rescaled to it
+  // (l on one lane of the quad: the lanes' sums are added at the end)
+  const size_t p0 = ((size_t)z * N + qc) * s;
+  float M = -INFINITY;
+  for (int sl = 0; sl < s; ++sl) M = fmaxf(M, pml[(p0 + sl) * 2]);
+  float lrun = 0.f;
   f32x4 o[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  {
-    KVRegs<T, D, sizeof(T) == 2 ? 2 : 1> LR;
-    load_landmarks<T, D>(LR, qtop, vtop, z, m, 0, tid);
-    attend_landmarks<T, D>(sm, LR, qf, qtop, vtop, z, m, sl2e, mrun, lrun, o, tid);
-  }
-  const float l = quad_sum(lrun);
-  if (!ok) return;
-  const size_t p0 = ((size_t)z * N + q) * s;
-  float M = mrun;
-  for (int sl = 0; sl < s; ++sl) M = fmaxf(M, pml[(p0 + sl) * 2]);
-  const float fl = exp2f(mrun - M);
-  float L = l * fl;
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) o[dt][j] *= fl;
   for (int sl = 0; sl < s; ++sl) {
     const float2 ml = *(const float2*)(pml + (p0 + sl) * 2);
     const float f = exp2f(ml.x - M);
-    L += f * ml.y;
+    lrun += f * ml.y;
     const float* prow = pacc + (p0 + sl) * D;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
@@ -764,7 +759,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Q, c
       o[dt][3] += f * a.w;
     }
   }
-  const float inv = 1.f / L;
+  if (g != 0) lrun = 0.f;
+  float mrun = M;
+  attend_landmarks<T, D>(sm, LR, qf, qtop, vtop, z, m, sl2e, mrun, lrun, o, tid);
+  if (!ok) return;
+  const float inv = 1.f / quad_sum(lrun);
   T* orow = out + ((size_t)z * N + q) * D;
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt)

@@ -169,8 +169,10 @@ def sweep(w, Qd, Kd, Vd, steps: int, warmup: int, breakdown: bool) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # the GPU reaches its steady clocks only after some tens of ms of work: with 5
+    # warm-up forwards (~3 ms) the timed forwards run ~12 % slower than after 100
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="vit_b")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--breakdown", action="store_true", help="print per-step times to stderr")

@@ -570,7 +570,20 @@ __global__ __launch_bounds__(256) void route_exact_kernel(const T* __restrict__ 
 template <typename T, int D, int TM, bool RES>
 static hipError_t route_fast_launch(const Plan& p, const void* Q, char* ws, hipStream_t st) {
   if constexpr (RES) {
-    const int tpw = 8;   // several query tiles per workgroup: the landmarks stay staged
+    // several query tiles per workgroup (the landmarks stay staged), as many as
+    // make the grid one round of resident workgroups
+    static int slots = 0;
+    if (slots == 0) {
+      int dev = 0, n_cu = 256, occ = 1;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        n_cu = 256;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, route_fast_kernel<T, D, TM>, 256, 0) != hipSuccess)
+        occ = 1;
+      slots = n_cu * std::max(1, occ);
+    }
+    const int per_slice = std::max(1, slots / p.BH);
+    const int tpw = (p.qtiles + per_slice - 1) / per_slice;
     hipLaunchKernelGGL((route_fast_kernel<T, D, TM>), dim3((p.qtiles + tpw - 1) / tpw, p.BH), dim3(256), 0,
                        st, (const T*)Q, (const void*)(ws + p.ws.qtop), (const double*)(ws + p.ws.qt64),
                        (const float*)(ws + p.ws.qtnorm), (int32_t*)(ws + p.ws.E), (uint32_t*)(ws + p.ws.counters),

@@ -122,25 +122,11 @@ __device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t& total) 
   return x - v;
 }
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor(v, o, WAVE));
-  return v;
-}
-
 // DPP-based reductions (no LDS round trip): within each row of 16 lanes, then
 // across the four rows with readlane; the result is wave-uniform.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
-}
-__device__ __forceinline__ uint32_t wave_sum_uniform(uint32_t x) {
-  x += dpp_u32<0xB1>(x);    // quad_perm [1,0,3,2]
-  x += dpp_u32<0x4E>(x);    // quad_perm [2,3,0,1]
-  x += dpp_u32<0x141>(x);   // row_half_mirror
-  x += dpp_u32<0x140>(x);   // row_mirror
-  return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) + __builtin_amdgcn_readlane(x, 32) +
-         __builtin_amdgcn_readlane(x, 48);
 }
 __device__ __forceinline__ uint32_t wave_max_uniform(uint32_t x) {
   x = max(x, dpp_u32<0xB1>(x));

@@ -218,15 +218,6 @@ __device__ __forceinline__ void load_landmarks(KVRegs<T, D, sizeof(T) == 2 ? 2 :
   R.v.load([&](int rr) { return vz + (size_t)(lb0 + rr) * D; }, live, tid);
 }
 
-// Routed block kb of one expert: token rows K[I[kb + r]], V[I[kb + r]].
-template <typename T, int D>
-__device__ __forceinline__ void load_routed(KVRegs<T, D, 1>& R, const T* Kz, const T* Vz, const int32_t* Ie, int k,
-                                            int kb, int tid) {
-  const int live = min(kKeyBlock, k - kb);
-  R.k[0].load([&](int rr) { return Kz + (size_t)Ie[kb + rr] * D; }, live, tid);
-  R.v.load([&](int rr) { return Vz + (size_t)Ie[kb + rr] * D; }, live, tid);
-}
-
 // Attention over the m landmark pairs (keys Q~, values V~), block 0 already in
 // registers (R). The next block is fetched into R while the current one
 // computes. Block-uniform call; ends with the LDS tiles free again.

@@ -51,12 +51,6 @@ __device__ __forceinline__ double row_bound(const float* qtnorm, const float* km
   return gamma * (double)qtnorm[row] * (double)wave_max(kmx);
 }
 
-template <typename T>
-__device__ __forceinline__ double kval64(const T* kr, int c) {
-  if constexpr (sizeof(T) == 2) return (double)bf16_to_f32(((const uint16_t*)kr)[c]);
-  else return (double)kr[c];
-}
-
 // fp64 dot product of a landmark query (fp64) with one key row, by one lane; the
 // key row is fetched in 16-byte pieces that are all in flight together.
 template <typename T, int D>

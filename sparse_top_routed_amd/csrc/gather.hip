@@ -7,10 +7,11 @@
 // scan, scatter). The gather kernel then runs one workgroup per tile of up to 64
 // queries of one bucket: the expert's k token rows are gathered into LDS 64 at a
 // time and every query of the tile attends them on MFMA, so each gathered row is
-// read once per tile rather than once per query. With s = 1 the same workgroup
-// also attends the m landmark pairs and writes the output; with s > 1 it writes
-// an unnormalised partial per (query, slot) and the combine kernel attends the
-// landmark pairs and merges the s + 1 partial softmaxes.
+// read once per tile rather than once per query. With s = 1 and m <= 64 the
+// same workgroup also attends the m landmark pairs (one block, resident in LDS)
+// and writes the output; otherwise it writes an unnormalised partial per
+// (query, slot) and the combine kernel attends the landmark pairs (once per 64
+// consecutive queries) and merges the s + 1 partial softmaxes.
 #include <type_traits>
 
 #include "attn_core.h"
@@ -358,10 +359,13 @@ __device__ __forceinline__ void load_rows(KVRegs<T, D, 1>& R, const RowIdx<T, D>
 // (block j = tile j / B, keys 64 (j % B), B = ceil(k / 64)). While block j
 // computes, the rows of block j + 1 (their indices already in registers) and the
 // indices of block j + 2 are in flight, so no prefetch waits on a dependent
-// load. With s = 1 each tile also attends the slice's landmark pairs, kept
-// resident in LDS while the slice does not change.
+// load. FUSED (s = 1, m <= 64): each tile also attends the slice's landmark
+// pairs, kept resident in LDS while the slice does not change.
+// The bf16 d = 64 forms need only a few registers more than three waves per
+// SIMD allow: held to three.
 template <typename T, int D, bool FUSED>
-__global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 && D == 64 ? 3 : 1)))
+void gather_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                      const T* __restrict__ V, const int32_t* __restrict__ I,
                                                      const int4* __restrict__ tiles, const int32_t* __restrict__ perm,
                                                      const void* __restrict__ qtop, const void* __restrict__ vtop,
@@ -380,7 +384,8 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ Q, co
   // this workgroup's entries: g0 + jj + gs e, e = 0 .. nent - 1
   const long g0 = (long)grp * gchunk, g1 = min(total, g0 + gchunk);
   const long nent = g1 - g0 > jj ? (g1 - g0 - jj + gs - 1) / gs : 0;
-  const bool resident = FUSED && m <= kKeyBlock;
+  // FUSED (s = 1, m <= 64): the slice's landmark block stays resident in LDS
+  const bool resident = FUSED;
   const int B = (k + kKeyBlock - 1) / kKeyBlock;
 
   for (long base = 0; base < nent; base += 256) {
@@ -474,23 +479,9 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ Q, co
         qf_n.load(Q + ((size_t)sm.tz[tn] * N + entry_n / s) * D, g);
       }
       const bool wave_live = 16 * w < cur.z;
-      if constexpr (FUSED) {
-        if (newtile) {
-          if (resident) {
-            if (wave_live) attend_tiles<T, D, KP>(sm.lm.k0, sm.lm.k1, sm.lm.v, qf, m, sl2e, mrun, lrun, o, lane);
-          } else {
-            for (int lb0 = 0; lb0 < m; lb0 += kKeyBlock) {
-              KVRegs<T, D, KP> LR;
-              load_landmarks<T, D>(LR, qtop, vtop, zc, m, lb0, tid);
-              __syncthreads();
-              LR.store(sm.lm, tid);
-              __syncthreads();
-              if (wave_live)
-                attend_tiles<T, D, KP>(sm.lm.k0, sm.lm.k1, sm.lm.v, qf, min(kKeyBlock, m - lb0), sl2e, mrun, lrun,
-                                       o, lane);
-            }
-          }
-        }
+      if constexpr (FUSED) {   // the landmark part, first block of each tile
+        if (newtile && wave_live)
+          attend_tiles<T, D, KP>(sm.lm.k0, sm.lm.k1, sm.lm.v, qf, m, sl2e, mrun, lrun, o, lane);
       }
       if (wave_live) attend_tiles<T, D, 1>(sm.rk, nullptr, sm.rv, qf, min(kKeyBlock, k - kb), sl2e, mrun, lrun, o, lane);
 
@@ -825,7 +816,7 @@ static hipError_t gather_launch(const Plan& p, const void* Q, const void* K, con
                        (const void*)(ws + p.ws.qtop), vtop, (T*)out, p.N, p.m, p.k, p.max_tiles, p.BH, gs, sl2e);
     return hipGetLastError();
   }
-  if (p.s == 1) {
+  if (p.s == 1 && p.m <= kKeyBlock) {
     hipLaunchKernelGGL((gather_kernel<T, D, true>), dim3(grid), dim3(256), 0, st, (const T*)Q, (const T*)K, (const T*)V,
                        (const int32_t*)(ws + p.ws.I), (const int4*)(ws + p.ws.tiles), (const int32_t*)(ws + p.ws.perm),
                        (const void*)(ws + p.ws.qtop), vtop, (T*)out, (float*)nullptr, (float*)nullptr, p.N, p.m, p.k,

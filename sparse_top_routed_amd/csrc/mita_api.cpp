@@ -122,7 +122,7 @@ mita_status make_plan(const mita_shape* shape, int m, int k, int s, Plan* p, con
   L.boff = take(bh * (m + 1) * 4);
   L.tiles = take(bh * (size_t)P.max_tiles * 16);
   L.perm = take(bh * N * s * 4);
-  if (s > 1) {
+  if (s > 1 || m > kKeyBlock) {   // partial outputs, merged with the landmark part by the combine kernel
     L.pacc = take(bh * N * s * d * 4);
     L.pml = take(bh * N * s * 2 * 4);
   } else {

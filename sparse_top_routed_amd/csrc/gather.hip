@@ -359,7 +359,7 @@ __device__ __forceinline__ void load_rows(KVRegs<T, D, 1>& R, const RowIdx<T, D>
 // (block j = tile j / B, keys 64 (j % B), B = ceil(k / 64)). While block j
 // computes, the rows of block j + 1 (their indices already in registers) and the
 // indices of block j + 2 are in flight, so no prefetch waits on a dependent
-// load. FUSED (s = 1, m <= 64): each tile also attends the slice's landmark
+// load; during a tile's last block, so are the next tile's query rows. FUSED (s = 1, m <= 64): each tile also attends the slice's landmark
 // pairs, kept resident in LDS while the slice does not change.
 // The bf16 d = 64 forms need only a few registers more than three waves per
 // SIMD allow: held to three.
@@ -475,8 +475,10 @@ void gather_kernel(const T* __restrict__ Q, const T* __restrict__ K,
         load_rows<T, D>(RR, ix, K + (size_t)zb * N * D, V + (size_t)zb * N * D, tid);
         blk(j + 2, zb, Ieb, kbb);
         ix.load(Ieb, k, kbb, tid);
-        const int tn = min(ti + 1, (int)nt - 1);
-        qf_n.load(Q + ((size_t)sm.tz[tn] * N + entry_n / s) * D, g);
+        if (kb + kKeyBlock >= k) {   // the tile's last block: the next tile's query rows (block-uniform)
+          const int tn = min(ti + 1, (int)nt - 1);
+          qf_n.load(Q + ((size_t)sm.tz[tn] * N + entry_n / s) * D, g);
+        }
       }
       const bool wave_live = 16 * w < cur.z;
       if constexpr (FUSED) {   // the landmark part, first block of each tile

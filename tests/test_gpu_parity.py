@@ -172,3 +172,35 @@ def test_full_size_sampled(name, lib):
         say(f"[parity-full] {name}: oracle on slice {z}")
         st = check_slice(w, Q, K, V, gpu, z, queries=queries, check_s=False)
         say(f"  slice {z}: {st}")
+
+
+def test_forward_on_a_side_stream_and_in_a_graph(lib):
+    """mita_forward runs on the stream it is given (here a non-default torch
+    stream) and can be captured into a HIP graph; every replay, with eager work
+    between replays, must match the eager output bit for bit."""
+    w = SMALL[1]
+    Q, K, V = synth.make_inputs(w)
+    Qd, Kd, Vd = (to_device(x, w.dtype) for x in (Q, K, V))
+    call = lib.Mita.create(Qd, w.m, w.k, w.s, pool=(w.pool_h, w.pool_w))
+    ref = call.forward(Qd, Kd, Vd).clone()           # eager, default stream (also creates the side stream)
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    out = torch.empty_like(Qd)
+    with torch.cuda.stream(st):
+        call.forward(Qd, Kd, Vd, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+    g = torch.cuda.CUDAGraph()
+    gout = torch.empty_like(Qd)
+    with torch.cuda.graph(g, stream=st):
+        call.forward(Qd, Kd, Vd, gout)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        gout.zero_()
+        eager = call.forward(Qd, Kd, Vd)             # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(gout.view(torch.int16), ref.view(torch.int16)), f"replay {rep} differs"
+        assert torch.equal(eager.view(torch.int16), ref.view(torch.int16))

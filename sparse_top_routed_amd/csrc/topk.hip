@@ -25,7 +25,8 @@
 
 namespace mita {
 
-constexpr int kBandMax = 1024;   // band members the select kernel re-scores in LDS (more: fallback)
+constexpr int kBandMax = 128;   // band members the select kernel re-scores in LDS (more: fallback; a band
+                                 // normally holds a few members, and LDS per wave sets the occupancy)
 
 __device__ __forceinline__ float round_down_f32(double x) {
   float f = (float)x;

@@ -176,6 +176,15 @@ __device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+// Two floats as fp16 bits (round to nearest even), low half first.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f16x2 v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[0]; }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[1]; }
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const bf16x2 v = {(__bf16)lo, (__bf16)hi};

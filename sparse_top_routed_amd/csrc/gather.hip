@@ -369,7 +369,7 @@ void gather_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                      const T* __restrict__ V, const int32_t* __restrict__ I,
                                                      const int4* __restrict__ tiles, const int32_t* __restrict__ perm,
                                                      const void* __restrict__ qtop, const void* __restrict__ vtop,
-                                                     T* __restrict__ out, float* __restrict__ pacc,
+                                                     T* __restrict__ out, void* __restrict__ pacc,
                                                      float* __restrict__ pml, int N, int m, int k, int s,
                                                      int max_tiles, long total, long gchunk, int gs, float sl2e) {
   using TL = Tiles<T, D>;
@@ -497,13 +497,30 @@ void gather_kernel(const T* __restrict__ Q, const T* __restrict__ K,
 #pragma unroll
             for (int dt = 0; dt < D / 16; ++dt)
               store4<T>(orow + 16 * dt + 4 * g, o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
-          } else {
+          } else {   // the slot's output o / l, divided by its largest magnitude (the quad holds the row)
             const size_t ps = ((size_t)zc * N + q) * s + slot;
-            float* prow = pacc + ps * D;
+            const float inv = 1.f / l;
+            float amax = 0.f;
 #pragma unroll
             for (int dt = 0; dt < D / 16; ++dt)
-              *(float4*)(prow + 16 * dt + 4 * g) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
-            if (g == 0) *(float2*)(pml + ps * 2) = make_float2(mrun, l);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(o[dt][j]));
+            amax = quad_max(amax) * inv;
+            const float sc = amax > 0.f ? amax : 1.f, wv = inv / sc;
+            if constexpr (BF) {   // fp16 in [-1, 1]: 2^-11 relative to the slot's largest value
+              uint16_t* prow = (uint16_t*)pacc + ps * D;
+#pragma unroll
+              for (int dt = 0; dt < D / 16; ++dt)
+                *(uint2*)(prow + 16 * dt + 4 * g) = make_uint2(pack_f16x2(o[dt][0] * wv, o[dt][1] * wv),
+                                                               pack_f16x2(o[dt][2] * wv, o[dt][3] * wv));
+            } else {
+              float* prow = (float*)pacc + ps * D;
+#pragma unroll
+              for (int dt = 0; dt < D / 16; ++dt)
+                *(float4*)(prow + 16 * dt + 4 * g) =
+                    make_float4(o[dt][0] * wv, o[dt][1] * wv, o[dt][2] * wv, o[dt][3] * wv);
+            }
+            if (g == 0) *(float4*)(pml + ps * 4) = make_float4(mrun, l, sc, 0.f);
           }
         }
       }
@@ -708,7 +725,7 @@ __global__ __launch_bounds__(256) void gather1_kernel(const T* __restrict__ Q, c
 // first landmark block; the landmark blocks then continue the same softmax.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Q, const void* __restrict__ qtop,
-                                                      const void* __restrict__ vtop, const float* __restrict__ pacc,
+                                                      const void* __restrict__ vtop, const void* __restrict__ pacc,
                                                       const float* __restrict__ pml, T* __restrict__ out, int N, int m,
                                                       int s, float sl2e) {
   __shared__ AttnLds<T, D> sm;
@@ -724,23 +741,29 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Q, c
   // (l on one lane of the quad: the lanes' sums are added at the end)
   const size_t p0 = ((size_t)z * N + qc) * s;
   float M = -INFINITY;
-  for (int sl = 0; sl < s; ++sl) M = fmaxf(M, pml[(p0 + sl) * 2]);
+  for (int sl = 0; sl < s; ++sl) M = fmaxf(M, pml[(p0 + sl) * 4]);
   float lrun = 0.f;
   f32x4 o[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int sl = 0; sl < s; ++sl) {
-    const float2 ml = *(const float2*)(pml + (p0 + sl) * 2);
+  for (int sl = 0; sl < s; ++sl) {   // slot partial: (max, sum, scale) and its output / (sum * scale)
+    const float4 ml = *(const float4*)(pml + (p0 + sl) * 4);
     const float f = exp2f(ml.x - M);
     lrun += f * ml.y;
-    const float* prow = pacc + (p0 + sl) * D;
+    const float wv = f * ml.y * ml.z;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const float4 a = *(const float4*)(prow + 16 * dt + 4 * g);
-      o[dt][0] += f * a.x;
-      o[dt][1] += f * a.y;
-      o[dt][2] += f * a.z;
-      o[dt][3] += f * a.w;
+      float4 a;
+      if constexpr (sizeof(T) == 2) {
+        const uint2 u = *(const uint2*)((const uint16_t*)pacc + (p0 + sl) * D + 16 * dt + 4 * g);
+        a = make_float4(f16_lo(u.x), f16_hi(u.x), f16_lo(u.y), f16_hi(u.y));
+      } else {
+        a = *(const float4*)((const float*)pacc + (p0 + sl) * D + 16 * dt + 4 * g);
+      }
+      o[dt][0] += wv * a.x;
+      o[dt][1] += wv * a.y;
+      o[dt][2] += wv * a.z;
+      o[dt][3] += wv * a.w;
     }
   }
   if (g != 0) lrun = 0.f;
@@ -827,11 +850,11 @@ static hipError_t gather_launch(const Plan& p, const void* Q, const void* K, con
   }
   hipLaunchKernelGGL((gather_kernel<T, D, false>), dim3(grid), dim3(256), 0, st, (const T*)Q, (const T*)K, (const T*)V,
                      (const int32_t*)(ws + p.ws.I), (const int4*)(ws + p.ws.tiles), (const int32_t*)(ws + p.ws.perm),
-                     (const void*)(ws + p.ws.qtop), vtop, (T*)out, (float*)(ws + p.ws.pacc), (float*)(ws + p.ws.pml),
+                     (const void*)(ws + p.ws.qtop), vtop, (T*)out, (void*)(ws + p.ws.pacc), (float*)(ws + p.ws.pml),
                      p.N, p.m, p.k, p.s, p.max_tiles, total, gchunk, gsz, sl2e);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((combine_kernel<T, D>), dim3(p.qtiles, p.BH), dim3(256), 0, st, (const T*)Q,
-                     (const void*)(ws + p.ws.qtop), vtop, (const float*)(ws + p.ws.pacc), (const float*)(ws + p.ws.pml),
+                     (const void*)(ws + p.ws.qtop), vtop, (const void*)(ws + p.ws.pacc), (const float*)(ws + p.ws.pml),
                      (T*)out, p.N, p.m, p.s, sl2e);
   return hipGetLastError();
 }

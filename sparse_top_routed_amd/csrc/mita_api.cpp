@@ -123,8 +123,8 @@ mita_status make_plan(const mita_shape* shape, int m, int k, int s, Plan* p, con
   L.tiles = take(bh * (size_t)P.max_tiles * 16);
   L.perm = take(bh * N * s * 4);
   if (s > 1 || m > kKeyBlock) {   // partial outputs, merged with the landmark part by the combine kernel
-    L.pacc = take(bh * N * s * d * 4);
-    L.pml = take(bh * N * s * 2 * 4);
+    L.pacc = take(bh * N * s * d * (sh.dtype == MITA_BF16 ? 2 : 4));   // fp16 for bf16 inputs, else fp32
+    L.pml = take(bh * N * s * 4 * 4);
   } else {
     L.pacc = L.pml = 0;
   }

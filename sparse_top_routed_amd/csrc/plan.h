@@ -44,8 +44,8 @@ struct Layout {
   size_t boff;      // u32 [BH, m + 1]    bucket offsets
   size_t tiles;     // int4 [BH, max_tiles] query tiles: (expert, first row, rows, perm offset) or -1
   size_t perm;      // i32 [BH, N * s]    (query * s + slot) grouped by expert
-  size_t pacc;      // f32 [BH, N, s, d]  per-slot partial outputs (s > 1)
-  size_t pml;       // f32 [BH, N, s, 2]  per-slot (max, sum)
+  size_t pacc;      // [BH, N, s, d] per-slot outputs o / (sum * scale): fp16 (bf16 inputs) or f32
+  size_t pml;       // f32 [BH, N, s, 4] per-slot (max, sum, scale, pad)
   size_t total;
   size_t counters_bytes;
 };

@@ -38,8 +38,11 @@ def step_bytes(w) -> dict:
         # group maxima read, K read once more (candidate pass), expert lists written
         "topk": BH * m * nbg * 4 + tok + BH * m * k * 4,
         "route": tok + BH * N * s * 4,
-        # Q read, each expert's k gathered K/V rows once, output written (+ partials when s > 1)
-        "gather": 2 * tok + BH * m * k * d * e * 2 + (BH * N * s * (d + 2) * 4 * 2 if s > 1 else 0),
+        # Q read, each expert's k gathered K/V rows once, output written, + the per-slot partials
+        # written and read back when s > 1 or m > 64 (d values in 16 bits for bf16, else 32, and
+        # 16 bytes of (max, sum, scale))
+        "gather": 2 * tok + BH * m * k * d * e * 2
+        + (BH * N * s * (d * e + 16) * 2 if (s > 1 or m > 64) else 0),
     }
 
 

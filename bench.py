@@ -169,6 +169,45 @@ def sweep(w, Qd, Kd, Vd, steps: int, warmup: int, breakdown: bool) -> int:
     return 0
 
 
+def dense_compare(w, Qd, Kd, Vd, steps: int, warmup: int) -> int:
+    """The full-attention comparator (softmax over all N keys, the quadratic
+    baseline) against the MiTA forward on the same inputs: mean time of each and
+    the ratio, plus the comparator's MFMA throughput (4 N^2 d flops per slice)."""
+    import torch
+
+    from sparse_top_routed_amd import mita
+
+    st = torch.cuda.current_stream()
+    call = mita.Mita.create(Qd, w.m, w.k, w.s, grid=(w.grid_h, w.grid_w), pool=(w.pool_h, w.pool_w))
+    out, dout = torch.empty_like(Qd), torch.empty_like(Qd)
+
+    def timed(fn, n):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(st)
+        for _ in range(n):
+            fn()
+        t1.record(st)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / n
+
+    for _ in range(warmup):
+        call.forward(Qd, Kd, Vd, out)
+    mita_ms = timed(lambda: call.forward(Qd, Kd, Vd, out), steps)
+    first = timed(lambda: mita.dense_attention(Qd, Kd, Vd, dout), 1)   # warm-up; sizes the timed run to ~2 s
+    n = max(1, min(steps, int(2000.0 / max(first, 1e-3))))
+    dense_ms = timed(lambda: mita.dense_attention(Qd, Kd, Vd, dout), n)
+    flops = 4.0 * w.slices * w.N * w.N * w.d
+    peak = 2500.0 if w.dtype == "bf16" else 157.3   # dense MFMA TFLOP/s of the input dtype
+    tf = flops / (dense_ms * 1e-3) / 1e12
+    res = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "m": w.m, "k": w.k, "s": w.s,
+           "dtype": w.dtype, "mita_ms": mita_ms, "mita_steps": steps, "dense_ms": dense_ms, "dense_steps": n,
+           "speedup": dense_ms / mita_ms, "keys_per_query": {"mita": w.m + w.k * w.s, "dense": w.N},
+           "dense_tflops": tf, "dense_mfma_frac": tf / peak}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,6 +225,9 @@ def main() -> int:
     ap.add_argument("--sweep", action="store_true",
                     help="time the forward pass over the inference-time (m, k, s) settings of synth.SWEEP on the "
                          "workload's inputs (one JSON line per setting) instead of the benchmark line")
+    ap.add_argument("--dense", action="store_true",
+                    help="time the full-attention comparator against the MiTA forward on the workload's inputs "
+                         "(one JSON line) instead of the benchmark line")
     a = ap.parse_args()
     if a.print_sha:
         for step in KERNEL_SOURCES:
@@ -213,6 +255,8 @@ def main() -> int:
     Qd, Kd, Vd = dev(Q), dev(K), dev(V)
     if a.sweep:
         return sweep(w, Qd, Kd, Vd, a.steps, a.warmup, a.breakdown)
+    if a.dense:
+        return dense_compare(w, Qd, Kd, Vd, a.steps, a.warmup)
     call = mita.Mita.create(Qd, w.m, w.k, w.s, grid=(w.grid_h, w.grid_w), pool=(w.pool_h, w.pool_w))
     out = torch.empty_like(Qd)
     for _ in range(a.warmup):

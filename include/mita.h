@@ -126,6 +126,20 @@ mita_status mita_route(const void* Q, int m, int k, int s, const mita_shape* sha
 mita_status mita_gather(const void* Q, const void* K, const void* V, int m, int k, int s, void* out,
                         const mita_shape* shape, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Full softmax attention, out = softmax(Q K^T / sqrt d) V over all N keys of each
+ * (batch, head) slice: the quadratic standard attention that MiTA replaces
+ * (MiTA pages: introduction and problem statement; the pages' speed-ups are
+ * quoted against it). Not part of the MiTA forward: a comparator on the same
+ * inputs. Q, K, V, out: [B, H, N, d] in shape->dtype, contiguous, 16-byte
+ * aligned device buffers owned by the caller; bf16 results are rounded to
+ * nearest even. Only B, H, N, d and dtype of `shape` are read (d in {64, 128},
+ * B * H * N * d < 2^31). Needs no workspace and allocates nothing; runs on
+ * `stream`. Errors: MITA_ERR_INVALID_ARG for a NULL or misaligned pointer or a
+ * bad size or dtype, MITA_ERR_UNSUPPORTED for another d, MITA_ERR_HIP if the
+ * launch fails. */
+mita_status mita_dense_attention(const void* Q, const void* K, const void* V, void* out, const mita_shape* shape,
+                                 void* stream);
+
 /* Short description of a status code (static storage). */
 const char* mita_status_string(int status);
 /* Message of the last failed call on this thread ("" if none). */

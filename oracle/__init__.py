@@ -9,6 +9,7 @@ from .mita_oracle import (  # noqa: F401
     pool,
     scores,
     shared_expert,
+    full_attention,
     topk_experts,
     route_scores,
     route,

@@ -84,6 +84,15 @@ def shared_expert(Qt: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
     return W @ np.asarray(V, np.float64)
 
 
+def full_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
+    """Standard softmax attention over all N keys, softmax(Q K^T / sqrt d) V,
+    [N, d]: the quadratic-cost baseline the pages set MiTA against (Arabic/Hindi
+    section 1 and the Dutch "Probleemstelling"). Not a step of MiTA."""
+    d = Q.shape[1]
+    W = _softmax_rows(np.asarray(Q, np.float64) @ np.asarray(K, np.float64).T / math.sqrt(d))
+    return W @ np.asarray(V, np.float64)
+
+
 def topk_experts(S: np.ndarray, k: int) -> np.ndarray:
     """Expert index sets I_i: the k tokens with the largest S[i, n], ties to the
     lower n, listed ascending; [m, k] int64 (top-k activations of K^T q~_i:

@@ -1,5 +1,5 @@
 // Wave-level pieces of flash-style attention on gfx950 MFMA, shared by the
-// shared-expert, gather and combine kernels.
+// shared-expert, gather, combine and full-attention kernels.
 //
 // A workgroup is 4 waves; each wave owns 16 queries. Keys arrive in blocks of
 // 64 staged in LDS. Scores are computed transposed, S^T = K Q^T, with the
@@ -9,6 +9,8 @@
 // so the probabilities never leave registers: bf16 needs V^T in LDS (written
 // transposed while staging), fp32 reads V rows directly.
 #pragma once
+#include <type_traits>
+
 #include "common.h"
 #include "plan.h"
 
@@ -229,6 +231,74 @@ __device__ __forceinline__ void pv_f32(const float* Vs, const f32x4 (&p)[4], f32
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) o[dt] = mma_f32(row[16 * dt], p[kt][j], o[dt]);
     }
+}
+
+// Query fragments of one query row (zeros when the row is absent).
+template <typename T, int D>
+struct QFrag {
+  uint4 b[1][D / 32];
+  float f[D / 4];
+  // qrow must be a valid row; absent rows (padding) load a real row and their
+  // results are never written, since every row of the tile is independent.
+  __device__ __forceinline__ void load(const T* qrow, int g) {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) b[0][ks] = ld16(qrow + 32 * ks + 8 * g);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < D / 4; ++ks) f[ks] = qrow[4 * ks + g];
+    }
+  }
+};
+
+template <typename T, int D>
+struct AttnLds {
+  using TL = Tiles<T, D>;
+  __align__(16) T k0[TL::KTILE];
+  __align__(16) T k1[sizeof(T) == 2 ? TL::KTILE : 8];
+  __align__(16) T v[TL::VTILE];
+};
+
+// One 64-key block of attention for the wave's 16 queries, keys already staged.
+template <typename T, int D, int KP>
+__device__ __forceinline__ void attend_block(AttnLds<T, D>& sm, const QFrag<T, D>& qf, int live, float sl2e,
+                                             float& mrun, float& lrun, f32x4 (&o)[D / 16], int lane,
+                                             bool wave_live = true) {
+  if (!wave_live) return;   // all 16 rows of this wave are padding (wave-uniform)
+  f32x4 acc[4];
+  if constexpr (sizeof(T) == 2)
+    qk_bf16<D, KP, 1>((const uint16_t*)sm.k0, (const uint16_t*)sm.k1, qf.b, acc, lane);
+  else
+    qk_f32<D>((const float*)sm.k0, qf.f, acc, lane);
+  const float alpha = online_softmax(acc, live, sl2e, mrun, lrun, lane);
+  rescale<D>(o, alpha);
+  if constexpr (sizeof(T) == 2)
+    pv_bf16<D>((const uint16_t*)sm.v, acc, o, lane);
+  else
+    pv_f32<D>((const float*)sm.v, acc, o, lane);
+}
+
+// Register copies of one key block and its value block (bf16 values transposed).
+template <typename T, int D, int KP>
+struct KVRegs {
+  RowRegs<T, D> k[KP];
+  std::conditional_t<sizeof(T) == 2, VtRegs<D>, RowRegs<T, D>> v;
+  __device__ __forceinline__ void store(AttnLds<T, D>& sm, int tid) const {
+    using TL = Tiles<T, D>;
+    k[0].store(sm.k0, TL::KSTR, tid);
+    if constexpr (KP == 2) k[1].store(sm.k1, TL::KSTR, tid);
+    if constexpr (sizeof(T) == 2) v.store((uint16_t*)sm.v, tid); else v.store(sm.v, TL::VSTR, tid);
+  }
+};
+
+// Write 4 consecutive outputs d0..d0+3 of one row.
+template <typename T>
+__device__ __forceinline__ void store4(T* dst, float a, float b, float c, float d) {
+  if constexpr (sizeof(T) == 2) {
+    *(uint2*)dst = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
+  } else {
+    *(float4*)dst = make_float4(a, b, c, d);
+  }
 }
 
 }  // namespace mita

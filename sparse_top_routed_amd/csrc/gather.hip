@@ -9,9 +9,11 @@
 // time and every query of the tile attends them on MFMA, so each gathered row is
 // read once per tile rather than once per query. With s = 1 and m <= 64 the
 // same workgroup also attends the m landmark pairs (one block, resident in LDS)
-// and writes the output; otherwise it writes an unnormalised partial per
-// (query, slot) and the combine kernel attends the landmark pairs (once per 64
-// consecutive queries) and merges the s + 1 partial softmaxes.
+// and writes the output; otherwise it writes a partial per (query, slot): its
+// softmax max and sum, and its output o / sum divided by its largest magnitude
+// (fp16 for bf16 inputs, fp32 otherwise), and the combine kernel attends the
+// landmark pairs (once per 64 consecutive queries) and merges the s + 1 partial
+// softmaxes.
 #include <type_traits>
 
 #include "attn_core.h"
@@ -148,64 +150,6 @@ __global__ __launch_bounds__(256) void bucket_slice_kernel(const int32_t* __rest
     if (ex[u] >= 0) pz[h[m + ex[u]] + rank[u]] = tid + 256 * u;
 }
 
-// Query fragments of one query row (zeros when the row is absent).
-template <typename T, int D>
-struct QFrag {
-  uint4 b[1][D / 32];
-  float f[D / 4];
-  // qrow must be a valid row; absent rows (padding) load a real row and their
-  // results are never written, since every row of the tile is independent.
-  __device__ __forceinline__ void load(const T* qrow, int g) {
-    if constexpr (sizeof(T) == 2) {
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) b[0][ks] = ld16(qrow + 32 * ks + 8 * g);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < D / 4; ++ks) f[ks] = qrow[4 * ks + g];
-    }
-  }
-};
-
-template <typename T, int D>
-struct AttnLds {
-  using TL = Tiles<T, D>;
-  __align__(16) T k0[TL::KTILE];
-  __align__(16) T k1[sizeof(T) == 2 ? TL::KTILE : 8];
-  __align__(16) T v[TL::VTILE];
-};
-
-// One 64-key block of attention for the wave's 16 queries, keys already staged.
-template <typename T, int D, int KP>
-__device__ __forceinline__ void attend_block(AttnLds<T, D>& sm, const QFrag<T, D>& qf, int live, float sl2e,
-                                             float& mrun, float& lrun, f32x4 (&o)[D / 16], int lane,
-                                             bool wave_live = true) {
-  if (!wave_live) return;   // all 16 rows of this wave are padding (wave-uniform)
-  f32x4 acc[4];
-  if constexpr (sizeof(T) == 2)
-    qk_bf16<D, KP, 1>((const uint16_t*)sm.k0, (const uint16_t*)sm.k1, qf.b, acc, lane);
-  else
-    qk_f32<D>((const float*)sm.k0, qf.f, acc, lane);
-  const float alpha = online_softmax(acc, live, sl2e, mrun, lrun, lane);
-  rescale<D>(o, alpha);
-  if constexpr (sizeof(T) == 2)
-    pv_bf16<D>((const uint16_t*)sm.v, acc, o, lane);
-  else
-    pv_f32<D>((const float*)sm.v, acc, o, lane);
-}
-
-// Register copies of one key block and its value block (bf16 values transposed).
-template <typename T, int D, int KP>
-struct KVRegs {
-  RowRegs<T, D> k[KP];
-  std::conditional_t<sizeof(T) == 2, VtRegs<D>, RowRegs<T, D>> v;
-  __device__ __forceinline__ void store(AttnLds<T, D>& sm, int tid) const {
-    using TL = Tiles<T, D>;
-    k[0].store(sm.k0, TL::KSTR, tid);
-    if constexpr (KP == 2) k[1].store(sm.k1, TL::KSTR, tid);
-    if constexpr (sizeof(T) == 2) v.store((uint16_t*)sm.v, tid); else v.store(sm.v, TL::VSTR, tid);
-  }
-};
-
 // Landmark block lb0 of slice z: keys Q~ (hi and lo planes for bf16), values V~.
 template <typename T, int D>
 __device__ __forceinline__ void load_landmarks(KVRegs<T, D, sizeof(T) == 2 ? 2 : 1>& R, const void* qtop,
@@ -235,16 +179,6 @@ __device__ __forceinline__ void attend_landmarks(AttnLds<T, D>& sm, KVRegs<T, D,
     if (lb0 + kKeyBlock < m) load_landmarks<T, D>(R, qtop, vtop, z, m, lb0 + kKeyBlock, tid);   // block-uniform
     attend_block<T, D, KP>(sm, qf, min(kKeyBlock, m - lb0), sl2e, mrun, lrun, o, lane, wave_live);
     __syncthreads();
-  }
-}
-
-// Write 4 consecutive outputs d0..d0+3 of one row.
-template <typename T>
-__device__ __forceinline__ void store4(T* dst, float a, float b, float c, float d) {
-  if constexpr (sizeof(T) == 2) {
-    *(uint2*)dst = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
-  } else {
-    *(float4*)dst = make_float4(a, b, c, d);
   }
 }
 

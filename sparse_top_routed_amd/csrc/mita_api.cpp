@@ -321,4 +321,22 @@ mita_status mita_forward(const void* Q, const void* K, const void* V, int m, int
   return hip_status(launch_gather(P, Q, K, V, out, ws, hs), "gather");
 }
 
+mita_status mita_dense_attention(const void* Q, const void* K, const void* V, void* out, const mita_shape* shape,
+                                 void* stream) {
+  if (!shape) { set_error("shape is NULL"); return MITA_ERR_INVALID_ARG; }
+  const mita_shape& sh = *shape;
+  if (sh.B < 1 || sh.H < 1 || sh.N < 1 || sh.d < 1) { set_error("B, H, N and d must be >= 1"); return MITA_ERR_INVALID_ARG; }
+  if (sh.dtype != MITA_F32 && sh.dtype != MITA_BF16) {
+    set_error("dtype must be MITA_F32 or MITA_BF16"); return MITA_ERR_INVALID_ARG;
+  }
+  if (sh.d != 64 && sh.d != 128) { set_error("d must be 64 or 128"); return MITA_ERR_UNSUPPORTED; }
+  const int64_t BH = (int64_t)sh.B * sh.H;
+  if (BH * sh.N * sh.d >= ((int64_t)1 << 31)) { set_error("B * H * N * d must be below 2^31"); return MITA_ERR_UNSUPPORTED; }
+  mita_status st;
+  if ((st = check_ptr(Q, "Q")) != MITA_OK || (st = check_ptr(K, "K")) != MITA_OK ||
+      (st = check_ptr(V, "V")) != MITA_OK || (st = check_ptr(out, "out")) != MITA_OK)
+    return st;
+  return hip_status(launch_dense(sh.dtype, sh.d, (int)BH, sh.N, Q, K, V, out, (hipStream_t)stream), "dense");
+}
+
 }  // extern "C"

@@ -84,6 +84,9 @@ hipError_t launch_landmark(const Plan& p, const void* K, const void* V, char* ws
 hipError_t launch_topk(const Plan& p, const void* K, char* ws, hipStream_t st);
 // Shared-expert merge into V~ and the top-k candidate thresholds (end of step 2).
 hipError_t launch_merge_thresh(const Plan& p, char* ws, hipStream_t st);
+// Full softmax attention over all N keys of each slice (the comparator; no workspace).
+hipError_t launch_dense(int dtype, int d, int BH, int N, const void* Q, const void* K, const void* V, void* out,
+                        hipStream_t st);
 hipError_t launch_route(const Plan& p, const void* Q, char* ws, hipStream_t st);
 hipError_t launch_bucket(const Plan& p, char* ws, hipStream_t st);
 hipError_t launch_gather(const Plan& p, const void* Q, const void* K, const void* V, void* out, char* ws,

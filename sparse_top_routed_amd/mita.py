@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libmita.so")
 MITA_OK, MITA_ERR_INVALID_ARG, MITA_ERR_UNSUPPORTED, MITA_ERR_WORKSPACE, MITA_ERR_HIP = 0, -1, -2, -3, -4
 MITA_F32, MITA_BF16 = 0, 1
 SYMBOLS = ("mita_workspace_bytes", "mita_forward", "mita_pool", "mita_landmark", "mita_topk", "mita_route",
-           "mita_gather", "mita_status_string", "mita_last_error")
+           "mita_gather", "mita_dense_attention", "mita_status_string", "mita_last_error")
 
 
 class Shape(ctypes.Structure):
@@ -52,7 +52,9 @@ def load() -> ctypes.CDLL:
     lib.mita_topk.argtypes = [vp, i, i, i, sp, vp, sz, vp, vp]
     lib.mita_route.argtypes = [vp, i, i, i, sp, vp, sz, vp, vp]
     lib.mita_gather.argtypes = [vp, vp, vp, i, i, i, vp, sp, vp, sz, vp]
-    for f in ("mita_forward", "mita_pool", "mita_landmark", "mita_topk", "mita_route", "mita_gather"):
+    lib.mita_dense_attention.argtypes = [vp, vp, vp, vp, sp, vp]
+    for f in ("mita_forward", "mita_pool", "mita_landmark", "mita_topk", "mita_route", "mita_gather",
+              "mita_dense_attention"):
         getattr(lib, f).restype = ctypes.c_int
     lib.mita_status_string.argtypes = [i]
     lib.mita_status_string.restype = ctypes.c_char_p
@@ -186,3 +188,28 @@ def forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, m: int, k: int, s
             out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """MiTA attention forward: Q, K, V [B, H, N, d] (bf16 or fp32) on the GPU."""
     return Mita.create(Q, m, k, s, grid, pool).forward(Q, K, V, out)
+
+
+def dense_attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Full softmax attention softmax(Q K^T / sqrt d) V over all N keys (the
+    quadratic baseline MiTA is compared with): Q, K, V [B, H, N, d], bf16 or
+    fp32, contiguous, on the GPU."""
+    if Q.dim() != 4:
+        raise ValueError("Q must be [B, H, N, d]")
+    B, H, N, d = Q.shape
+    for t in (K, V):
+        if t.shape != Q.shape or t.dtype != Q.dtype:
+            raise ValueError("Q, K and V must have one shape and dtype")
+    for t in (Q, K, V):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous and on the GPU")
+    if Q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("dtype must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty_like(Q)
+    elif out.shape != Q.shape or out.dtype != Q.dtype or not out.is_contiguous():
+        raise ValueError("out must match Q")
+    shape = make_shape(B, H, N, d, 1, Q.dtype)
+    _check(load().mita_dense_attention(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), ctypes.byref(shape), _stream()))
+    return out

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import synth
-from helpers import check_slice, run_gpu_steps, say, to_device, out_to_f64
+from helpers import TOL_OUT, check_slice, run_gpu_steps, say, slice_f64, to_device, out_to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -120,6 +120,26 @@ def test_degenerate_ties(lib):
     check_slice(w, Q, K, V, gpu, 0)
 
 
+def test_partials_scale_with_v(lib):
+    """With s > 1 each slot's partial output is stored relative to its own largest
+    magnitude (fp16 for bf16 inputs): values far beyond fp16's range pass through,
+    scaling V by a power of two scales the output by exactly that power (bit for
+    bit: every rounding on the way scales with it), and V = 0 gives exactly 0."""
+    for dt in ("bf16", "f32"):
+        w = small(f"v_scale_{dt}", B=1, H=2, N=3000, grid_w=3000, pool_w=30, k=70, s=3, dtype=dt)
+        say(f"[v-scale] {w.name}")
+        Q, K, V = synth.make_inputs(w)
+        Qd, Kd, Vd = (to_device(x, w.dtype) for x in (Q, K, V))
+        call = lib.Mita.create(Qd, w.m, w.k, w.s, pool=(w.pool_h, w.pool_w))
+        a = call.forward(Qd, Kd, Vd).clone()
+        b = call.forward(Qd, Kd, Vd * 2.0 ** 20).clone()
+        c = call.forward(Qd, Kd, torch.zeros_like(Vd))
+        torch.cuda.synchronize()
+        assert b.float().abs().max().item() > 65504.0
+        assert torch.equal(a.float() * 2.0 ** 20, b.float())
+        assert not c.float().abs().max().item()
+
+
 def test_single_landmark_and_identity_pool(lib):
     for pw, k, s in ((1, 20, 1), (128, 5, 3)):
         w = small(f"pool{pw}", N=128, grid_w=128, pool_w=pw, k=k, s=s, dtype="bf16")
@@ -204,3 +224,29 @@ def test_forward_on_a_side_stream_and_in_a_graph(lib):
         torch.cuda.synchronize()
         assert torch.equal(gout.view(torch.int16), ref.view(torch.int16)), f"replay {rep} differs"
         assert torch.equal(eager.view(torch.int16), ref.view(torch.int16))
+
+
+# The full-attention comparator (standard softmax attention over all N keys):
+# ragged N, both head sizes and dtypes, several XCD groups, a single key.
+DENSE = [
+    small("dense_bf16", B=1, H=2, N=1000, grid_w=1000, pool_w=10, dtype="bf16"),
+    small("dense_f32_d128", B=2, H=1, N=777, d=128, grid_w=777, pool_w=7),
+    small("dense_bf16_d128", B=1, H=1, N=4100, d=128, grid_w=4100, pool_w=41, dtype="bf16"),
+    small("dense_f32_many_tiles", B=3, H=7, N=300, grid_w=300, pool_w=3),
+    small("dense_one_key", B=1, H=3, N=1, grid_w=1, pool_w=1, k=1, s=1, dtype="bf16"),
+]
+
+
+@pytest.mark.parametrize("w", DENSE, ids=lambda w: w.name)
+def test_dense_attention(w, lib):
+    import oracle
+    say(f"[dense] {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}")
+    Q, K, V = synth.make_inputs(w)
+    Qd, Kd, Vd = (to_device(x, w.dtype) for x in (Q, K, V))
+    O = lib.dense_attention(Qd, Kd, Vd)
+    torch.cuda.synchronize()
+    O = out_to_f64(O).reshape(-1, w.N, w.d)
+    for z in range(w.slices):
+        ref = oracle.full_attention(*(slice_f64(x, w.dtype, z) for x in (Q, K, V)))
+        err = np.abs(O[z] - ref).max()
+        assert err <= TOL_OUT[w.dtype], f"slice {z}: max abs error {err:.3g}"

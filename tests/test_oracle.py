@@ -330,3 +330,35 @@ def test_needles_scale_keys_only():
     changed = np.nonzero((K != K0).any(axis=1))[0]
     assert len(changed) == round(0.01 * 4096)
     np.testing.assert_array_equal(K[changed], 4 * K0[changed])
+
+
+# Standard attention over all keys (the baseline the pages compare MiTA with;
+# the GPU comparator kernel is checked against oracle.full_attention).
+@pytest.mark.parametrize("N,d", [(1, 8), (37, 16), (300, 64)])
+def test_full_attention_matches_torch_sdpa(N, d):
+    Q, K, V = rand((N, d), 30), rand((N, d), 31), rand((N, d), 32)
+    ref = F.scaled_dot_product_attention(*(torch.from_numpy(x)[None, None] for x in (Q, K, V)))[0, 0].numpy()
+    np.testing.assert_allclose(oracle.full_attention(Q, K, V), ref, rtol=1e-12, atol=1e-13)
+
+
+def test_full_attention_brute_force():
+    N, d = 5, 3
+    Q, K, V = rand((N, d), 33), rand((N, d), 34), rand((N, d), 35)
+    out = oracle.full_attention(Q, K, V)
+    for i in range(N):
+        w = [math.exp(sum(Q[i, c] * K[j, c] for c in range(d)) / math.sqrt(d)) for j in range(N)]
+        for c in range(d):
+            assert abs(out[i, c] - sum(w[j] * V[j, c] for j in range(N)) / sum(w)) < 1e-13
+
+
+def test_full_attention_closed_forms():
+    N, d = 50, 8
+    Q, V = rand((N, d), 36), rand((N, d), 37)
+    # identical keys: uniform weights, every row is the mean of V
+    K = np.tile(rand((1, d), 38), (N, 1))
+    np.testing.assert_allclose(oracle.full_attention(Q, K, V), np.tile(V.mean(axis=0), (N, 1)), rtol=1e-13, atol=1e-14)
+    # one key far above the rest for every query: the output is its value row
+    K = np.zeros((N, d))
+    K[7, 0] = 1e3
+    Qp = np.abs(Q) + 1.0
+    np.testing.assert_allclose(oracle.full_attention(Qp, K, V), np.tile(V[7], (N, 1)), rtol=0, atol=1e-12)

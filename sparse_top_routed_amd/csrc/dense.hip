@@ -8,8 +8,9 @@
 // wave) and streams the slice's keys and values through LDS 64 at a time (the
 // next block is fetched into registers while the current one computes) with
 // an online softmax; scores and probabilities stay in registers. Same MFMA
-// tiles as the output step. Blocks of 8 consecutive workgroups share a slice
-// and so one XCD's L2 (workgroups are dealt round-robin over the 8 XCDs).
+// tiles as the output step. Each XCD takes a contiguous run of the (slice,
+// query tile) items, so the workgroups reading one slice's keys and values
+// share that XCD's L2 (workgroups are dealt round-robin over the 8 XCDs).
 #include "attn_core.h"
 
 namespace mita {

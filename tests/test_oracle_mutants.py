@@ -114,3 +114,34 @@ def test_mutant_shared_expert_unscaled(monkeypatch):
         return (W / W.sum(axis=1, keepdims=True)) @ V
     _patch(monkeypatch, "shared_expert", shared_expert)
     assert _fails(lambda: pins.test_shared_expert_matches_torch_sdpa(16, 1024, 64))
+
+
+def _full_attention_mutant(scale=None, transpose_weights=False, keys_as_values=False):
+    def full_attention(Q, K, V):
+        Q, K, V = (np.asarray(x, np.float64) for x in (Q, K, V))
+        d = Q.shape[1]
+        lg = Q @ K.T * (scale(d) if scale else 1 / math.sqrt(d))
+        W = np.exp(lg - lg.max(axis=1, keepdims=True))
+        W = W / W.sum(axis=1, keepdims=True)
+        if transpose_weights:
+            W = W.T
+        return W @ (K if keys_as_values else V)
+    return full_attention
+
+
+FULL_PINS = (lambda: pins.test_full_attention_matches_torch_sdpa(37, 16),
+             pins.test_full_attention_brute_force, pins.test_full_attention_closed_forms)
+
+
+@pytest.mark.parametrize("kw", [dict(scale=lambda d: 1.0 / d), dict(scale=lambda d: 1.0),
+                                dict(transpose_weights=True), dict(keys_as_values=True)],
+                         ids=["scale_1_over_d", "unscaled", "transposed_weights", "keys_as_values"])
+def test_mutant_full_attention(monkeypatch, kw):
+    _patch(monkeypatch, "full_attention", _full_attention_mutant(**kw))
+    assert _fails(*FULL_PINS)
+
+
+def test_full_attention_mutant_harness_is_faithful(monkeypatch):
+    # the unmutated rewrite passes every pin, so a failure above is the mutation's
+    _patch(monkeypatch, "full_attention", _full_attention_mutant())
+    assert not _fails(*FULL_PINS)

@@ -84,3 +84,23 @@ def test_status_strings():
     for code in (0, -1, -2, -3, -4):
         assert lib.mita_status_string(code)
     assert b"unknown" in lib.mita_status_string(42)
+
+
+def test_dense_attention_argument_checks():
+    # every case fails its checks before anything is enqueued (no GPU needed)
+    lib = mita.load()
+    good = mita.Shape(1, 2, 1000, 64, 1, 1000, 1, 16, mita.MITA_BF16)
+    for sh, ptrs, code in [
+        (None, (FAKE,) * 4, mita.MITA_ERR_INVALID_ARG),
+        (mita.Shape(1, 2, 0, 64, 1, 1, 1, 1, mita.MITA_BF16), (FAKE,) * 4, mita.MITA_ERR_INVALID_ARG),
+        (mita.Shape(1, 2, 1000, 64, 1, 1000, 1, 16, 7), (FAKE,) * 4, mita.MITA_ERR_INVALID_ARG),
+        (mita.Shape(1, 2, 1000, 96, 1, 1000, 1, 16, mita.MITA_F32), (FAKE,) * 4, mita.MITA_ERR_UNSUPPORTED),
+        (mita.Shape(1 << 10, 1 << 10, 1 << 12, 128, 1, 1 << 12, 1, 1, mita.MITA_F32), (FAKE,) * 4,
+         mita.MITA_ERR_UNSUPPORTED),   # B H N d >= 2^31
+        (good, (None, FAKE, FAKE, FAKE), mita.MITA_ERR_INVALID_ARG),
+        (good, (FAKE, FAKE + 8, FAKE, FAKE), mita.MITA_ERR_INVALID_ARG),   # misaligned K
+        (good, (FAKE, FAKE, FAKE, None), mita.MITA_ERR_INVALID_ARG),
+    ]:
+        st = lib.mita_dense_attention(*ptrs, ctypes.byref(sh) if sh is not None else None, None)
+        assert st == code, (sh and (sh.N, sh.d, sh.dtype), ptrs, st)
+        assert lib.mita_last_error()

@@ -250,3 +250,27 @@ def test_dense_attention(w, lib):
         ref = oracle.full_attention(*(slice_f64(x, w.dtype, z) for x in (Q, K, V)))
         err = np.abs(O[z] - ref).max()
         assert err <= TOL_OUT[w.dtype], f"slice {z}: max abs error {err:.3g}"
+
+
+@pytest.mark.parametrize("name", ["vit_b", "seg", "long"])
+def test_dense_attention_full_size_sampled(name, lib):
+    """The comparator on whole workloads (the launches bench.py --dense times),
+    checked on sampled queries of two slices (each query row is independent)."""
+    import oracle
+    w = W[name]
+    say(f"[dense-full] {name}: generating")
+    Q, K, V = synth.make_inputs(w)
+    Qd, Kd, Vd = (to_device(x, w.dtype) for x in (Q, K, V))
+    say(f"[dense-full] {name}: kernel")
+    O = lib.dense_attention(Qd, Kd, Vd)
+    torch.cuda.synchronize()
+    O = out_to_f64(O).reshape(-1, w.N, w.d)
+    del Qd, Kd, Vd
+    rng = np.random.default_rng(2)
+    for z in (0, w.slices - 1):
+        qsel = np.sort(rng.choice(w.N, size=128, replace=False))
+        q64, k64, v64 = (slice_f64(x, w.dtype, z) for x in (Q, K, V))
+        ref = oracle.full_attention(q64[qsel], k64, v64)
+        err = np.abs(O[z][qsel] - ref).max()
+        say(f"  slice {z}: max abs error {err:.3g}")
+        assert err <= TOL_OUT[w.dtype], f"slice {z}: max abs error {err:.3g}"

@@ -301,6 +301,64 @@ def test_validity_rule():
     assert not oracle.valid_topk_sets(S, np.array([[0, 1, 1]]), 3)[0]   # duplicate
 
 
+# ---------------------------------------------------------------- margins
+# The margin decides which rows must equal the oracle's set exactly (relative
+# gap between the k-th and (k+1)-th largest score at least 1e-6). Hand-worked
+# values: the row's scores sorted by hand, the gap divided by |k-th score|.
+
+def test_topk_margins_hand_worked():
+    S = np.array([
+        [5.0, 3.0, 3.000001, 1.0],   # sorted 5, 3.000001, 3, 1: k = 2 -> 1e-6 / 3.000001
+        [1.0, 2.0, 0.0, 1.0],        # sorted 2, 1, 1, 0: exact tie at the cut, 0
+        [-1.0, -4.0, -2.0, -8.0],    # negative k-th score: (-2 - (-4)) / |-2| = 1
+        [0.0, 7.0, -1.0, -3.0],      # sorted 7, 0, -1, -3: k-th score 0, gap 1 / 1e-300 (finite)
+    ])
+    got = oracle.topk_margins(S, 2)
+    assert got[0] == pytest.approx(1e-6 / 3.000001, rel=1e-9)
+    assert got[1] == 0.0
+    assert got[2] == 1.0
+    assert got[3] == pytest.approx(1.0 / 1e-300, rel=1e-12)
+    # k = 1 uses the largest and second largest; k = 3 the third and fourth
+    np.testing.assert_allclose(oracle.topk_margins(S[:1], 1), [(5.0 - 3.000001) / 5.0], rtol=1e-14)
+    np.testing.assert_allclose(oracle.topk_margins(S[:1], 3), [(3.0 - 1.0) / 3.0], rtol=1e-14)
+
+
+def test_topk_margins_k_equals_n_is_inf():
+    S = rand((3, 5), 11)
+    assert np.isinf(oracle.topk_margins(S, 5)).all()
+    assert np.isfinite(oracle.topk_margins(S, 4)).all()
+
+
+def test_route_margins_hand_worked():
+    # router row q . q~_i = [0.5, 2.0, 1.0, 1.5]: s = 2 -> (1.5 - 1.0) / 1.5; s = 1 -> (2 - 1.5) / 2
+    R = np.array([[0.5, 2.0, 1.0, 1.5], [1.0, 1.0, 1.0, 1.0]])
+    np.testing.assert_allclose(oracle.route_margins(R, 2), [1.0 / 3.0, 0.0], rtol=1e-14)
+    np.testing.assert_allclose(oracle.route_margins(R, 1), [0.25, 0.0], rtol=1e-14)
+    assert np.isinf(oracle.route_margins(R, 4)).all()
+
+
+def test_margins_brute_force_random_rows():
+    # pure-Python sort of each row, gap taken by the definition
+    S = rand((20, 13), 12)
+    S[3, 5] = S[3, 7]   # one exact tie
+    for k in (1, 4, 12):
+        got = oracle.topk_margins(S, k)
+        for i, row in enumerate(S.tolist()):
+            srt = sorted(row, reverse=True)
+            want = (srt[k - 1] - srt[k]) / max(abs(srt[k - 1]), 1e-300)
+            assert got[i] == pytest.approx(want, rel=1e-13, abs=0.0)
+
+
+def test_margins_agree_with_validity_rule():
+    # a row with margin >= 1e-6 admits exactly one valid set (the oracle's); a row
+    # below it admits a swap across the cut
+    S = np.array([[4.0, 3.0, 3.0 * (1 - 1e-7), 1.0], [4.0, 3.0, 2.0, 1.0]])
+    marg = oracle.topk_margins(S, 2)
+    assert marg[0] < 1e-6 <= marg[1]
+    assert oracle.valid_topk_sets(S[:1], np.array([[0, 2]]), 2)[0]
+    assert not oracle.valid_topk_sets(S[1:], np.array([[0, 2]]), 2)[0]
+
+
 # ---------------------------------------------------------------- generator
 
 def test_generator_is_deterministic_and_sliceable():

@@ -145,3 +145,43 @@ def test_full_attention_mutant_harness_is_faithful(monkeypatch):
     # the unmutated rewrite passes every pin, so a failure above is the mutation's
     _patch(monkeypatch, "full_attention", _full_attention_mutant())
     assert not _fails(*FULL_PINS)
+
+
+MARGIN_PINS = (pins.test_topk_margins_hand_worked, pins.test_topk_margins_k_equals_n_is_inf,
+               pins.test_route_margins_hand_worked, pins.test_margins_brute_force_random_rows)
+
+
+def _margins_mutant(kind):
+    def topk_margins(S, k):
+        S = np.asarray(S, np.float64)
+        N = S.shape[1]
+        if kind == "zeros":
+            return np.zeros(S.shape[0])
+        if k >= N:
+            return np.full(S.shape[0], np.inf)
+        srt = -np.sort(-S, axis=1)
+        if kind == "off_by_one":   # (k+1)-th and (k+2)-th instead of k-th and (k+1)-th
+            a, b = srt[:, k], srt[:, min(k + 1, N - 1)]
+        else:
+            a, b = srt[:, k - 1], srt[:, k]
+        if kind == "absolute":
+            return a - b
+        if kind == "wrong_denominator":   # divided by the (k+1)-th score
+            return (a - b) / np.maximum(np.abs(b), 1e-300)
+        return (a - b) / np.maximum(np.abs(a), 1e-300)
+    return topk_margins
+
+
+@pytest.mark.parametrize("kind", ["off_by_one", "absolute", "wrong_denominator", "zeros"])
+def test_mutant_margins(monkeypatch, kind):
+    fn = _margins_mutant(kind)
+    _patch(monkeypatch, "topk_margins", fn)
+    _patch(monkeypatch, "route_margins", lambda R, s: fn(R, s))
+    assert _fails(*MARGIN_PINS)
+
+
+def test_margins_mutant_harness_is_faithful(monkeypatch):
+    fn = _margins_mutant("faithful")
+    _patch(monkeypatch, "topk_margins", fn)
+    _patch(monkeypatch, "route_margins", lambda R, s: fn(R, s))
+    assert not _fails(*MARGIN_PINS)

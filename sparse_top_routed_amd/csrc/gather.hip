@@ -745,29 +745,21 @@ static hipError_t gather_launch(const Plan& p, const void* Q, const void* K, con
   hipError_t e = hipSuccess;
   const float sl2e = (float)(1.4426950408889634 / sqrt((double)D));
   const void* vtop = p.dtype == MITA_BF16 ? (const void*)(ws + p.ws.vt16) : (const void*)(ws + p.ws.vt32);
-  static int n_cu = 0, occ_f = 0, occ_p = 0;
-  if (n_cu == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      n_cu = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_f, gather_kernel<T, D, true>, 256, 0) != hipSuccess) occ_f = 1;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_p, gather_kernel<T, D, false>, 256, 0) != hipSuccess) occ_p = 1;
-  }
+  static PerDevice c_f, c_p, c_1;
+  const int n_cu = device_cu_count();
   // persistent grid: one resident workgroup per slot, in groups of gs on one XCD,
   // each group walking a contiguous run of the tile table
   const long total = (long)p.max_tiles * p.BH;
-  const int slots = n_cu * std::max(1, p.s == 1 ? occ_f : occ_p);
+  const int slots = n_cu * (p.s == 1 ? resident_per_cu(c_f, gather_kernel<T, D, true>, 256)
+                                     : resident_per_cu(c_p, gather_kernel<T, D, false>, 256));
   const int gsz = std::max(1, std::min(8, slots / 8));
   const int grid = std::max(8 * gsz, slots / (8 * gsz) * 8 * gsz);
   const long gchunk = (total + grid / gsz - 1) / (grid / gsz);
   // the one-pass kernel where its double-buffered LDS fits a workgroup
   constexpr bool one_pass_fits = sizeof(Gather1Lds<T, D>) <= 160 * 1024;
   if constexpr (one_pass_fits) if (p.s == 1 && p.k <= kKeyBlock && p.m <= kKeyBlock) {
-    static int occ1 = 0;
-    if (occ1 == 0 && hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ1, gather1_kernel<T, D>, 256, 0) != hipSuccess)
-      occ1 = 1;
     // resident workgroups in groups of up to 16 per XCD-slice (a multiple of 8 x gs)
-    const int slots = n_cu * std::max(1, occ1);
+    const int slots = n_cu * resident_per_cu(c_1, gather1_kernel<T, D>, 256);
     const int gs = std::max(1, std::min(8, slots / 8));
     const int g1 = std::max(8 * gs, slots / (8 * gs) * 8 * gs);
     hipLaunchKernelGGL((gather1_kernel<T, D>), dim3(g1), dim3(256), 0, st, (const T*)Q, (const T*)K, (const T*)V,

@@ -19,7 +19,18 @@ static void set_error(const char* msg) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-mita_status make_plan(const mita_shape* shape, int m, int k, int s, Plan* p, const char** err) {
+int device_cu_count() {
+  static PerDevice cus;
+  return cus.get([] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    return n;
+  });
+}
+
+mita_status make_plan(const mita_shape* shape, int m, int k, int s, Plan* p, const char** err, bool compact) {
   *err = "";
   if (!shape) { *err = "shape is NULL"; return MITA_ERR_INVALID_ARG; }
   const mita_shape& sh = *shape;
@@ -113,8 +124,9 @@ mita_status make_plan(const mita_shape* shape, int m, int k, int s, Plan* p, con
   L.ccnt = take(bh * m * P.nsplit * 4);
   L.glist = take((bh * m + 1) * 4);
   // fallback rows: one fp64 score row of scratch per wave, ~64 MiB in all
-  P.gwaves = (int)std::min<int64_t>(kTopkGeneralWavesMax,
-                                    std::max<int64_t>(kTopkGeneralWaves, ((int64_t)64 << 20) / ((int64_t)N * 8)));
+  P.gwaves = compact ? kTopkGeneralWaves
+                     : (int)std::min<int64_t>(kTopkGeneralWavesMax,
+                                              std::max<int64_t>(kTopkGeneralWaves, ((int64_t)64 << 20) / ((int64_t)N * 8)));
   L.gscr = take((size_t)P.gwaves * N * 8);
   L.I = take(bh * m * (size_t)k * 4);
   L.E = take(bh * N * s * 4);
@@ -168,9 +180,19 @@ mita_status hip_status(hipError_t e, const char* where) {
   return MITA_ERR_HIP;
 }
 
+// Optional copy-out pointer: NULL, or 8-byte aligned (checked before any launch).
+mita_status check_out(const void* p, const char* name) {
+  static thread_local char buf[128];
+  if (p && ((uintptr_t)p & 7) != 0) {
+    snprintf(buf, sizeof buf, "%s must be 8-byte aligned", name);
+    set_error(buf);
+    return MITA_ERR_INVALID_ARG;
+  }
+  return MITA_OK;
+}
+
 mita_status copy_out(void* dst, const void* src, size_t bytes, hipStream_t st, const char* what) {
   if (!dst) return MITA_OK;
-  if (((uintptr_t)dst & 7) != 0) { set_error("output pointer must be 8-byte aligned"); return MITA_ERR_INVALID_ARG; }
   return hip_status(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st), what);
 }
 
@@ -203,7 +225,7 @@ mita_status mita_pool(const void* Q, int m, int k, int s, const mita_shape* shap
   Plan P;
   mita_status st = check_common(shape, m, k, s, workspace, workspace_bytes, &P);
   if (st != MITA_OK) return st;
-  if ((st = check_ptr(Q, "Q")) != MITA_OK) return st;
+  if ((st = check_ptr(Q, "Q")) != MITA_OK || (st = check_out(Qt_out, "Qt_out")) != MITA_OK) return st;
   hipStream_t hs = (hipStream_t)stream;
   char* ws = (char*)workspace;
   if ((st = hip_status(launch_pool(P, Q, ws, hs), "pool")) != MITA_OK) return st;
@@ -215,7 +237,9 @@ mita_status mita_landmark(const void* K, const void* V, int m, int k, int s, con
   Plan P;
   mita_status st = check_common(shape, m, k, s, workspace, workspace_bytes, &P);
   if (st != MITA_OK) return st;
-  if ((st = check_ptr(K, "K")) != MITA_OK || (st = check_ptr(V, "V")) != MITA_OK) return st;
+  if ((st = check_ptr(K, "K")) != MITA_OK || (st = check_ptr(V, "V")) != MITA_OK ||
+      (st = check_out(Vt_out, "Vt_out")) != MITA_OK)
+    return st;
   hipStream_t hs = (hipStream_t)stream;
   char* ws = (char*)workspace;
   if (S_out && ((uintptr_t)S_out & 15) != 0) { set_error("S_out must be 16-byte aligned"); return MITA_ERR_INVALID_ARG; }
@@ -228,7 +252,7 @@ mita_status mita_topk(const void* K, int m, int k, int s, const mita_shape* shap
   Plan P;
   mita_status st = check_common(shape, m, k, s, workspace, workspace_bytes, &P);
   if (st != MITA_OK) return st;
-  if ((st = check_ptr(K, "K")) != MITA_OK) return st;
+  if ((st = check_ptr(K, "K")) != MITA_OK || (st = check_out(I_out, "I_out")) != MITA_OK) return st;
   hipStream_t hs = (hipStream_t)stream;
   char* ws = (char*)workspace;
   if ((st = hip_status(launch_topk(P, K, ws, hs), "topk")) != MITA_OK) return st;
@@ -240,7 +264,7 @@ mita_status mita_route(const void* Q, int m, int k, int s, const mita_shape* sha
   Plan P;
   mita_status st = check_common(shape, m, k, s, workspace, workspace_bytes, &P);
   if (st != MITA_OK) return st;
-  if ((st = check_ptr(Q, "Q")) != MITA_OK) return st;
+  if ((st = check_ptr(Q, "Q")) != MITA_OK || (st = check_out(E_out, "E_out")) != MITA_OK) return st;
   hipStream_t hs = (hipStream_t)stream;
   char* ws = (char*)workspace;
   if ((st = hip_status(launch_clear(P, ws, hs), "clear")) != MITA_OK) return st;
@@ -268,6 +292,26 @@ namespace {
 // first forward call on that device, so that routing (which needs only step 1)
 // runs concurrently with steps 2 and 3. The mutex keeps each call's fork and
 // join together when several host threads share the device.
+// Keeps the first failing HIP call of a sequence and its message.
+struct FirstError {
+  mita_status st = MITA_OK;
+  char msg[512] = "";
+  bool ok() const { return st == MITA_OK; }
+  // Returns whether `e` succeeded.
+  bool add(hipError_t e, const char* where) {
+    if (e == hipSuccess) return true;
+    if (st == MITA_OK) {
+      st = MITA_ERR_HIP;
+      snprintf(msg, sizeof msg, "%s: %s", where, hipGetErrorString(e));
+    }
+    return false;
+  }
+  mita_status finish() const {
+    if (st != MITA_OK) set_error(msg);
+    return st;
+  }
+};
+
 struct SideStream {
   std::mutex mu;
   hipStream_t stream = nullptr;
@@ -315,15 +359,20 @@ mita_status mita_forward(const void* Q, const void* K, const void* V, int m, int
   // fork: routing (+ bucketing) on the side stream, steps 2-3 on the caller's
   if ((st = hip_status(hipEventRecord(sd->fork, hs), "fork")) != MITA_OK) return st;
   if ((st = hip_status(hipStreamWaitEvent(rs, sd->fork, 0), "fork wait")) != MITA_OK) return st;
-  if ((st = hip_status(launch_clear(P, ws, rs), "clear")) != MITA_OK) return st;
-  if ((st = hip_status(launch_route(P, Q, ws, rs), "route")) != MITA_OK) return st;
-  if ((st = hip_status(launch_bucket(P, ws, rs), "bucket")) != MITA_OK) return st;
-  if ((st = hip_status(hipEventRecord(sd->join, rs), "join")) != MITA_OK) return st;
-  if ((st = hip_status(launch_landmark(P, K, V, ws, nullptr, hs), "landmark")) != MITA_OK) return st;
-  if ((st = hip_status(launch_topk(P, K, ws, hs), "topk")) != MITA_OK) return st;
+  // From here the side stream depends on the caller's: every path joins it back
+  // (also after a failed launch, so a graph being captured is never left forked).
+  // The first failure is the one reported.
+  FirstError fe;
+  fe.add(launch_clear(P, ws, rs), "clear");
+  if (fe.ok()) fe.add(launch_route(P, Q, ws, rs), "route");
+  if (fe.ok()) fe.add(launch_bucket(P, ws, rs), "bucket");
+  const bool joined = fe.add(hipEventRecord(sd->join, rs), "join");
+  if (fe.ok()) fe.add(launch_landmark(P, K, V, ws, nullptr, hs), "landmark");
+  if (fe.ok()) fe.add(launch_topk(P, K, ws, hs), "topk");
   // join: the output step needs both branches
-  if ((st = hip_status(hipStreamWaitEvent(hs, sd->join, 0), "join wait")) != MITA_OK) return st;
-  return hip_status(launch_gather(P, Q, K, V, out, ws, hs), "gather");
+  if (joined) fe.add(hipStreamWaitEvent(hs, sd->join, 0), "join wait");
+  if (fe.ok()) fe.add(launch_gather(P, Q, K, V, out, ws, hs), "gather");
+  return fe.finish();
 }
 
 mita_status mita_dense_attention(const void* Q, const void* K, const void* V, void* out, const mita_shape* shape,

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/mita.h"
 
 namespace mita {
@@ -73,9 +75,41 @@ struct Plan {
   Layout ws;
 };
 
+// A value per device, computed once on first use with that device current;
+// safe when several host threads launch at once.
+struct PerDevice {
+  static constexpr int kMax = 64;
+  std::once_flag once[kMax];
+  int val[kMax] = {};
+  template <class F>
+  int get(F&& f) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMax) return f();
+    std::call_once(once[dev], [&] { val[dev] = f(); });
+    return val[dev];
+  }
+};
+
+// Compute units of the current device (cached per device; 256 if the query fails).
+int device_cu_count();
+
+// Workgroups of `threads` threads (no dynamic LDS) of `kern` resident per CU on the
+// current device, at least 1; `cache` holds the answer per device.
+template <typename Kern>
+int resident_per_cu(PerDevice& cache, Kern kern, int threads) {
+  return cache.get([&] {
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, threads, 0) != hipSuccess || occ < 1) occ = 1;
+    return occ;
+  });
+}
+
 // Validate arguments and build the plan. Returns MITA_OK or a negative status and
 // fills `err` (static storage) with the reason.
-mita_status make_plan(const mita_shape* shape, int m, int k, int s, Plan* p, const char** err);
+// `compact`: the exact top-k fallback gets its fewest waves (kTopkGeneralWaves), so
+// the workspace is as small as it can be (the fixed-scratch entry point uses it).
+mita_status make_plan(const mita_shape* shape, int m, int k, int s, Plan* p, const char** err,
+                      bool compact = false);
 
 // Kernel launchers (one per step; each returns the first HIP error it meets).
 hipError_t launch_clear(const Plan& p, char* ws, hipStream_t st);

@@ -572,16 +572,8 @@ static hipError_t route_fast_launch(const Plan& p, const void* Q, char* ws, hipS
   if constexpr (RES) {
     // several query tiles per workgroup (the landmarks stay staged), as many as
     // make the grid one round of resident workgroups
-    static int slots = 0;
-    if (slots == 0) {
-      int dev = 0, n_cu = 256, occ = 1;
-      if (hipGetDevice(&dev) != hipSuccess ||
-          hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        n_cu = 256;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, route_fast_kernel<T, D, TM>, 256, 0) != hipSuccess)
-        occ = 1;
-      slots = n_cu * std::max(1, occ);
-    }
+    static PerDevice occ;
+    const int slots = device_cu_count() * resident_per_cu(occ, route_fast_kernel<T, D, TM>, 256);
     const int per_slice = std::max(1, slots / p.BH);
     const int tpw = (p.qtiles + per_slice - 1) / per_slice;
     hipLaunchKernelGGL((route_fast_kernel<T, D, TM>), dim3((p.qtiles + tpw - 1) / tpw, p.BH), dim3(256), 0,

@@ -17,5 +17,9 @@ from .mita_oracle import (  # noqa: F401
     forward,
     topk_margins,
     route_margins,
+    pool_matrix,
+    attend_backward,
+    shared_expert_backward,
+    backward,
 )
 from .validity import valid_topk_sets, valid_route_sets  # noqa: F401

@@ -176,3 +176,86 @@ def forward(Q, K, V, grid_h: int, grid_w: int, pool_h: int, pool_w: int, k: int,
         E[list(queries)] = E_part
     O = attend(Q, K, V, Qt, Vt, I, E, queries)
     return {"Qt": Qt, "S": S, "Vt": Vt, "I": I, "E": E, "O": O, "R": R}
+
+
+# ---------------------------------------------------------------- backward
+# Gradients of the forward pass above with respect to Q, K and V, the expert sets
+# I and the routing E held fixed (they are selections, not differentiable). The
+# Long Range Arena training result on the MiTA pages (Arabic/Hindi section 4,
+# Dutch "Resultaten") implies training through this operator; the pages give no
+# backward, so this is the derivative of the forward as defined, by the chain
+# rule, written out step by step.
+
+def pool_matrix(N: int, grid_h: int, grid_w: int, pool_h: int, pool_w: int) -> np.ndarray:
+    """The pooling as a matrix P [m, N]: Q~ = P Q, row i holding 1/|window i| on
+    the window's tokens (the landmark construction of the method sections)."""
+    P = np.zeros((pool_h * pool_w, N), dtype=np.float64)
+    for a, (r0, r1) in enumerate(adaptive_windows(grid_h, pool_h)):
+        for b, (c0, c1) in enumerate(adaptive_windows(grid_w, pool_w)):
+            toks = [r * grid_w + c for r in range(r0, r1) for c in range(c0, c1)]
+            P[a * pool_w + b, toks] = 1.0 / len(toks)
+    return P
+
+
+def attend_backward(Q, K, V, Qt, Vt, I, E, dO):
+    """Backward of `attend` (the final attention over [Q~, K^(e_1(q)), ...] with
+    values [V~, V^(e_1(q)), ...], Dutch "Wiskundige Formulering"): for each query,
+    with p its attention weights and O its output, dp_j = dO . v*_j, the logit
+    gradient is p_j (dp_j - dO . O), and it flows to q (times k*_j / sqrt d), to
+    each key k*_j (times q / sqrt d) and, through p, to each value v*_j (p_j dO).
+    A token present in two of the query's experts receives both contributions.
+    Returns dQ (direct part), dK, dV (routed part), dQt, dVt."""
+    Q, K, V, Qt, Vt, dO = (np.asarray(x, np.float64) for x in (Q, K, V, Qt, Vt, dO))
+    N, d = Q.shape
+    m = Qt.shape[0]
+    sc = 1.0 / math.sqrt(d)
+    dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    dQt, dVt = np.zeros_like(Qt), np.zeros_like(Vt)
+    for q in range(N):
+        toks = np.concatenate([np.asarray(I[e], dtype=np.int64) for e in E[q]])
+        Ks = np.concatenate([Qt, K[toks]], axis=0)
+        Vs = np.concatenate([Vt, V[toks]], axis=0)
+        logits = (Ks @ Q[q]) * sc
+        p = np.exp(logits - logits.max())
+        p /= p.sum()
+        O = p @ Vs
+        dp = Vs @ dO[q]
+        dl = p * (dp - dO[q] @ O)
+        dQ[q] += (dl @ Ks) * sc
+        dKs = np.outer(dl, Q[q]) * sc
+        dVs = np.outer(p, dO[q])
+        dQt += dKs[:m]
+        dVt += dVs[:m]
+        np.add.at(dK, toks, dKs[m:])
+        np.add.at(dV, toks, dVs[m:])
+    return dQ, dK, dV, dQt, dVt
+
+
+def shared_expert_backward(Qt, K, V, dVt):
+    """Backward of V~ = softmax(Q~ K^T / sqrt d) V (the shared expert, Arabic/Hindi
+    section 2): with A the weights, dA = dV~ V^T, the score gradient is
+    A (dA - rowsum(A dA)), and it flows to Q~ (times K / sqrt d) and to K (times
+    Q~ / sqrt d); V gets A^T dV~. Returns dQt, dK, dV."""
+    Qt, K, V, dVt = (np.asarray(x, np.float64) for x in (Qt, K, V, dVt))
+    d = Qt.shape[1]
+    sc = 1.0 / math.sqrt(d)
+    A = _softmax_rows(scores(Qt, K) * sc)
+    dA = dVt @ V.T
+    dS = A * (dA - (A * dA).sum(axis=1, keepdims=True))
+    return (dS @ K) * sc, (dS.T @ Qt) * sc, A.T @ dVt
+
+
+def backward(Q, K, V, grid_h: int, grid_w: int, pool_h: int, pool_w: int, I, E, dO) -> Dict[str, np.ndarray]:
+    """Gradients (dQ, dK, dV) of sum(dO * O) for the forward pass on one slice, with
+    the expert sets I and routing E held fixed. Chain: the final attention, then
+    the shared expert (its V~ feeds the final attention; Q~ is both its query and
+    a key of the final attention), then the pooling (dQ += P^T dQ~)."""
+    Q, K, V = (np.asarray(x, np.float64) for x in (Q, K, V))
+    N = Q.shape[0]
+    Qt = pool(Q, grid_h, grid_w, pool_h, pool_w)
+    Vt = shared_expert(Qt, K, V)
+    dQ, dK, dV, dQt, dVt = attend_backward(Q, K, V, Qt, Vt, I, E, dO)
+    dQt2, dK2, dV2 = shared_expert_backward(Qt, K, V, dVt)
+    dQt = dQt + dQt2
+    dQ = dQ + pool_matrix(N, grid_h, grid_w, pool_h, pool_w).T @ dQt
+    return {"dQ": dQ, "dK": dK + dK2, "dV": dV + dV2, "dQt": dQt, "dVt": dVt}

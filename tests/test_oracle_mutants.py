@@ -185,3 +185,65 @@ def test_margins_mutant_harness_is_faithful(monkeypatch):
     _patch(monkeypatch, "topk_margins", fn)
     _patch(monkeypatch, "route_margins", lambda R, s: fn(R, s))
     assert not _fails(*MARGIN_PINS)
+
+
+# ---------------------------------------------------------------- backward
+import test_oracle_backward as bpins
+
+BACKWARD_PINS = (lambda: bpins.test_backward_matches_finite_differences(bpins.CASES[0]),
+                 lambda: bpins.test_backward_matches_finite_differences(bpins.CASES[1]),
+                 lambda: bpins.test_backward_matches_torch_autograd(bpins.CASES[1]),
+                 bpins.test_value_gradient_mass_is_sum_of_output_gradients)
+
+
+def _attend_backward_mutant(kind):
+    def attend_backward(Q, K, V, Qt, Vt, I, E, dO):
+        Q, K, V, Qt, Vt, dO = (np.asarray(x, np.float64) for x in (Q, K, V, Qt, Vt, dO))
+        N, d = Q.shape
+        m = Qt.shape[0]
+        sc = 1.0 / math.sqrt(d)
+        dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+        dQt, dVt = np.zeros_like(Qt), np.zeros_like(Vt)
+        for q in range(N):
+            toks = np.concatenate([np.asarray(I[e], dtype=np.int64) for e in E[q]])
+            Ks = np.concatenate([Qt, K[toks]], axis=0)
+            Vs = np.concatenate([Vt, V[toks]], axis=0)
+            lg = (Ks @ Q[q]) * sc
+            p = np.exp(lg - lg.max())
+            p /= p.sum()
+            O = p @ Vs
+            dp = Vs @ dO[q]
+            dl = p * (dO[q] @ O - dp) if kind == "sign" else p * (dp - dO[q] @ O)
+            dQ[q] += (dl @ Ks) * (1.0 if kind == "dq_unscaled" else sc)
+            dKs, dVs = np.outer(dl, Q[q]) * sc, np.outer(p, dO[q])
+            dQt += dKs[:m]
+            dVt += dVs[:m]
+            if kind == "duplicates_dropped":   # fancy-index += keeps one contribution per token
+                dK[toks] += dKs[m:]
+                dV[toks] += dVs[m:]
+            else:
+                np.add.at(dK, toks, dKs[m:])
+                np.add.at(dV, toks, dVs[m:])
+        return dQ, dK, dV, dQt, dVt
+    return attend_backward
+
+
+@pytest.mark.parametrize("kind", ["sign", "dq_unscaled", "duplicates_dropped"])
+def test_mutant_attend_backward(monkeypatch, kind):
+    monkeypatch.setattr(mo, "attend_backward", _attend_backward_mutant(kind))
+    assert _fails(*BACKWARD_PINS)
+
+
+def test_mutant_backward_without_shared_expert_path(monkeypatch):
+    monkeypatch.setattr(mo, "shared_expert_backward", lambda Qt, K, V, dVt: (0 * Qt, 0 * K, 0 * V))
+    assert _fails(*BACKWARD_PINS)
+
+
+def test_mutant_backward_without_pooling_path(monkeypatch):
+    monkeypatch.setattr(mo, "pool_matrix", lambda N, gh, gw, ph, pw: np.zeros((ph * pw, N)))
+    assert _fails(*BACKWARD_PINS)
+
+
+def test_backward_mutant_harness_is_faithful(monkeypatch):
+    monkeypatch.setattr(mo, "attend_backward", _attend_backward_mutant("faithful"))
+    assert not _fails(*BACKWARD_PINS)

@@ -1,11 +1,14 @@
 """MiTA attention forward throughput on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload vit_b]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload very_long]
 
 Prints one JSON line: query-tokens/s of the whole forward pass (B*H*N per call)
-on seeded synthetic inputs resident in HBM, the roofline position of the
-dominant kernel (timed live with HIP events on the library's stream) and the
-fp64 CPU oracle timed on a bounded sample of the same workload.
+on seeded synthetic inputs resident in HBM (default: the very long sequence,
+B=1, H=8, N=262144, d=128, m=512, k=512, s=4, bf16), the roofline position of
+the dominant kernel (timed live with HIP events on the library's stream; MFMA
+fraction against the bf16 dense peak and HBM fraction beside it), the MFMA and
+HBM fractions of every step, and the fp64 CPU oracle timed on the host's cores
+over a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -23,14 +26,23 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
 
+def _fused(w) -> bool:
+    """Whether the routed-expert kernel also attends the landmark pairs and writes
+    the output (s = 1 with m <= 64), so that the combine step launches nothing."""
+    return w.s == 1 and w.m <= 64
+
+
 def step_bytes(w) -> dict:
     """Algorithmic HBM bytes per forward call, by step (each input or
     intermediate counted once per step that must read or write it)."""
     e = 2 if w.dtype == "bf16" else 4
+    ep = 2 if w.dtype == "bf16" else 4   # partial outputs: fp16 for bf16 inputs, else fp32
     BH, N, d, m, k, s = w.slices, w.N, w.d, w.m, w.k, w.s
     tok = BH * N * d * e
     nblk = -(-N // 64)
     nbg = nblk * (1 if nblk >= 4 * k else (4 if 4 * nblk >= k else 16))   # group maxima per row (64, 16 or 4 scores)
+    partials = BH * N * s * (d * ep + 16)
+    fused = _fused(w)
     return {
         "pool": tok + BH * m * d * (8 + 4 + 4),
         # K and V read once, group maxima of the score rows written once
@@ -38,11 +50,26 @@ def step_bytes(w) -> dict:
         # group maxima read, K read once more (candidate pass), expert lists written
         "topk": BH * m * nbg * 4 + tok + BH * m * k * 4,
         "route": tok + BH * N * s * 4,
-        # Q read, each expert's k gathered K/V rows once, output written, + the per-slot partials
-        # written and read back when s > 1 or m > 64 (d values in 16 bits for bf16, else 32, and
-        # 16 bytes of (max, sum, scale))
-        "gather": 2 * tok + BH * m * k * d * e * 2
-        + (BH * N * s * (d * e + 16) * 2 if (s > 1 or m > 64) else 0),
+        # each query row read once per routed slot, each expert's k gathered K/V rows once, and the
+        # output (fused) or the per-slot partials written
+        "gather": BH * N * s * d * e + BH * m * k * d * e * 2 + (tok if fused else partials),
+        # query rows and the partials read, the output written (the landmark pairs are m rows)
+        "combine": 0 if fused else 2 * tok + partials,
+    }
+
+
+def step_flops(w) -> dict:
+    """Algorithmic MFMA flops per forward call, by step (2 per multiply-add; the
+    bf16 hi + lo split of Q~ that keeps scores fp32-accurate is not counted)."""
+    BH, N, d, m, k, s = w.slices, w.N, w.d, w.m, w.k, w.s
+    fused = _fused(w)
+    return {
+        "pool": 0,
+        "landmark": 4 * BH * m * N * d,            # Q~ K^T and P V
+        "topk": 2 * BH * m * N * d,                # Q~ K^T again (candidate pass)
+        "route": 2 * BH * N * m * d,               # Q Q~^T
+        "gather": 4 * BH * N * k * s * d + (4 * BH * N * m * d if fused else 0),
+        "combine": 0 if fused else 4 * BH * N * m * d,
     }
 
 
@@ -51,6 +78,7 @@ def step_bytes(w) -> dict:
 # was measured on.
 KERNEL_SOURCES = {
     "gather": ["sparse_top_routed_amd/csrc/gather.hip", "sparse_top_routed_amd/csrc/attn_core.h"],
+    "combine": ["sparse_top_routed_amd/csrc/gather.hip", "sparse_top_routed_amd/csrc/attn_core.h"],
     "topk": ["sparse_top_routed_amd/csrc/topk.hip", "sparse_top_routed_amd/csrc/attn_core.h"],
     "route": ["sparse_top_routed_amd/csrc/route.hip", "sparse_top_routed_amd/csrc/attn_core.h"],
     "landmark": ["sparse_top_routed_amd/csrc/landmark.hip", "sparse_top_routed_amd/csrc/attn_core.h"],
@@ -58,10 +86,18 @@ KERNEL_SOURCES = {
 }
 COMMON_SOURCES = ["sparse_top_routed_amd/csrc/common.h", "sparse_top_routed_amd/csrc/plan.h",
                   "sparse_top_routed_amd/build.py"]
-KERNEL_NAMES = {
-    "gather": "gather1_kernel", "topk": "topk_cand_kernel", "route": "route_fast_kernel",
-    "landmark": "landmark_kernel", "pool": "pool_kernel",
-}
+STEPS = ["pool", "landmark", "topk", "route", "gather", "combine"]
+
+
+def kernel_names(w) -> dict:
+    """The kernel that does each step's arithmetic for this workload."""
+    if _fused(w):
+        gather = "gather1_kernel" if w.k <= 64 else "gather_kernel"
+    else:   # partials: the direct-load kernel for bf16 inputs
+        gather = "gatherd_kernel" if w.dtype == "bf16" else "gather_kernel"
+    return {"pool": "pool_kernel", "landmark": "landmark_kernel", "topk": "topk_cand_kernel",
+            "route": "route_fast_kernel" if w.m <= 64 else "route_multi_kernel", "gather": gather,
+            "combine": "combine_kernel"}
 
 
 def sources_sha256(step: str) -> str:
@@ -95,25 +131,96 @@ def stored_traffic(step: str, workload: str, kernel: str):
         return None
 
 
-def cpu_baseline(w, Q, K, V, budget_s: float = 12.0) -> dict:
-    import numpy as np
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _cpu_worker_init():
     from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)   # one BLAS thread per process: the processes are the parallelism
 
-    import oracle
+
+def _cpu_slice(w, z):
     import synth
+    b, h = divmod(z, w.H)
+    Q, K, V = synth.make_inputs(w, slices=[(b, h)])
+    return tuple(synth.to_f64(x[0], w.dtype) for x in (Q, K, V))
 
-    done, t0 = 0, time.perf_counter()
-    with threadpool_limits(limits=1):
-        for z in range(w.slices):
-            q64, k64, v64 = (synth.to_f64(x.reshape(-1, w.N, w.d)[z], w.dtype) for x in (Q, K, V))
-            oracle.forward(q64, k64, v64, w.grid_h, w.grid_w, w.pool_h, w.pool_w, w.k, w.s)
-            done += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
-    el = time.perf_counter() - t0
-    return {"value": done * w.N / el, "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {w.slices} (batch, head) slices of {w.name}, all {w.N} queries each, "
-                      f"fp64 numpy, BLAS limited to 1 thread, {el:.1f} s"}
+
+def _cpu_fixed(args):
+    """Per-slice part of the oracle (pooling, shared expert, expert sets): its time
+    and the small results the per-query part needs (input generation untimed)."""
+    import oracle
+    w, z = args
+    q64, k64, v64 = _cpu_slice(w, z)
+    t0 = time.perf_counter()
+    Qt = oracle.pool(q64, w.grid_h, w.grid_w, w.pool_h, w.pool_w)
+    S = oracle.scores(Qt, k64)
+    Vt = oracle.shared_expert(Qt, k64, v64)
+    I = oracle.topk_experts(S, w.k)
+    return z, time.perf_counter() - t0, Qt, Vt, I
+
+
+def _cpu_queries(args):
+    """Per-query part of the oracle (routing, output) for a sample of queries."""
+    import numpy as np
+    import oracle
+    w, z, qs, Qt, Vt, I = args
+    q64, k64, v64 = _cpu_slice(w, z)
+    t0 = time.perf_counter()
+    E = np.full((w.N, w.s), -1, dtype=np.int64)
+    E[qs] = oracle.route(q64[qs], Qt, w.s)
+    oracle.attend(q64, k64, v64, Qt, Vt, I, E, qs)
+    return z, len(qs), time.perf_counter() - t0
+
+
+def cpu_baseline(w, workers: int, queries_per_slice: int = 4096) -> dict:
+    """The fp64 oracle as it stands on the host's cores: one single-threaded process
+    per core (at most 16, the CPU share of one GPU on the box). The per-slice part
+    runs whole on up to 2 x workers slices; the per-query part on a sample of
+    queries of each of them, in chunks spread over all workers. Each task is
+    timed inside its process while all processes run (so memory contention is
+    included); the whole-job time is estimated as the summed task times, scaled
+    to all slices and queries, divided by the number of processes (perfect load
+    balance, which favours the CPU)."""
+    import multiprocessing as mp
+
+    import numpy as np
+
+    nslice = min(w.slices, 2 * workers)
+    zs = [int(z) for z in np.linspace(0, w.slices - 1, nslice).round().astype(int)]
+    zs = sorted(set(zs))
+    ctx = mp.get_context("spawn")
+    wall0 = time.perf_counter()
+    with ctx.Pool(workers, initializer=_cpu_worker_init) as pool:
+        fixed = pool.map(_cpu_fixed, [(w, z) for z in zs], chunksize=1)
+        rng = np.random.default_rng(3)
+        tasks = []
+        for z, _, Qt, Vt, I in fixed:
+            qs = np.sort(rng.choice(w.N, size=min(w.N, queries_per_slice), replace=False))
+            for c in np.array_split(qs, max(1, len(qs) // 512)):
+                tasks.append((w, z, c, Qt, Vt, I))
+        per_q = pool.map(_cpu_queries, tasks, chunksize=1)
+    wall = time.perf_counter() - wall0
+    t_fixed = sum(f[1] for f in fixed) / len(fixed)                     # per slice
+    nq = sum(p[1] for p in per_q)
+    t_query = sum(p[2] for p in per_q) / nq                             # per query
+    t_slice = t_fixed + w.N * t_query
+    t_job = w.slices * t_slice / workers
+    nproc = os.cpu_count()
+    return {"value": w.slices * w.N / t_job, "unit": "query-tokens/s", "cores": workers, "kind": "oracle",
+            "cpu_model": _cpu_model(), "nproc": nproc,
+            "sample": f"{w.name}: per-slice part (pool, shared expert, expert sets) whole on {len(zs)} of "
+                      f"{w.slices} slices ({t_fixed:.2f} s each), per-query part (routing, output) on {nq} "
+                      f"sampled queries ({t_query * 1e6:.1f} us each); fp64 numpy, {workers} single-threaded "
+                      f"processes, job time = {w.slices} slices x {t_slice:.2f} s / {workers}; {wall:.1f} s wall"}
 
 
 def step_times(call, Qd, Kd, Vd, out, steps: int) -> dict:
@@ -122,7 +229,7 @@ def step_times(call, Qd, Kd, Vd, out, steps: int) -> dict:
     import torch
 
     st = torch.cuda.current_stream()
-    names = ["pool", "landmark", "topk", "route", "gather"]
+    names = STEPS
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
     acc = dict.fromkeys(names, 0.0)
     for _ in range(steps):
@@ -132,6 +239,7 @@ def step_times(call, Qd, Kd, Vd, out, steps: int) -> dict:
         call.topk(Kd); ev[3].record(st)
         call.route(Qd); ev[4].record(st)
         call.gather(Qd, Kd, Vd, out); ev[5].record(st)
+        call.combine(Qd, out); ev[6].record(st)
         torch.cuda.synchronize()
         for i, n in enumerate(names):
             acc[n] += ev[i].elapsed_time(ev[i + 1])
@@ -208,15 +316,22 @@ def dense_compare(w, Qd, Kd, Vd, steps: int, warmup: int) -> int:
     return 0
 
 
+def _cpu_workers(requested: int) -> int:
+    have = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return max(1, min(requested or have, have, 16))
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    # the GPU reaches its steady clocks only after some tens of ms of work: with 5
-    # warm-up forwards (~3 ms) the timed forwards run ~12 % slower than after 100
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="vit_b")
+    ap.add_argument("--steps", type=int, default=20)
+    # the GPU reaches its steady clocks only after some tens of ms of work (a very long
+    # forward is ~10 ms, so a few warm-up forwards suffice; small workloads need more)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="very_long")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="processes of the CPU baseline (default: the usable cores, at most 16)")
     ap.add_argument("--breakdown", action="store_true", help="print per-step times to stderr")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 3 elementwise copies of 512 MiB (read and write 2^29 bytes each), the "
@@ -231,7 +346,7 @@ def main() -> int:
     a = ap.parse_args()
     if a.print_sha:
         for step in KERNEL_SOURCES:
-            print(step, KERNEL_NAMES[step], sources_sha256(step))
+            print(step, sources_sha256(step))
         return 0
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the MiTA forward here runs on a single MI355X "
@@ -239,12 +354,20 @@ def main() -> int:
         return 2
 
     import numpy as np
-    import torch
 
     import synth
-    from sparse_top_routed_amd import mita
 
     w = synth.WORKLOADS[a.workload]
+    # the CPU baseline runs first, before anything touches the GPU: its worker
+    # processes start from a clean interpreter and never share the GPU timing
+    cpu = None
+    if not (a.no_cpu or a.sweep or a.dense):
+        cpu = cpu_baseline(w, _cpu_workers(a.cpu_workers))
+
+    import torch
+
+    from sparse_top_routed_amd import mita
+
     Q, K, V = synth.make_inputs(w)
 
     def dev(x):
@@ -253,6 +376,7 @@ def main() -> int:
         return torch.from_numpy(x).cuda()
 
     Qd, Kd, Vd = dev(Q), dev(K), dev(V)
+    del Q, K, V
     if a.sweep:
         return sweep(w, Qd, Kd, Vd, a.steps, a.warmup, a.breakdown)
     if a.dense:
@@ -276,20 +400,39 @@ def main() -> int:
     ms = t0.elapsed_time(t1) / a.steps
     tokens = w.slices * w.N
 
-    # per-step times: the same launches as forward, one step entry point at a time
-    names = ["pool", "landmark", "topk", "route", "gather"]
+    # per-step times: the same launches as forward, one step entry point at a time,
+    # events on the stream the library launches on (the current stream)
     per = step_times(call, Qd, Kd, Vd, out, a.steps)
-    nbytes = step_bytes(w)
-    dom = max(per, key=per.get)
-    kname = KERNEL_NAMES[dom]
-    if dom == "gather" and not (w.s == 1 and w.k <= 64 and w.m <= 64):
-        # the one-pass kernel serves s = 1 with k, m <= 64 only
-        kname = "gather_kernel" if w.s == 1 else "gather_kernel+combine_kernel"
-    achieved = nbytes[dom] / (per[dom] * 1e-3) / 1e9
+    nbytes, nflops, names = step_bytes(w), step_flops(w), kernel_names(w)
+    frac = {}
+    for n in STEPS:
+        if per[n] <= 0 or (nflops[n] == 0 and nbytes[n] == 0):
+            continue
+        sec = per[n] * 1e-3
+        frac[n] = {"kernel": names[n], "ms": per[n],
+                   "mfma_frac": nflops[n] / sec / 1e12 / BF16_PEAK_TFLOPS if w.dtype == "bf16" and nflops[n] else None,
+                   "hbm_frac": nbytes[n] / sec / 1e9 / HBM_PEAK_GBS}
+    dom = max((n for n in STEPS if n in frac), key=lambda n: per[n])
+    sec = per[dom] * 1e-3
+    # the binding roof by the roofline model: the larger of flops / peak and bytes / bandwidth
+    t_mfma = nflops[dom] / (BF16_PEAK_TFLOPS * 1e12) if w.dtype == "bf16" else 0.0
+    t_hbm = nbytes[dom] / (HBM_PEAK_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        roof = {"bound": "mfma", "kernel": names[dom], "achieved": nflops[dom] / sec / 1e12,
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": nflops[dom] / sec / 1e12 / BF16_PEAK_TFLOPS}
+    else:
+        roof = {"bound": "hbm", "kernel": names[dom], "achieved": nbytes[dom] / sec / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": nbytes[dom] / sec / 1e9 / HBM_PEAK_GBS}
+    roof.update({"traffic": stored_traffic(dom, w.name, names[dom]), "algorithmic_flops": nflops[dom],
+                 "algorithmic_bytes": nbytes[dom], "hbm_frac": nbytes[dom] / sec / 1e9 / HBM_PEAK_GBS,
+                 "ms": per[dom]})
     if a.breakdown:
-        for n in names:
-            print(f"{n:9s} {per[n] * 1e3:9.1f} us  {nbytes[n] / (per[n] * 1e-3) / 1e9:8.1f} GB/s (algorithmic)",
-                  file=sys.stderr)
+        for n in STEPS:
+            if n in frac:
+                f = frac[n]
+                mf = f"{f['mfma_frac'] * 100:5.1f} % MFMA" if f["mfma_frac"] is not None else " " * 12
+                print(f"{n:9s} {per[n] * 1e3:9.1f} us  {mf}  {f['hbm_frac'] * 100:5.1f} % HBM  ({f['kernel']})",
+                      file=sys.stderr)
         print(f"forward  {ms * 1e3:9.1f} us  wall {wall / a.steps * 1e6:9.1f} us", file=sys.stderr)
     if a.copy_calibration:
         src = torch.ones(1 << 27, dtype=torch.float32, device="cuda")
@@ -305,13 +448,11 @@ def main() -> int:
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "m": w.m, "k": w.k, "s": w.s,
                    "grid": [w.grid_h, w.grid_w], "pool": [w.pool_h, w.pool_w]},
-        "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": stored_traffic(dom, w.name, kname), "algorithmic_bytes": nbytes[dom]},
-        "step_ms": per,
+        "roofline": roof,
+        "steps_roofline": frac,
     }
-    if not a.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(w, Q, K, V)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res))
     return 0
 

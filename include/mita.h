@@ -75,8 +75,8 @@ size_t mita_workspace_bytes(const mita_shape* shape, int m, int k, int s);
  * k tokens and s routed experts per query. Requires 1 <= m <= N, 1 <= k <= N,
  * 1 <= s <= m. `out` has the input dtype ([B, H, N, d]); bf16 results are
  * rounded to nearest even. Equivalent to calling mita_pool, mita_landmark,
- * mita_topk, mita_route and mita_gather in that order on the same workspace,
- * except that routing (step 4, which needs only step 1) runs concurrently with
+ * mita_topk, mita_route, mita_gather and mita_combine in that order on the same
+ * workspace, except that routing (step 4, which needs only step 1) runs concurrently with
  * steps 2 and 3 on a side stream: per device the library keeps one stream
  * (default priority) and two events, created on the first call, and joins the
  * side stream back into `stream` before step 5 (so the call stays ordered on
@@ -86,9 +86,9 @@ mita_status mita_forward(const void* Q, const void* K, const void* V, int m, int
 
 /* Step entry points, for per-step checks and timing. They run the steps of
  * mita_forward one at a time: each reads what the earlier steps left in the
- * workspace, so they must be called in this order with the same shape, (m, k, s)
- * and workspace. Each may also copy its result out for inspection; every
- * `*_out` pointer may be NULL. */
+ * workspace, so they must be called in this order (pool, landmark, topk, route,
+ * gather, combine) with the same shape, (m, k, s) and workspace. Each may also
+ * copy its result out for inspection; every `*_out` pointer may be NULL. */
 
 /* Step 1 (pooling). Qt_out: fp64 [B, H, m, d], the landmark queries. */
 mita_status mita_pool(const void* Q, int m, int k, int s, const mita_shape* shape, void* workspace,
@@ -120,11 +120,22 @@ mita_status mita_topk(const void* K, int m, int k, int s, const mita_shape* shap
 mita_status mita_route(const void* Q, int m, int k, int s, const mita_shape* shape, void* workspace,
                        size_t workspace_bytes, int32_t* E_out, void* stream);
 
-/* Step 5 (output): runs attention of each expert's bucket of queries over the
- * expert's gathered keys (and, for s = 1, the shared expert), and merges the
- * s + 1 partial softmaxes of each query into out. */
+/* Step 5, routed part (output: Dutch "Wiskundige Formulering", the keys and
+ * values of the experts a query is routed to): attention of each expert's bucket
+ * of queries over the expert's k gathered key/value rows. With s = 1 and
+ * m <= 64 the same kernel also attends the m shared-expert pairs and writes
+ * `out` (mita_combine then does nothing); otherwise it leaves one partial
+ * softmax per (query, slot) in the workspace and `out` is written by
+ * mita_combine. */
 mita_status mita_gather(const void* Q, const void* K, const void* V, int m, int k, int s, void* out,
                         const mita_shape* shape, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Step 5, shared-expert part and merge: attention of every query over the m
+ * pairs (Q~, V~), merged with the s partial softmaxes mita_gather left, into
+ * `out` ([B, H, N, d], input dtype). Call after mita_gather with the same
+ * arguments; enqueues nothing when mita_gather already wrote `out`. */
+mita_status mita_combine(const void* Q, int m, int k, int s, void* out, const mita_shape* shape, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /* Full softmax attention, out = softmax(Q K^T / sqrt d) V over all N keys of each
  * (batch, head) slice: the quadratic standard attention that MiTA replaces

@@ -291,6 +291,116 @@ struct KVRegs {
   }
 };
 
+// gfx950 transpose read ds_read_b64_tr_b16: within each 16-lane group, lane i
+// supplies the address of 4 consecutive 16-bit elements (row i / 4 of a 4 x 16
+// patch, columns 4 (i % 4) ..) and receives column i of the patch, one element
+// per row (lane layout checked on the GPU).
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// ---------------------------------------------------------------- swizzled tiles, direct loads
+// 64-row bf16 tiles without padding, filled by direct global-to-LDS loads
+// (global_load_lds_dwordx4: lane i of a wave's instruction writes 16 bytes at the
+// instruction's LDS base + 16 i, so each instruction fills 1 KB of whole rows).
+// Bank conflicts are avoided by placing 16-byte chunk c of row r at chunk
+// c ^ swz(r) of the row instead of padding:
+//   K (read as QK fragments, 16 consecutive rows at one chunk): the 16 rows must
+//     land on 16 distinct chunks (D = 128: r & 15; D = 64, two rows per 64 banks:
+//     (r >> 1) & 7);
+//   V (read transposed, a half-wave takes 8 consecutive rows x 2 neighbouring
+//     chunks): the 8 rows' chunk pairs must be disjoint (D = 128: 2 (r & 7);
+//     D = 64: 2 ((r >> 1) & 3)).
+template <int D>
+struct SwzTile {
+  static constexpr int CPR = D / 8;              // 16-byte chunks per row
+  static constexpr int TILE = kKeyBlock * D;     // elements
+  static constexpr int RPI = 512 / D;            // rows per 1 KB load instruction
+  static constexpr int NI = kKeyBlock / RPI / 4; // load instructions per wave per tile
+  __device__ static __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  __device__ static __forceinline__ int swz_v(int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
+};
+
+__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+}
+
+// A wave's share of one 64-row block (rows 16 w .. 16 w + 15) by direct loads:
+// row ids from `ids` (the token of each of the lane's NI rows), K and V tiles.
+template <int D>
+__device__ __forceinline__ void dma_rows(uint16_t* Kt, uint16_t* Vt, const uint16_t* Kz, const uint16_t* Vz,
+                                         const int (&ids)[SwzTile<D>::NI], int w, int lane) {
+  using S = SwzTile<D>;
+  const int p = lane % S::CPR;
+#pragma unroll
+  for (int u = 0; u < S::NI; ++u) {
+    const int row = 16 * w + u * S::RPI + lane / S::CPR;
+    const size_t src = (size_t)ids[u] * D;
+    const int lds_row0 = 16 * w + u * S::RPI;
+    lds_dma16(Kz + src + 8 * (p ^ S::swz_k(row)), Kt + lds_row0 * D);
+    lds_dma16(Vz + src + 8 * (p ^ S::swz_v(row)), Vt + lds_row0 * D);
+  }
+}
+
+// QT column tiles of scores from a swizzled K tile.
+template <int D, int QT>
+__device__ __forceinline__ void qk_bf16_swz(const uint16_t* Ks, const uint4 (&qf)[QT][D / 32], f32x4 (&acc)[QT][4],
+                                            int lane) {
+  using S = SwzTile<D>;
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) acc[qt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    // row 16 kt + r has the swizzle of r (16 kt changes neither r & 15 nor (r >> 1) & 7)
+    const uint16_t* col = Ks + r * D + 8 * ((4 * ks + g) ^ S::swz_k(r));
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const uint4 a0 = *(const uint4*)(col + 16 * kt * D);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) acc[qt][kt] = mma_bf16(a0, qf[qt][ks], acc[qt][kt]);
+    }
+  }
+}
+
+// P V from a swizzled row-major V tile: V^T fragments by transposed reads. Lane (r,
+// g) needs rows (keys) 4 q .. 4 q + 3 of column (d) 16 dt + r with q = 8 h + g (low
+// half) or 8 h + 4 + g (high half): the 4 x 16 patch of rows 4 q .. and columns 16 dt ..
+template <int D, int QT>
+__device__ __forceinline__ void pv_bf16_swz(const uint16_t* Vs, const f32x4 (&p)[QT][4], f32x4 (&o)[QT][D / 16],
+                                            int lane) {
+  using S = SwzTile<D>;
+  const int g = lane >> 4, i = lane & 15;
+  const int row = 4 * g + (i >> 2);           // + 32 h + 16 hi: multiples of 8, same swizzle
+  const int sw = S::swz_v(row), b = (i & 3) >> 1, half = i & 1;
+  const uint16_t* rb = Vs + row * D + 4 * half;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint4 bb[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      bb[qt].x = pack_bf16x2(p[qt][2 * h][0], p[qt][2 * h][1]);
+      bb[qt].y = pack_bf16x2(p[qt][2 * h][2], p[qt][2 * h][3]);
+      bb[qt].z = pack_bf16x2(p[qt][2 * h + 1][0], p[qt][2 * h + 1][1]);
+      bb[qt].w = pack_bf16x2(p[qt][2 * h + 1][2], p[qt][2 * h + 1][3]);
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const int ch = 8 * ((2 * dt + b) ^ sw);
+      const uint2 lo = lds_read_tr16(rb + (32 * h) * D + ch);
+      const uint2 hi = lds_read_tr16(rb + (32 * h + 16) * D + ch);
+      const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) o[qt][dt] = mma_bf16(a, bb[qt], o[qt][dt]);
+    }
+  }
+}
+
 // Write 4 consecutive outputs d0..d0+3 of one row.
 template <typename T>
 __device__ __forceinline__ void store4(T* dst, float a, float b, float c, float d) {

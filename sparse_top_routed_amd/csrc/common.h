@@ -92,15 +92,28 @@ __device__ __forceinline__ int wave_sum_i(int v) {
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
   return v;
 }
-// Reduce over the four lanes l, l^16, l^32, l^48 (one column of an MFMA 16x16 tile).
-__device__ __forceinline__ float quad_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16, WAVE));
-  return fmaxf(v, __shfl_xor(v, 32, WAVE));
+// Reduce over the four lanes l, l^16, l^32, l^48 (one column of an MFMA 16x16 tile)
+// with the gfx950 lane swaps (VALU; no LDS round trip). v_permlane16_swap with both
+// operands v leaves v[l] in one result and v[l ^ 16] in the other (likewise 32),
+// so every lane combines the same pairs as an xor-shuffle reduction would.
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
-__device__ __forceinline__ float quad_sum(float v) {
-  v += __shfl_xor(v, 16, WAVE);
-  return v + __shfl_xor(v, 32, WAVE);
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float quad_max(float v) { return xor32_max(xor16_max(v)); }
+__device__ __forceinline__ float quad_sum(float v) { return xor32_sum(xor16_sum(v)); }
 
 // Orders LDS traffic between the lanes of one wave (waves execute their LDS
 // operations in order; this stops the compiler from moving them across).

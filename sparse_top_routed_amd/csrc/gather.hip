@@ -20,6 +20,9 @@
 
 namespace mita {
 
+// Wave priority of the partial-path kernel while a block's MFMA work is in flight.
+constexpr int kGatherPrio = 1;
+
 __global__ __launch_bounds__(256) void clear_kernel(uint32_t* __restrict__ p, int n) {
   for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
 }
@@ -42,16 +45,16 @@ __global__ __launch_bounds__(256) void bucket_hist_kernel(const int32_t* __restr
 }
 
 // Exclusive scan of the bucket sizes, then the table of query tiles (at most
-// kQueryTile rows of one bucket each) that the gather kernel walks; unused
+// trows rows of one bucket each) that the gather kernel walks; unused
 // entries are marked with expert -1.
 __global__ __launch_bounds__(256) void bucket_scan_kernel(const uint32_t* __restrict__ bcount, uint32_t* __restrict__ boff,
-                                                          int4* __restrict__ tiles, int m, int max_tiles) {
+                                                          int4* __restrict__ tiles, int m, int max_tiles, int trows) {
   __shared__ uint32_t wtot[4];
   const int z = blockIdx.x, tid = threadIdx.x;
   const int per = (m + 255) / 256, i0 = min(m, tid * per), i1 = min(m, i0 + per);
   const uint32_t* c = bcount + (size_t)z * m;
   uint32_t sc = 0, st = 0;
-  for (int i = i0; i < i1; ++i) { sc += c[i]; st += (c[i] + kQueryTile - 1) / kQueryTile; }
+  for (int i = i0; i < i1; ++i) { sc += c[i]; st += (c[i] + trows - 1) / trows; }
   uint32_t totc, tott;
   uint32_t oc = block_incl_scan(sc, wtot, totc) - sc;
   uint32_t ot = block_incl_scan(st, wtot, tott) - st;
@@ -59,8 +62,8 @@ __global__ __launch_bounds__(256) void bucket_scan_kernel(const uint32_t* __rest
   int4* tz = tiles + (size_t)z * max_tiles;
   for (int i = i0; i < i1; ++i) {
     bo[i] = oc;
-    for (uint32_t r = 0; r < c[i]; r += kQueryTile, ++ot)
-      tz[ot] = make_int4(i, (int)r, (int)min((uint32_t)kQueryTile, c[i] - r), (int)(oc + r));
+    for (uint32_t r = 0; r < c[i]; r += trows, ++ot)
+      tz[ot] = make_int4(i, (int)r, (int)min((uint32_t)trows, c[i] - r), (int)(oc + r));
     oc += c[i];
   }
   if (tid == 0) bo[m] = totc;
@@ -105,7 +108,7 @@ __global__ __launch_bounds__(256) void bucket_scatter_kernel(const int32_t* __re
 template <int PER>
 __global__ __launch_bounds__(256) void bucket_slice_kernel(const int32_t* __restrict__ E, uint32_t* __restrict__ boff,
                                                            int4* __restrict__ tiles, int32_t* __restrict__ perm,
-                                                           int Ns, int m, int max_tiles) {
+                                                           int Ns, int m, int max_tiles, int trows) {
   extern __shared__ uint32_t h[];   // [0, m): bucket sizes, [m, 2m): bucket offsets
   __shared__ uint32_t wtot[4];
   const int z = blockIdx.x, tid = threadIdx.x;
@@ -127,7 +130,7 @@ __global__ __launch_bounds__(256) void bucket_slice_kernel(const int32_t* __rest
   __syncthreads();
   const int per = (m + 255) / 256, i0 = min(m, tid * per), i1 = min(m, i0 + per);
   uint32_t sc = 0, st = 0;
-  for (int i = i0; i < i1; ++i) { sc += h[i]; st += (h[i] + kQueryTile - 1) / kQueryTile; }
+  for (int i = i0; i < i1; ++i) { sc += h[i]; st += (h[i] + trows - 1) / trows; }
   uint32_t totc, tott;
   uint32_t oc = block_incl_scan(sc, wtot, totc) - sc;
   uint32_t ot = block_incl_scan(st, wtot, tott) - st;
@@ -137,8 +140,8 @@ __global__ __launch_bounds__(256) void bucket_slice_kernel(const int32_t* __rest
     const uint32_t c = h[i];
     bo[i] = oc;
     h[m + i] = oc;
-    for (uint32_t r = 0; r < c; r += kQueryTile, ++ot)
-      tz[ot] = make_int4(i, (int)r, (int)min((uint32_t)kQueryTile, c - r), (int)(oc + r));
+    for (uint32_t r = 0; r < c; r += trows, ++ot)
+      tz[ot] = make_int4(i, (int)r, (int)min((uint32_t)trows, c - r), (int)(oc + r));
     oc += c;
   }
   if (tid == 0) bo[m] = totc;
@@ -305,7 +308,8 @@ void gather_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                      const void* __restrict__ qtop, const void* __restrict__ vtop,
                                                      T* __restrict__ out, void* __restrict__ pacc,
                                                      float* __restrict__ pml, int N, int m, int k, int s,
-                                                     int max_tiles, long total, long gchunk, int gs, float sl2e) {
+                                                     int max_tiles, long total, long gchunk, int gs, float sl2e,
+                                                     float* __restrict__ lse) {
   using TL = Tiles<T, D>;
   constexpr bool BF = TL::BF;
   constexpr int KP = BF ? 2 : 1;
@@ -428,6 +432,7 @@ void gather_kernel(const T* __restrict__ Q, const T* __restrict__ K,
           if constexpr (FUSED) {
             T* orow = out + ((size_t)zc * N + q) * D;
             const float inv = 1.f / l;
+            if (g == 0) lse[(size_t)zc * N + q] = mrun + log2f(l);
 #pragma unroll
             for (int dt = 0; dt < D / 16; ++dt)
               store4<T>(orow + 16 * dt + 4 * g, o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
@@ -460,6 +465,193 @@ void gather_kernel(const T* __restrict__ Q, const T* __restrict__ K,
       }
     }
     __syncthreads();   // the tile list is rewritten by the next batch
+  }
+}
+
+// Routed part of the output for bf16 inputs when each (query, slot) pair leaves a
+// partial softmax (s > 1 or m > 64). Tiles of 64 QT queries of one bucket: each
+// wave owns QT column tiles of 16 queries, so every K and V fragment it reads
+// from LDS feeds QT MFMAs. Same persistent walk as gather_kernel (groups of gs
+// workgroups on one XCD, interleaved over a contiguous run of the tile table, so
+// an expert's gathered rows are shared through that XCD's L2). The routed blocks
+// are staged by direct global-to-LDS loads into swizzled tiles (no staging
+// registers: that room goes to the second column tile) and double-buffered: a
+// block's rows are requested one block ahead (they land while the previous block
+// computes), its token ids two blocks ahead, and during a tile's last block the
+// next tile's query rows load into the registers of the current ones once its
+// last scores are taken. V stays row-major and is read transposed. While a wave's
+// MFMA work is in flight its priority is raised, so the other wave of the SIMD
+// does its softmax meanwhile. Held to two waves per SIMD.
+template <int D>
+struct GatherDLds {
+  __align__(16) uint16_t rk[2][SwzTile<D>::TILE];
+  __align__(16) uint16_t rv[2][SwzTile<D>::TILE];
+  int4 tile[256];
+  int tz[256];
+  uint32_t wtot[4];
+};
+
+template <int D, int QT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gatherd_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const int32_t* __restrict__ I, const int4* __restrict__ tiles, const int32_t* __restrict__ perm,
+    uint16_t* __restrict__ pacc, float* __restrict__ pml, int N, int m, int k, int s, int max_tiles, long total,
+    long gchunk, int gs, float sl2e) {
+  using T = uint16_t;
+  using S = SwzTile<D>;
+  __shared__ GatherDLds<D> sm;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4;
+  const int row0 = QT * 16 * w + (lane & 15);   // row of the wave's column tile qt: row0 + 16 qt
+  const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3, gpx = (int)(gridDim.x >> 3) / gs;
+  if (jx >= gpx * gs) return;   // workgroup-uniform
+  const int grp = xcd * gpx + jx / gs, jj = jx % gs;
+  const long g0 = (long)grp * gchunk, g1 = min(total, g0 + gchunk);
+  const long nent = g1 - g0 > jj ? (g1 - g0 - jj + gs - 1) / gs : 0;
+  const int B = (k + kKeyBlock - 1) / kKeyBlock;
+
+  for (long base = 0; base < nent; base += 256) {
+    const long e = base + tid, ent = g0 + jj + gs * e;
+    const int4 te = e < nent ? tiles[ent] : make_int4(-1, 0, 0, 0);
+    const uint32_t f = te.x >= 0 ? 1u : 0u;
+    uint32_t nt;
+    const uint32_t pos = block_incl_scan(f, sm.wtot, nt) - f;
+    if (f) {
+      sm.tile[pos] = te;
+      sm.tz[pos] = (int)(ent / max_tiles);
+    }
+    __syncthreads();
+    if (nt == 0) continue;
+    const int nblk = (int)nt * B;
+    auto blk = [&](int j, int& zb, const int32_t*& Ieb, int& kbb) {
+      j = min(j, nblk - 1);
+      const int ti = j / B;
+      zb = sm.tz[ti];
+      Ieb = I + ((size_t)zb * m + sm.tile[ti].x) * k;
+      kbb = (j % B) * kKeyBlock;
+    };
+    // token ids of this lane's rows of block j (rows past the expert's end repeat its last token)
+    auto ids = [&](int j, int (&id)[S::NI], int& zb) {
+      const int32_t* Ieb;
+      int kbb;
+      blk(j, zb, Ieb, kbb);
+#pragma unroll
+      for (int u = 0; u < S::NI; ++u) id[u] = Ieb[min(kbb + 16 * w + u * S::RPI + lane / S::CPR, k - 1)];
+    };
+    auto qids = [&](int t, int (&ent_)[QT]) {
+      t = min(t, (int)nt - 1);
+      const int4 tt = sm.tile[t];
+      const size_t pb = (size_t)sm.tz[t] * N * s + tt.w;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) ent_[qt] = perm[pb + min(row0 + 16 * qt, tt.z - 1)];
+    };
+    auto qload = [&](int t, const int (&ent_)[QT], uint4 (&qf_)[QT][D / 32]) {
+      const T* Qz = Q + (size_t)sm.tz[min(t, (int)nt - 1)] * N * D;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const T* qrow = Qz + (size_t)(ent_[qt] / s) * D;
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) qf_[qt][ks] = ld16(qrow + 32 * ks + 8 * g);
+      }
+    };
+
+    // prologue: block 0 requested into buffer 0, ids of block 1 in flight
+    int id_n[S::NI], z_n;
+    {
+      int id0[S::NI], z0;
+      ids(0, id0, z0);
+      dma_rows<D>(sm.rk[0], sm.rv[0], K + (size_t)z0 * N * D, V + (size_t)z0 * N * D, id0, w, lane);
+      ids(1, id_n, z_n);
+    }
+    int qe[QT], qe_n[QT], qe_nn[QT];
+    qids(0, qe);
+    qids(1, qe_n);
+    uint4 qf[QT][D / 32];
+    qload(0, qe, qf);
+    float mrun[QT], lrun[QT];
+    f32x4 o[QT][D / 16];
+    int4 cur = sm.tile[0];
+    int zc = sm.tz[0];
+
+    for (int j = 0; j < nblk; ++j) {
+      const int ti = j / B, kb = (j % B) * kKeyBlock;
+      const bool newtile = kb == 0;   // block-uniform
+      const bool lastblk = kb + kKeyBlock >= k;
+      if (newtile) {
+        if (j > 0) {
+          cur = sm.tile[ti];
+          zc = sm.tz[ti];
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) {
+            qe[qt] = qe_n[qt];
+            qe_n[qt] = qe_nn[qt];
+          }
+        }
+        qids(ti + 2, qe_nn);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          mrun[qt] = -INFINITY;
+          lrun[qt] = 0.f;
+#pragma unroll
+          for (int dt = 0; dt < D / 16; ++dt) o[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      // this wave's loads of block j have landed; after the barrier every wave's
+      // have, and every wave is done with block j - 1 (buffer (j + 1) & 1 is free)
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      // The next block's loads and this block's reads go through distinct
+      // __restrict__ parameters of one inlined function, so the compiler knows
+      // they cannot overlap and does not wait for the loads before the reads.
+      auto step = [&](uint16_t* __restrict__ nk, uint16_t* __restrict__ nv, const uint16_t* __restrict__ ck,
+                      const uint16_t* __restrict__ cv) __attribute__((always_inline)) {
+        if (j + 1 < nblk)   // block-uniform
+          dma_rows<D>(nk, nv, K + (size_t)z_n * N * D, V + (size_t)z_n * N * D, id_n, w, lane);
+        ids(j + 2, id_n, z_n);
+        const bool live = QT * 16 * w < cur.z;   // the wave has live rows (wave-uniform)
+        f32x4 acc[QT][4];
+        if (live) {
+          __builtin_amdgcn_s_setprio(kGatherPrio);
+          qk_bf16_swz<D, QT>(ck, qf, acc, lane);
+        }
+        if (lastblk) qload(ti + 1, qe_n, qf);   // the next tile's query rows (block-uniform)
+        if (live) {
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) {
+            const float alpha = online_softmax(acc[qt], min(kKeyBlock, k - kb), sl2e, mrun[qt], lrun[qt], lane);
+            rescale<D>(o[qt], alpha);
+          }
+          pv_bf16_swz<D, QT>(cv, acc, o, lane);
+          __builtin_amdgcn_s_setprio(0);
+        }
+      };
+      step(sm.rk[(j + 1) & 1], sm.rv[(j + 1) & 1], sm.rk[j & 1], sm.rv[j & 1]);
+      if (lastblk) {   // the tile's partials: o / l divided by its largest magnitude, as fp16
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          const float l = quad_sum(lrun[qt]);
+          if (row0 + 16 * qt < cur.z) {
+            const int q = qe[qt] / s, slot = qe[qt] % s;
+            const size_t ps = ((size_t)zc * N + q) * s + slot;
+            const float inv = 1.f / l;
+            float amax = 0.f;
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+              for (int jj2 = 0; jj2 < 4; ++jj2) amax = fmaxf(amax, fabsf(o[qt][dt][jj2]));
+            amax = quad_max(amax) * inv;
+            const float sc = amax > 0.f ? amax : 1.f, wv = inv / sc;
+            uint16_t* prow = pacc + ps * D;
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt)
+              *(uint2*)(prow + 16 * dt + 4 * g) = make_uint2(pack_f16x2(o[qt][dt][0] * wv, o[qt][dt][1] * wv),
+                                                             pack_f16x2(o[qt][dt][2] * wv, o[qt][dt][3] * wv));
+            if (g == 0) *(float4*)(pml + ps * 4) = make_float4(mrun[qt], l, sc, 0.f);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();   // the tile list and the buffers are rewritten by the next batch
   }
 }
 
@@ -496,7 +688,7 @@ __global__ __launch_bounds__(256) void gather1_kernel(const T* __restrict__ Q, c
                                                       const int4* __restrict__ tiles, const int32_t* __restrict__ perm,
                                                       const void* __restrict__ qtop, const void* __restrict__ vtop,
                                                       T* __restrict__ out, int N, int m, int k, int max_tiles,
-                                                      int BH, int gs, float sl2e) {
+                                                      int BH, int gs, float sl2e, float* __restrict__ lse) {
   using TL = Tiles<T, D>;
   constexpr bool BF = TL::BF;
   constexpr int KP = BF ? 2 : 1;
@@ -636,8 +828,9 @@ __global__ __launch_bounds__(256) void gather1_kernel(const T* __restrict__ Q, c
           pv_f32<D>((const float*)sm.lm.v, xl, o, lane);
           pv_f32<D>((const float*)sm.rv[b], xr, o, lane);
         }
-        const float inv = 1.f / quad_sum(l);
+        const float lt = quad_sum(l), inv = 1.f / lt;
         if (rowi < cur.z) {
+          if (g == 0) lse[(size_t)zc * N + q] = mx + log2f(lt);
           T* orow = out + ((size_t)zc * N + q) * D;
 #pragma unroll
           for (int dt = 0; dt < D / 16; ++dt)
@@ -661,7 +854,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Q, const void* __restrict__ qtop,
                                                       const void* __restrict__ vtop, const void* __restrict__ pacc,
                                                       const float* __restrict__ pml, T* __restrict__ out, int N, int m,
-                                                      int s, float sl2e) {
+                                                      int s, float sl2e, float* __restrict__ lse) {
   __shared__ AttnLds<T, D> sm;
   const int z = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
   const int q = blockIdx.x * kQueryTile + 16 * w + r;
@@ -704,7 +897,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Q, c
   float mrun = M;
   attend_landmarks<T, D>(sm, LR, qf, qtop, vtop, z, m, sl2e, mrun, lrun, o, tid);
   if (!ok) return;
-  const float inv = 1.f / quad_sum(lrun);
+  const float lt = quad_sum(lrun), inv = 1.f / lt;
+  if (g == 0) lse[(size_t)z * N + q] = mrun + log2f(lt);
   T* orow = out + ((size_t)z * N + q) * D;
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt)
@@ -717,7 +911,7 @@ hipError_t launch_bucket(const Plan& p, char* ws, hipStream_t st) {
   if (Ns <= 256 * kBucketSlicePer && (size_t)p.m * 8 <= 64 * 1024) {   // one workgroup per slice
     hipLaunchKernelGGL(bucket_slice_kernel<kBucketSlicePer>, dim3(p.BH), dim3(256), (size_t)p.m * 8, st,
                        (const int32_t*)(ws + p.ws.E), (uint32_t*)(ws + p.ws.boff), (int4*)(ws + p.ws.tiles),
-                       (int32_t*)(ws + p.ws.perm), Ns, p.m, p.max_tiles);
+                       (int32_t*)(ws + p.ws.perm), Ns, p.m, p.max_tiles, p.trows);
     return hipGetLastError();
   }
   const int nclear = (int)((p.ws.bcursor + (size_t)p.BH * p.m * 4 - p.ws.bcount) / 4);
@@ -730,7 +924,7 @@ hipError_t launch_bucket(const Plan& p, char* ws, hipStream_t st) {
                      (uint32_t*)(ws + p.ws.bcount), Ns, p.m);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bucket_scan_kernel, dim3(p.BH), dim3(256), 0, st, (const uint32_t*)(ws + p.ws.bcount),
-                     (uint32_t*)(ws + p.ws.boff), (int4*)(ws + p.ws.tiles), p.m, p.max_tiles);
+                     (uint32_t*)(ws + p.ws.boff), (int4*)(ws + p.ws.tiles), p.m, p.max_tiles, p.trows);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bucket_scatter_kernel, bgrid, dim3(256), (size_t)p.m * 8, st, (const int32_t*)(ws + p.ws.E),
                      (const uint32_t*)(ws + p.ws.boff), (uint32_t*)(ws + p.ws.bcursor), (int32_t*)(ws + p.ws.perm), Ns,
@@ -764,24 +958,46 @@ static hipError_t gather_launch(const Plan& p, const void* Q, const void* K, con
     const int g1 = std::max(8 * gs, slots / (8 * gs) * 8 * gs);
     hipLaunchKernelGGL((gather1_kernel<T, D>), dim3(g1), dim3(256), 0, st, (const T*)Q, (const T*)K, (const T*)V,
                        (const int32_t*)(ws + p.ws.I), (const int4*)(ws + p.ws.tiles), (const int32_t*)(ws + p.ws.perm),
-                       (const void*)(ws + p.ws.qtop), vtop, (T*)out, p.N, p.m, p.k, p.max_tiles, p.BH, gs, sl2e);
+                       (const void*)(ws + p.ws.qtop), vtop, (T*)out, p.N, p.m, p.k, p.max_tiles, p.BH, gs, sl2e,
+                       (float*)(ws + p.ws.lse));
     return hipGetLastError();
   }
   if (p.s == 1 && p.m <= kKeyBlock) {
     hipLaunchKernelGGL((gather_kernel<T, D, true>), dim3(grid), dim3(256), 0, st, (const T*)Q, (const T*)K, (const T*)V,
                        (const int32_t*)(ws + p.ws.I), (const int4*)(ws + p.ws.tiles), (const int32_t*)(ws + p.ws.perm),
                        (const void*)(ws + p.ws.qtop), vtop, (T*)out, (float*)nullptr, (float*)nullptr, p.N, p.m, p.k,
-                       p.s, p.max_tiles, total, gchunk, gsz, sl2e);
+                       p.s, p.max_tiles, total, gchunk, gsz, sl2e, (float*)(ws + p.ws.lse));
+    return hipGetLastError();
+  }
+  if constexpr (sizeof(T) == 2) {   // bf16 partials: the direct-load kernel, 1 or 2 column tiles per wave
+    static PerDevice c_q1, c_q2;
+    auto go = [&](auto kern, PerDevice& cache) {
+      const int sl = n_cu * resident_per_cu(cache, kern, 256);
+      const int gq = std::max(1, std::min(8, sl / 8));
+      const int gr = std::max(8 * gq, sl / (8 * gq) * 8 * gq);
+      const long gc = (total + gr / gq - 1) / (gr / gq);
+      hipLaunchKernelGGL(kern, dim3(gr), dim3(256), 0, st, (const uint16_t*)Q, (const uint16_t*)K,
+                         (const uint16_t*)V, (const int32_t*)(ws + p.ws.I), (const int4*)(ws + p.ws.tiles),
+                         (const int32_t*)(ws + p.ws.perm), (uint16_t*)(ws + p.ws.pacc), (float*)(ws + p.ws.pml), p.N,
+                         p.m, p.k, p.s, p.max_tiles, total, gc, gq, sl2e);
+    };
+    if (p.gqt == 2) go(gatherd_kernel<D, 2>, c_q2); else go(gatherd_kernel<D, 1>, c_q1);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((gather_kernel<T, D, false>), dim3(grid), dim3(256), 0, st, (const T*)Q, (const T*)K, (const T*)V,
                      (const int32_t*)(ws + p.ws.I), (const int4*)(ws + p.ws.tiles), (const int32_t*)(ws + p.ws.perm),
                      (const void*)(ws + p.ws.qtop), vtop, (T*)out, (void*)(ws + p.ws.pacc), (float*)(ws + p.ws.pml),
-                     p.N, p.m, p.k, p.s, p.max_tiles, total, gchunk, gsz, sl2e);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+                     p.N, p.m, p.k, p.s, p.max_tiles, total, gchunk, gsz, sl2e, (float*)nullptr);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t combine_launch(const Plan& p, const void* Q, void* out, char* ws, hipStream_t st) {
+  const float sl2e = (float)(1.4426950408889634 / sqrt((double)D));
+  const void* vtop = p.dtype == MITA_BF16 ? (const void*)(ws + p.ws.vt16) : (const void*)(ws + p.ws.vt32);
   hipLaunchKernelGGL((combine_kernel<T, D>), dim3(p.qtiles, p.BH), dim3(256), 0, st, (const T*)Q,
                      (const void*)(ws + p.ws.qtop), vtop, (const void*)(ws + p.ws.pacc), (const float*)(ws + p.ws.pml),
-                     (T*)out, p.N, p.m, p.s, sl2e);
+                     (T*)out, p.N, p.m, p.s, sl2e, (float*)(ws + p.ws.lse));
   return hipGetLastError();
 }
 
@@ -790,6 +1006,15 @@ hipError_t launch_gather(const Plan& p, const void* Q, const void* K, const void
   if (p.dtype == MITA_BF16)
     return p.d == 64 ? gather_launch<uint16_t, 64>(p, Q, K, V, out, ws, st) : gather_launch<uint16_t, 128>(p, Q, K, V, out, ws, st);
   return p.d == 64 ? gather_launch<float, 64>(p, Q, K, V, out, ws, st) : gather_launch<float, 128>(p, Q, K, V, out, ws, st);
+}
+
+bool has_combine(const Plan& p) { return p.s > 1 || p.m > kKeyBlock; }
+
+hipError_t launch_combine(const Plan& p, const void* Q, void* out, char* ws, hipStream_t st) {
+  if (!has_combine(p)) return hipSuccess;   // the gather kernels wrote the output
+  if (p.dtype == MITA_BF16)
+    return p.d == 64 ? combine_launch<uint16_t, 64>(p, Q, out, ws, st) : combine_launch<uint16_t, 128>(p, Q, out, ws, st);
+  return p.d == 64 ? combine_launch<float, 64>(p, Q, out, ws, st) : combine_launch<float, 128>(p, Q, out, ws, st);
 }
 
 // Route-step counter block (queued-query count) is cleared before routing; only

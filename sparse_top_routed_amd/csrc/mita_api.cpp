@@ -95,7 +95,13 @@ mita_status make_plan(const mita_shape* shape, int m, int k, int s, Plan* p, con
     P.capc = P.cap ? (int)std::min<int64_t>(P.lchunk, P.cap) : 0;
   }
   P.qtiles = (sh.N + kQueryTile - 1) / kQueryTile;
-  P.max_tiles = (int)(((int64_t)sh.N * s + kQueryTile - 1) / kQueryTile + m);
+  // Routed-expert kernel (bf16 partial path): two 16-query column tiles per wave
+  // (each staged key/value fragment feeds two MFMAs) when buckets hold 256 or more
+  // (query, slot) pairs on average, so 128-row tiles are mostly full; else one.
+  const bool partial_path = s > 1 || m > kKeyBlock;
+  P.gqt = (sh.dtype == MITA_BF16 && partial_path && (int64_t)sh.N * s >= 256 * (int64_t)m) ? 2 : 1;
+  P.trows = 64 * P.gqt;
+  P.max_tiles = (int)(((int64_t)sh.N * s + P.trows - 1) / P.trows + m);
 
   // Error bound of an approximate score relative to |q~|_2 |k|_2 (a factor 2 of slack):
   // bf16: Q~ split in two bf16 parts (representation error 2^-16) and 2d products
@@ -145,6 +151,10 @@ mita_status make_plan(const mita_shape* shape, int m, int k, int s, Plan* p, con
   } else {
     L.pacc = L.pml = 0;
   }
+  // softmax normalisers the forward leaves for the backward (log2 domain: with
+  // c = log2(e) / sqrt(d), a weight is 2^(c s - lse))
+  L.lse = take(bh * N * 4);
+  L.lse_se = take(bh * m * 4);
   L.total = off;
   return MITA_OK;
 }
@@ -284,6 +294,15 @@ mita_status mita_gather(const void* Q, const void* K, const void* V, int m, int 
   return hip_status(launch_gather(P, Q, K, V, out, (char*)workspace, (hipStream_t)stream), "gather");
 }
 
+mita_status mita_combine(const void* Q, int m, int k, int s, void* out, const mita_shape* shape, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  Plan P;
+  mita_status st = check_common(shape, m, k, s, workspace, workspace_bytes, &P);
+  if (st != MITA_OK) return st;
+  if ((st = check_ptr(Q, "Q")) != MITA_OK || (st = check_ptr(out, "out")) != MITA_OK) return st;
+  return hip_status(launch_combine(P, Q, out, (char*)workspace, (hipStream_t)stream), "combine");
+}
+
 }  // extern "C"
 
 namespace {
@@ -372,6 +391,7 @@ mita_status mita_forward(const void* Q, const void* K, const void* V, int m, int
   // join: the output step needs both branches
   if (joined) fe.add(hipStreamWaitEvent(hs, sd->join, 0), "join wait");
   if (fe.ok()) fe.add(launch_gather(P, Q, K, V, out, ws, hs), "gather");
+  if (fe.ok()) fe.add(launch_combine(P, Q, out, ws, hs), "combine");
   return fe.finish();
 }
 
@@ -394,3 +414,4 @@ mita_status mita_dense_attention(const void* Q, const void* K, const void* V, vo
 }
 
 }  // extern "C"
+

@@ -48,6 +48,8 @@ struct Layout {
   size_t perm;      // i32 [BH, N * s]    (query * s + slot) grouped by expert
   size_t pacc;      // [BH, N, s, d] per-slot outputs o / (sum * scale): fp16 (bf16 inputs) or f32
   size_t pml;       // f32 [BH, N, s, 4] per-slot (max, sum, scale, pad)
+  size_t lse;       // f32 [BH, N]        log2-sum-exp of each query's final softmax (for the backward)
+  size_t lse_se;    // f32 [BH, m]        log2-sum-exp of each landmark's shared-expert softmax
   size_t total;
   size_t counters_bytes;
 };
@@ -70,6 +72,8 @@ struct Plan {
   int capc;         // candidate slots per (row, key chunk): min(lchunk, cap)
   // router and output
   int qtiles;       // ceil(N / kQueryTile)
+  int gqt;          // 16-query column tiles per wave of the routed-expert kernel (1 or 2)
+  int trows;        // rows (queries) per tile of the bucket tile table: 64 gqt
   int max_tiles;    // upper bound of query tiles over all buckets of one slice
   double gamma_qk;  // relative error bound of an approximate score, in units of |q~| |k|
   Layout ws;
@@ -123,7 +127,12 @@ hipError_t launch_dense(int dtype, int d, int BH, int N, const void* Q, const vo
                         hipStream_t st);
 hipError_t launch_route(const Plan& p, const void* Q, char* ws, hipStream_t st);
 hipError_t launch_bucket(const Plan& p, char* ws, hipStream_t st);
+// Step 5, routed part: each expert's bucket of queries over its gathered keys. Writes
+// the output itself when the landmark part is fused (s = 1, m <= 64), else partials.
 hipError_t launch_gather(const Plan& p, const void* Q, const void* K, const void* V, void* out, char* ws,
                          hipStream_t st);
+// Step 5, landmark part and merge (no launch when launch_gather wrote the output).
+bool has_combine(const Plan& p);
+hipError_t launch_combine(const Plan& p, const void* Q, void* out, char* ws, hipStream_t st);
 
 }  // namespace mita

@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void merge_thresh_kernel(const float* __restri
                                                            const float* __restrict__ qtnorm,
                                                            const float* __restrict__ kmax, int nsplit,
                                                            uint32_t* __restrict__ thr, int nbg, int m, int k,
-                                                           double gamma, int rows) {
+                                                           double gamma, int rows, float* __restrict__ lse_se) {
   constexpr int CW = D / 64;
   const int tid = threadIdx.x, lane = tid & 63, row = blockIdx.x * 4 + (tid >> 6);
   if (row >= rows) return;   // wave-uniform
@@ -204,6 +204,7 @@ __global__ __launch_bounds__(256) void merge_thresh_kernel(const float* __restri
     }
   }
   const float inv = 1.f / L;
+  if (lane == 0) lse_se[row] = M + log2f(L);
 #pragma unroll
   for (int e = 0; e < CW; ++e) {
     const float x = acc[e] * inv;
@@ -546,7 +547,7 @@ static hipError_t merge_thresh_launch(const Plan& p, char* ws, hipStream_t st) {
     hipLaunchKernelGGL(kern, dim3((rows + 3) / 4), dim3(256), 0, st, (const float*)(ws + p.ws.lpart),
                        (float*)(ws + p.ws.vt32), (uint16_t*)(ws + p.ws.vt16), (const float*)(ws + p.ws.bmax),
                        (const float*)(ws + p.ws.qtnorm), (const float*)(ws + p.ws.kmax), p.nsplit,
-                       (uint32_t*)(ws + p.ws.thr), nbg, p.m, p.k, p.gamma_qk, rows);
+                       (uint32_t*)(ws + p.ws.thr), nbg, p.m, p.k, p.gamma_qk, rows, (float*)(ws + p.ws.lse_se));
   };
   if (p.nsplit <= 4) {
     if (nbg <= 256) go(merge_thresh_kernel<D, 4, 4>);

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libmita.so")
 MITA_OK, MITA_ERR_INVALID_ARG, MITA_ERR_UNSUPPORTED, MITA_ERR_WORKSPACE, MITA_ERR_HIP = 0, -1, -2, -3, -4
 MITA_F32, MITA_BF16 = 0, 1
 SYMBOLS = ("mita_workspace_bytes", "mita_forward", "mita_pool", "mita_landmark", "mita_topk", "mita_route",
-           "mita_gather", "mita_dense_attention", "mita_status_string", "mita_last_error")
+           "mita_gather", "mita_combine", "mita_dense_attention", "mita_status_string", "mita_last_error")
 
 
 class Shape(ctypes.Structure):
@@ -52,9 +52,10 @@ def load() -> ctypes.CDLL:
     lib.mita_topk.argtypes = [vp, i, i, i, sp, vp, sz, vp, vp]
     lib.mita_route.argtypes = [vp, i, i, i, sp, vp, sz, vp, vp]
     lib.mita_gather.argtypes = [vp, vp, vp, i, i, i, vp, sp, vp, sz, vp]
+    lib.mita_combine.argtypes = [vp, i, i, i, vp, sp, vp, sz, vp]
     lib.mita_dense_attention.argtypes = [vp, vp, vp, vp, sp, vp]
     for f in ("mita_forward", "mita_pool", "mita_landmark", "mita_topk", "mita_route", "mita_gather",
-              "mita_dense_attention"):
+              "mita_combine", "mita_dense_attention"):
         getattr(lib, f).restype = ctypes.c_int
     lib.mita_status_string.argtypes = [i]
     lib.mita_status_string.restype = ctypes.c_char_p
@@ -101,7 +102,8 @@ def _stream():
 @dataclass
 class Mita:
     """One problem (shape and m, k, s) with its workspace; runs the whole pass or
-    its steps (which must be called in order: pool, landmark, topk, route, gather)."""
+    its steps (which must be called in order: pool, landmark, topk, route, gather,
+    combine; ``output`` runs the last two)."""
     shape: Shape
     m: int
     k: int
@@ -175,6 +177,7 @@ class Mita:
         return E
 
     def gather(self, Q, K, V, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """Routed part of step 5 (writes ``out`` itself only when the landmark part is fused)."""
         self._inputs(Q, K, V)
         out = torch.empty_like(Q) if out is None else out
         self._inputs(out)
@@ -183,11 +186,24 @@ class Mita:
                                   ctypes.byref(self.shape), ws, n, _stream()))
         return out
 
+    def combine(self, Q, out: torch.Tensor) -> torch.Tensor:
+        """Landmark part and merge of step 5 into ``out`` (after ``gather`` with the same ``out``)."""
+        self._inputs(Q, out)
+        ws, n = self._ws()
+        _check(load().mita_combine(_ptr(Q), self.m, self.k, self.s, _ptr(out), ctypes.byref(self.shape), ws, n,
+                                   _stream()))
+        return out
+
+    def output(self, Q, K, V, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """Both parts of step 5."""
+        return self.combine(Q, self.gather(Q, K, V, out))
+
 
 def forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, m: int, k: int, s: int, grid=None, pool=None,
             out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """MiTA attention forward: Q, K, V [B, H, N, d] (bf16 or fp32) on the GPU."""
     return Mita.create(Q, m, k, s, grid, pool).forward(Q, K, V, out)
+
 
 
 def dense_attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,

@@ -42,7 +42,7 @@ def run_gpu_steps(w: synth.Workload, Q, K, V, lib, want_s: bool = True) -> Dict[
     Vt, S = call.landmark(Kd, Vd, want_vt=True, want_s=want_s)
     I = call.topk(Kd, want=True)
     E = call.route(Qd, want=True)
-    O = call.gather(Qd, Kd, Vd)
+    O = call.output(Qd, Kd, Vd)
     torch.cuda.synchronize()
     res = {"Qt": Qt.cpu().numpy(), "Vt": Vt.cpu().numpy().astype(np.float64), "I": I.cpu().numpy(),
            "E": E.cpu().numpy(), "O": out_to_f64(O)}

@@ -90,7 +90,7 @@ def test_forward_equals_steps_and_is_deterministic(lib):
     call.landmark(Kd, Vd)
     call.topk(Kd)
     call.route(Qd)
-    c = call.gather(Qd, Kd, Vd)
+    c = call.output(Qd, Kd, Vd)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
@@ -180,7 +180,7 @@ def test_full_size_sampled(name, lib):
     Vt, _ = call.landmark(Kd, Vd, want_vt=True)
     I = call.topk(Kd, want=True)
     E = call.route(Qd, want=True)
-    O2 = call.gather(Qd, Kd, Vd)
+    O2 = call.output(Qd, Kd, Vd)
     torch.cuda.synchronize()
     assert torch.equal(O.view(torch.int16), O2.view(torch.int16))
     gpu = {"Qt": Qt.cpu().numpy(), "Vt": Vt.cpu().numpy().astype(np.float64), "I": I.cpu().numpy(),

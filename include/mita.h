@@ -151,6 +151,30 @@ mita_status mita_combine(const void* Q, int m, int k, int s, void* out, const mi
 mita_status mita_dense_attention(const void* Q, const void* K, const void* V, void* out, const mita_shape* shape,
                                  void* stream);
 
+/* Size of the fixed scratch array behind mita_forward_noalloc (64 MiB per GPU). */
+#define MITA_NOALLOC_SCRATCH_BYTES 67108864u
+
+/* Whole forward pass like mita_forward, for callers that cannot allocate device
+ * memory or hand over a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation. The caller still passes Q, K, V and
+ * `out` (same layout, dtype and checks as mita_forward); the intermediates live
+ * in a fixed array of MITA_NOALLOC_SCRATCH_BYTES in the library's device code,
+ * one per GPU, which each GPU the library runs on holds until the process ends.
+ * Nothing is allocated and no stream or event is created: every step runs in
+ * order on `stream`. Results are bit-identical to mita_forward's.
+ * Limit: problems whose intermediates need more than the array (the same sizes as
+ * mita_workspace_bytes, except that the exact top-k fallback keeps only its
+ * fewest 64 score rows) are rejected with MITA_ERR_WORKSPACE before anything is
+ * enqueued; small problems fit, e.g. B = H = 1, N = 1024, d = 64 with m = 16,
+ * k = 64 takes under 2 MiB.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (different streams or host threads, or a graph replay beside an
+ * eager call) race and give wrong results; calls kept in order on one stream are
+ * safe. Each call sets every part of the array it reads, so what an earlier call
+ * left there does not matter. */
+mita_status mita_forward_noalloc(const void* Q, const void* K, const void* V, int m, int k, int s, void* out,
+                                 const mita_shape* shape, void* stream);
+
 /* Short description of a status code (static storage). */
 const char* mita_status_string(int status);
 /* Message of the last failed call on this thread ("" if none). */

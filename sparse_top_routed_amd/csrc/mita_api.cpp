@@ -415,3 +415,68 @@ mita_status mita_dense_attention(const void* Q, const void* K, const void* V, vo
 
 }  // extern "C"
 
+// ---------------------------------------------------------------- fixed scratch
+// Intermediates of mita_forward_noalloc: one array per GPU in the library's device
+// code, held until the process ends. Host code never uses the array's name as an
+// address (on the host it is only a stand-in): its device address is looked up
+// once per device with hipGetSymbolAddress and kept in g_scratch.
+static __device__ __align__(256) char scratch[MITA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the first call
+// on that device, with the device current).
+mita_status scratch_ptr(char** out) {
+  int dev = 0;
+  mita_status st;
+  if ((st = hip_status(hipGetDevice(&dev), "hipGetDevice")) != MITA_OK) return st;
+  if (dev < 0 || dev >= kMaxDevices) { set_error("device id out of range"); return MITA_ERR_UNSUPPORTED; }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if ((st = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)")) != MITA_OK)
+      return st;
+    if (!p || ((uintptr_t)p & 255) != 0) { set_error("scratch array misplaced"); return MITA_ERR_HIP; }
+    g_scratch[dev] = p;
+  }
+  *out = (char*)g_scratch[dev];
+  return MITA_OK;
+}
+
+}  // namespace
+
+extern "C" mita_status mita_forward_noalloc(const void* Q, const void* K, const void* V, int m, int k, int s,
+                                            void* out, const mita_shape* shape, void* stream) {
+  Plan P;
+  const char* err = "";
+  mita_status st = make_plan(shape, m, k, s, &P, &err, /*compact=*/true);
+  if (st != MITA_OK) { set_error(err); return st; }
+  if (P.ws.total > (size_t)MITA_NOALLOC_SCRATCH_BYTES) {
+    static thread_local char buf[200];
+    snprintf(buf, sizeof buf, "problem needs %zu bytes of scratch, above the fixed %zu of mita_forward_noalloc",
+             P.ws.total, (size_t)MITA_NOALLOC_SCRATCH_BYTES);
+    set_error(buf);
+    return MITA_ERR_WORKSPACE;
+  }
+  if ((st = check_ptr(Q, "Q")) != MITA_OK || (st = check_ptr(K, "K")) != MITA_OK ||
+      (st = check_ptr(V, "V")) != MITA_OK || (st = check_ptr(out, "out")) != MITA_OK)
+    return st;
+  char* ws = nullptr;
+  if ((st = scratch_ptr(&ws)) != MITA_OK) return st;
+  // every step on the caller's stream, in order (no side stream, nothing created);
+  // each kernel sets what it needs, so the last call's contents do not matter
+  hipStream_t hs = (hipStream_t)stream;
+  FirstError fe;
+  fe.add(launch_pool(P, Q, ws, hs), "pool");
+  if (fe.ok()) fe.add(launch_clear(P, ws, hs), "clear");
+  if (fe.ok()) fe.add(launch_route(P, Q, ws, hs), "route");
+  if (fe.ok()) fe.add(launch_bucket(P, ws, hs), "bucket");
+  if (fe.ok()) fe.add(launch_landmark(P, K, V, ws, nullptr, hs), "landmark");
+  if (fe.ok()) fe.add(launch_topk(P, K, ws, hs), "topk");
+  if (fe.ok()) fe.add(launch_gather(P, Q, K, V, out, ws, hs), "gather");
+  if (fe.ok()) fe.add(launch_combine(P, Q, out, ws, hs), "combine");
+  return fe.finish();
+}

@@ -19,7 +19,9 @@ LIB_PATH = os.path.join(_HERE, "libmita.so")
 MITA_OK, MITA_ERR_INVALID_ARG, MITA_ERR_UNSUPPORTED, MITA_ERR_WORKSPACE, MITA_ERR_HIP = 0, -1, -2, -3, -4
 MITA_F32, MITA_BF16 = 0, 1
 SYMBOLS = ("mita_workspace_bytes", "mita_forward", "mita_pool", "mita_landmark", "mita_topk", "mita_route",
-           "mita_gather", "mita_combine", "mita_dense_attention", "mita_status_string", "mita_last_error")
+           "mita_gather", "mita_combine", "mita_dense_attention", "mita_forward_noalloc", "mita_status_string",
+           "mita_last_error")
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MITA_NOALLOC_SCRATCH_BYTES
 
 
 class Shape(ctypes.Structure):
@@ -54,8 +56,9 @@ def load() -> ctypes.CDLL:
     lib.mita_gather.argtypes = [vp, vp, vp, i, i, i, vp, sp, vp, sz, vp]
     lib.mita_combine.argtypes = [vp, i, i, i, vp, sp, vp, sz, vp]
     lib.mita_dense_attention.argtypes = [vp, vp, vp, vp, sp, vp]
+    lib.mita_forward_noalloc.argtypes = [vp, vp, vp, i, i, i, vp, sp, vp]
     for f in ("mita_forward", "mita_pool", "mita_landmark", "mita_topk", "mita_route", "mita_gather",
-              "mita_combine", "mita_dense_attention"):
+              "mita_combine", "mita_dense_attention", "mita_forward_noalloc"):
         getattr(lib, f).restype = ctypes.c_int
     lib.mita_status_string.argtypes = [i]
     lib.mita_status_string.restype = ctypes.c_char_p
@@ -204,6 +207,28 @@ def forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, m: int, k: int, s
     """MiTA attention forward: Q, K, V [B, H, N, d] (bf16 or fp32) on the GPU."""
     return Mita.create(Q, m, k, s, grid, pool).forward(Q, K, V, out)
 
+
+def forward_noalloc(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, m: int, k: int, s: int, grid=None,
+                    pool=None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """MiTA forward through mita_forward_noalloc: no workspace, the library's fixed
+    scratch array instead (small problems only; calls on one GPU must not overlap)."""
+    if Q.dim() != 4:
+        raise ValueError("Q must be [B, H, N, d]")
+    B, H, N, d = Q.shape
+    shape = make_shape(B, H, N, d, m, Q.dtype, grid, pool)
+    for t in (K, V):
+        if t.shape != Q.shape or t.dtype != Q.dtype:
+            raise ValueError("Q, K and V must have one shape and dtype")
+    for t in (Q, K, V):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous and on the GPU")
+    if out is None:
+        out = torch.empty_like(Q)
+    elif out.shape != Q.shape or out.dtype != Q.dtype or not out.is_contiguous():
+        raise ValueError("out must match Q")
+    _check(load().mita_forward_noalloc(_ptr(Q), _ptr(K), _ptr(V), m, k, s, _ptr(out), ctypes.byref(shape),
+                                       _stream()))
+    return out
 
 
 def dense_attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,

@@ -137,6 +137,30 @@ mita_status mita_gather(const void* Q, const void* K, const void* V, int m, int 
 mita_status mita_combine(const void* Q, int m, int k, int s, void* out, const mita_shape* shape, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* Backward of the forward pass (bf16 inputs only): dQ, dK, dV (fp32 [B, H, N, d],
+ * owned by the caller) of sum(dout * out), with the expert sets I and the
+ * routing E held fixed (they are selections, not differentiable). The pages
+ * report training through MiTA (Long Range Arena training wall-clock: Arabic/
+ * Hindi section 4, Dutch "Resultaten") but give no backward; this is the chain
+ * rule through the forward as defined: the final attention over
+ * [Q~, K_{I_e1}, ..] / [V~, V_{I_e1}, ..] (a token in two of a query's experts
+ * receives both contributions), the shared expert V~ = softmax(Q~ K^T / sqrt d) V,
+ * and the pooling Q -> Q~.
+ * Reads what mita_forward (or the step entry points through mita_combine) left
+ * in `workspace` for the same Q, K, V, shape and (m, k, s): landmarks, V~, the
+ * expert sets, the routing buckets and the softmax normalisers. `out` is that
+ * forward's output and `dout` the gradient of the loss with respect to it, both
+ * bf16 [B, H, N, d]. The forward workspace is not modified. `bwd_workspace`
+ * (256-byte aligned, mita_backward_workspace_bytes bytes) holds the partial
+ * gradients. Sums run in a fixed order (no float atomics): two calls on the same
+ * inputs give bit-identical gradients. Errors as for mita_forward; fp32 inputs
+ * give MITA_ERR_UNSUPPORTED. */
+size_t mita_backward_workspace_bytes(const mita_shape* shape, int m, int k, int s);
+mita_status mita_backward(const void* Q, const void* K, const void* V, const void* out, const void* dout, int m,
+                          int k, int s, float* dQ, float* dK, float* dV, const mita_shape* shape,
+                          const void* workspace, size_t workspace_bytes, void* bwd_workspace,
+                          size_t bwd_workspace_bytes, void* stream);
+
 /* Full softmax attention, out = softmax(Q K^T / sqrt d) V over all N keys of each
  * (batch, head) slice: the quadratic standard attention that MiTA replaces
  * (MiTA pages: introduction and problem statement; the pages' speed-ups are

@@ -14,7 +14,8 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmita.so")
-SOURCES = ["mita_api.cpp", "pool.hip", "landmark.hip", "topk.hip", "route.hip", "gather.hip", "dense.hip"]
+SOURCES = ["mita_api.cpp", "pool.hip", "landmark.hip", "topk.hip", "route.hip", "gather.hip", "dense.hip",
+           "backward.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -395,6 +395,42 @@ mita_status mita_forward(const void* Q, const void* K, const void* V, int m, int
   return fe.finish();
 }
 
+size_t mita_backward_workspace_bytes(const mita_shape* shape, int m, int k, int s) {
+  Plan P;
+  const char* err;
+  if (make_plan(shape, m, k, s, &P, &err) != MITA_OK) { set_error(err); return 0; }
+  if (P.dtype != MITA_BF16) { set_error("the backward supports bf16 inputs only"); return 0; }
+  BwdLayout L;
+  backward_plan(P, &L);
+  return L.total;
+}
+
+mita_status mita_backward(const void* Q, const void* K, const void* V, const void* out, const void* dout, int m,
+                          int k, int s, float* dQ, float* dK, float* dV, const mita_shape* shape,
+                          const void* workspace, size_t workspace_bytes, void* bwd_workspace,
+                          size_t bwd_workspace_bytes, void* stream) {
+  Plan P;
+  mita_status st = check_common(shape, m, k, s, const_cast<void*>(workspace), workspace_bytes, &P);
+  if (st != MITA_OK) return st;
+  if (P.dtype != MITA_BF16) { set_error("the backward supports bf16 inputs only"); return MITA_ERR_UNSUPPORTED; }
+  if ((st = check_ptr(Q, "Q")) != MITA_OK || (st = check_ptr(K, "K")) != MITA_OK ||
+      (st = check_ptr(V, "V")) != MITA_OK || (st = check_ptr(out, "out")) != MITA_OK ||
+      (st = check_ptr(dout, "dout")) != MITA_OK || (st = check_ptr(dQ, "dQ")) != MITA_OK ||
+      (st = check_ptr(dK, "dK")) != MITA_OK || (st = check_ptr(dV, "dV")) != MITA_OK)
+    return st;
+  BwdLayout L;
+  backward_plan(P, &L);
+  if (!bwd_workspace) { set_error("backward workspace is NULL"); return MITA_ERR_WORKSPACE; }
+  if (((uintptr_t)bwd_workspace & 255) != 0) { set_error("backward workspace must be 256-byte aligned"); return MITA_ERR_WORKSPACE; }
+  if (bwd_workspace_bytes < L.total) {
+    set_error("backward workspace smaller than mita_backward_workspace_bytes()");
+    return MITA_ERR_WORKSPACE;
+  }
+  return hip_status(launch_backward(P, L, Q, K, V, out, dout, dQ, dK, dV, (const char*)workspace,
+                                    (char*)bwd_workspace, (hipStream_t)stream),
+                    "backward");
+}
+
 mita_status mita_dense_attention(const void* Q, const void* K, const void* V, void* out, const mita_shape* shape,
                                  void* stream) {
   if (!shape) { set_error("shape is NULL"); return MITA_ERR_INVALID_ARG; }

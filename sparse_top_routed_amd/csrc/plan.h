@@ -79,6 +79,36 @@ struct Plan {
   Layout ws;
 };
 
+// Backward workspace: offsets (bytes) of its buffers, and the parts that split
+// the landmark part's queries and the shared part's keys for parallelism.
+struct BwdLayout {
+  int qparts, kparts;
+  size_t Dq;        // f32 [BH, N]          rowsum(dO * O)
+  size_t Di;        // f32 [BH, m]          rowsum(dV~ * V~)
+  size_t dvt;       // f32 [BH, m, d]       dV~
+  size_t dvt16;     // bf16 [BH, m, d]      dV~ (MFMA operand)
+  size_t dqt;       // f32 [BH, m, d]       dQ~ (landmark and shared parts)
+  size_t lm_dqt;    // f32 [qparts, BH, m, d]
+  size_t lm_dvt;    // f32 [qparts, BH, m, d]
+  size_t se_dqt;    // f32 [kparts, BH, m, d]
+  size_t dQp;       // f32 [BH, N, s, d]    routed dQ per (query, slot)
+  size_t dQl;       // f32 [BH, N, d]       landmark-part dQ
+  size_t dKe;       // f32 [BH, m, k, d]    routed dK per (expert, list slot)
+  size_t dVe;       // f32 [BH, m, k, d]
+  size_t dKs;       // f32 [BH, N, d]       shared-part dK
+  size_t dVs;       // f32 [BH, N, d]
+  size_t icnt;      // u32 [BH, N]          experts holding each token
+  size_t icur;      // u32 [BH, N]          fill cursors
+  size_t ioff;      // u32 [BH, N]          list offsets
+  size_t ilist;     // u32 [BH, m k]        (expert, slot) entries per token, in expert order
+  size_t total;
+};
+void backward_plan(const Plan& p, BwdLayout* L);
+// The backward on `stream`: reads the forward's workspace fws, writes fp32 dQ, dK, dV.
+hipError_t launch_backward(const Plan& p, const BwdLayout& L, const void* Q, const void* K, const void* V,
+                           const void* O, const void* dO, float* dQ, float* dK, float* dV, const char* fws, char* bws,
+                           hipStream_t st);
+
 // A value per device, computed once on first use with that device current;
 // safe when several host threads launch at once.
 struct PerDevice {

@@ -19,8 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libmita.so")
 MITA_OK, MITA_ERR_INVALID_ARG, MITA_ERR_UNSUPPORTED, MITA_ERR_WORKSPACE, MITA_ERR_HIP = 0, -1, -2, -3, -4
 MITA_F32, MITA_BF16 = 0, 1
 SYMBOLS = ("mita_workspace_bytes", "mita_forward", "mita_pool", "mita_landmark", "mita_topk", "mita_route",
-           "mita_gather", "mita_combine", "mita_dense_attention", "mita_forward_noalloc", "mita_status_string",
-           "mita_last_error")
+           "mita_gather", "mita_combine", "mita_dense_attention", "mita_forward_noalloc",
+           "mita_backward_workspace_bytes", "mita_backward", "mita_status_string", "mita_last_error")
 NOALLOC_SCRATCH_BYTES = 64 << 20   # MITA_NOALLOC_SCRATCH_BYTES
 
 
@@ -57,8 +57,11 @@ def load() -> ctypes.CDLL:
     lib.mita_combine.argtypes = [vp, i, i, i, vp, sp, vp, sz, vp]
     lib.mita_dense_attention.argtypes = [vp, vp, vp, vp, sp, vp]
     lib.mita_forward_noalloc.argtypes = [vp, vp, vp, i, i, i, vp, sp, vp]
+    lib.mita_backward_workspace_bytes.argtypes = [sp, i, i, i]
+    lib.mita_backward_workspace_bytes.restype = sz
+    lib.mita_backward.argtypes = [vp, vp, vp, vp, vp, i, i, i, vp, vp, vp, sp, vp, sz, vp, sz, vp]
     for f in ("mita_forward", "mita_pool", "mita_landmark", "mita_topk", "mita_route", "mita_gather",
-              "mita_combine", "mita_dense_attention", "mita_forward_noalloc"):
+              "mita_combine", "mita_dense_attention", "mita_forward_noalloc", "mita_backward"):
         getattr(lib, f).restype = ctypes.c_int
     lib.mita_status_string.argtypes = [i]
     lib.mita_status_string.restype = ctypes.c_char_p
@@ -112,6 +115,7 @@ class Mita:
     k: int
     s: int
     workspace: torch.Tensor
+    bwd_workspace: Optional[torch.Tensor] = None
 
     @classmethod
     def create(cls, Q: torch.Tensor, m: int, k: int, s: int, grid=None, pool=None) -> "Mita":
@@ -200,6 +204,29 @@ class Mita:
     def output(self, Q, K, V, out: Optional[torch.Tensor] = None) -> torch.Tensor:
         """Both parts of step 5."""
         return self.combine(Q, self.gather(Q, K, V, out))
+
+    def backward(self, Q, K, V, out, dout, grads=None):
+        """dQ, dK, dV (fp32) of sum(dout * out) for the forward this workspace holds
+        (bf16 only); ``grads`` may give the three output tensors."""
+        self._inputs(Q, K, V, out, dout)
+        sh = self.shape
+        if self.bwd_workspace is None:
+            n = load().mita_backward_workspace_bytes(ctypes.byref(sh), self.m, self.k, self.s)
+            if n == 0:
+                raise ValueError(load().mita_last_error().decode())
+            self.bwd_workspace = torch.empty(n, dtype=torch.uint8, device=Q.device)
+        if grads is None:
+            grads = tuple(torch.empty(Q.shape, dtype=torch.float32, device=Q.device) for _ in range(3))
+        dQ, dK, dV = grads
+        for g_ in grads:
+            if g_.dtype != torch.float32 or g_.shape != Q.shape or not g_.is_contiguous():
+                raise ValueError("gradients must be contiguous fp32 tensors shaped like Q")
+        ws, n = self._ws()
+        _check(load().mita_backward(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(dout), self.m, self.k, self.s,
+                                    _ptr(dQ), _ptr(dK), _ptr(dV), ctypes.byref(sh), ws, n,
+                                    ctypes.c_void_p(self.bwd_workspace.data_ptr()), self.bwd_workspace.numel(),
+                                    _stream()))
+        return dQ, dK, dV
 
 
 def forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, m: int, k: int, s: int, grid=None, pool=None,

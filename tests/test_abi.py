@@ -104,3 +104,21 @@ def test_dense_attention_argument_checks():
         st = lib.mita_dense_attention(*ptrs, ctypes.byref(sh) if sh is not None else None, None)
         assert st == code, (sh and (sh.N, sh.d, sh.dtype), ptrs, st)
         assert lib.mita_last_error()
+
+
+def test_backward_rejects_before_launch():
+    lib = mita.load()
+    sh = shape(dt=mita.MITA_F32)
+    assert lib.mita_backward_workspace_bytes(ctypes.byref(sh), 16, 64, 1) == 0   # bf16 only
+    st = lib.mita_backward(FAKE, FAKE, FAKE, FAKE, FAKE, 16, 64, 1, FAKE, FAKE, FAKE, ctypes.byref(sh), FAKE, 1 << 40,
+                           FAKE, 1 << 40, None)
+    assert st == mita.MITA_ERR_UNSUPPORTED
+    sb = shape(dt=mita.MITA_BF16)
+    n = lib.mita_backward_workspace_bytes(ctypes.byref(sb), 16, 64, 1)
+    assert n > 0 and n % 256 == 0
+    st = lib.mita_backward(FAKE, FAKE, FAKE, FAKE, FAKE, 16, 64, 1, FAKE, FAKE, FAKE, ctypes.byref(sb), FAKE, 1 << 40,
+                           None, n, None)
+    assert st == mita.MITA_ERR_WORKSPACE
+    st = lib.mita_backward(FAKE, FAKE, FAKE, FAKE, FAKE, 16, 64, 1, FAKE, FAKE, FAKE, ctypes.byref(sb), FAKE, 1 << 40,
+                           FAKE, n - 256, None)
+    assert st == mita.MITA_ERR_WORKSPACE

@@ -401,6 +401,92 @@ __device__ __forceinline__ void pv_bf16_swz(const uint16_t* Vs, const f32x4 (&p)
   }
 }
 
+// ---------------------------------------------------------------- tiles read both ways
+// 64-row bf16 tiles (no padding) read as QK operands (16 consecutive rows at one
+// 16-byte chunk) and transposed (8 consecutive rows x 2 neighbouring chunks per
+// half-wave) with one swizzle, chunk c of row r at c ^ f(r): f(r) = 2 (r & 7) |
+// (r >> 3 & 1) for D = 128 (16 distinct values over 16 rows; over 8 aligned rows
+// the even parts differ) and 2 (r >> 1 & 3) | (r >> 3 & 1) for D = 64 (rows are
+// half a bank line, so r & 1 separates neighbours). Filled by direct loads from
+// NW waves (rows w 64 / NW .. of the tile per wave).
+template <int D>
+struct UTile {
+  static constexpr int CPR = D / 8, TILE = kKeyBlock * D, RPI = 512 / D;
+  __device__ static __forceinline__ int swz(int r) {
+    return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+  }
+};
+
+template <int D, int NW, typename RowFn>
+__device__ __forceinline__ void udma(uint16_t* tile, RowFn rowp, int w, int lane) {
+  using U = UTile<D>;
+  constexpr int RPW = kKeyBlock / NW, NI = RPW / U::RPI;
+  static_assert(NI >= 1, "rows per wave below one load instruction");
+  const int p = lane % U::CPR;
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int r0 = w * RPW + u * U::RPI, row = r0 + lane / U::CPR;
+    lds_dma16(rowp(row) + 8 * (p ^ U::swz(row)), tile + r0 * D);
+  }
+}
+
+// Scores of the 64 tile rows against the wave's QT x 16 register rows; with KP =
+// 2 the second tile (the lo plane of Q~) is added after the first at every step,
+// the order qk_bf16<D, 2, 1> uses.
+template <int D, int QT, int KP>
+__device__ __forceinline__ void uqk(const uint16_t* T0, const uint16_t* T1, const uint4 (&qf)[QT][D / 32],
+                                    f32x4 (&acc)[QT][4], int lane) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) acc[qt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    const int off = r * D + 8 * ((4 * ks + g) ^ UTile<D>::swz(r));   // 16 kt keeps the swizzle
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const uint4 a0 = *(const uint4*)(T0 + off + 16 * kt * D);
+      uint4 a1;
+      if constexpr (KP == 2) a1 = *(const uint4*)(T1 + off + 16 * kt * D);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        acc[qt][kt] = mma_bf16(a0, qf[qt][ks], acc[qt][kt]);
+        if constexpr (KP == 2) acc[qt][kt] = mma_bf16(a1, qf[qt][ks], acc[qt][kt]);
+      }
+    }
+  }
+}
+
+// o[qt][dt] += T^T p[qt] (transposed reads of the tile), the order pv_bf16 uses.
+template <int D, int QT>
+__device__ __forceinline__ void upv(const uint16_t* T, const f32x4 (&p)[QT][4], f32x4 (&o)[QT][D / 16], int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int row = 4 * g + (i >> 2);   // + 32 h + 16 hi: bits the swizzle does not use
+  const int sw = UTile<D>::swz(row), b = (i & 3) >> 1;
+  const uint16_t* rb = T + row * D + 4 * (i & 1);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint4 bb[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      bb[qt].x = pack_bf16x2(p[qt][2 * h][0], p[qt][2 * h][1]);
+      bb[qt].y = pack_bf16x2(p[qt][2 * h][2], p[qt][2 * h][3]);
+      bb[qt].z = pack_bf16x2(p[qt][2 * h + 1][0], p[qt][2 * h + 1][1]);
+      bb[qt].w = pack_bf16x2(p[qt][2 * h + 1][2], p[qt][2 * h + 1][3]);
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const int ch = 8 * ((2 * dt + b) ^ sw);
+      const uint2 lo = lds_read_tr16(rb + (32 * h) * D + ch);
+      const uint2 hi = lds_read_tr16(rb + (32 * h + 16) * D + ch);
+      const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) o[qt][dt] = mma_bf16(a, bb[qt], o[qt][dt]);
+    }
+  }
+}
+
 // Write 4 consecutive outputs d0..d0+3 of one row.
 template <typename T>
 __device__ __forceinline__ void store4(T* dst, float a, float b, float c, float d) {

@@ -905,6 +905,107 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Q, c
     store4<T>(orow + 16 * dt + 4 * g, o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
 }
 
+// The same for bf16 inputs with 8 waves of QT column tiles (16 QT NW consecutive
+// queries per workgroup): the landmark blocks (Q~ hi and lo planes,
+// V~) are staged by direct loads into double-buffered tiles that every wave
+// reads (V~ transposed), so each block is fetched once per 16 QT NW queries and
+// each fragment read feeds QT MFMAs. Same arithmetic per query as combine_kernel.
+template <int D, int QT, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void combined_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ qtop, const uint16_t* __restrict__ vt16,
+    const uint16_t* __restrict__ pacc, const float* __restrict__ pml, uint16_t* __restrict__ out, int N, int m, int s,
+    float sl2e, float* __restrict__ lse) {
+  using U = UTile<D>;
+  // one shared object: with separate ones the compiler's LDS scopes would make the
+  // next block's loads look like writes to the block being read
+  __shared__ __align__(16) struct {
+    uint16_t kk[2][2 * U::TILE];   // per buffer: Q~ hi tile, then lo tile
+    uint16_t vv[2][U::TILE];
+  } sm;
+  const int z = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
+  const int qw = blockIdx.x * (16 * QT * NW) + QT * 16 * w + r;   // query of column tile qt: qw + 16 qt
+  const uint16_t* hz = qtop + (size_t)z * 2 * m * D;
+  const uint16_t* lz = hz + (size_t)m * D;
+  const uint16_t* vz = vt16 + (size_t)z * m * D;
+  auto stage = [&](int lb, uint16_t* tk, uint16_t* tv) __attribute__((always_inline)) {
+    udma<D, NW>(tk, [&](int row) __attribute__((always_inline)) { return hz + (size_t)min(lb + row, m - 1) * D; }, w, lane);
+    udma<D, NW>(tk + U::TILE, [&](int row) __attribute__((always_inline)) { return lz + (size_t)min(lb + row, m - 1) * D; }, w, lane);
+    udma<D, NW>(tv, [&](int row) __attribute__((always_inline)) { return vz + (size_t)min(lb + row, m - 1) * D; }, w, lane);
+  };
+  stage(0, sm.kk[0], sm.vv[0]);
+  // seed: per query, M = the largest partial reference; o, l = the partials rescaled to it
+  // (l on one lane of the quad: the lanes' sums are added at the end)
+  uint4 qf[QT][D / 32];
+  float mrun[QT], lrun[QT];
+  f32x4 o[QT][D / 16];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int qc = min(qw + 16 * qt, N - 1);
+    const uint16_t* qrow = Q + ((size_t)z * N + qc) * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) qf[qt][ks] = ld16(qrow + 32 * ks + 8 * g);
+    const size_t p0 = ((size_t)z * N + qc) * s;
+    float M = -INFINITY;
+    for (int sl = 0; sl < s; ++sl) M = fmaxf(M, pml[(p0 + sl) * 4]);
+    float l = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sl = 0; sl < s; ++sl) {
+      const float4 ml = *(const float4*)(pml + (p0 + sl) * 4);
+      const float f = exp2f(ml.x - M);
+      l += f * ml.y;
+      const float wv = f * ml.y * ml.z;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const uint2 u = *(const uint2*)(pacc + (p0 + sl) * D + 16 * dt + 4 * g);
+        o[qt][dt][0] += wv * f16_lo(u.x);
+        o[qt][dt][1] += wv * f16_hi(u.x);
+        o[qt][dt][2] += wv * f16_lo(u.y);
+        o[qt][dt][3] += wv * f16_hi(u.y);
+      }
+    }
+    mrun[qt] = M;
+    lrun[qt] = g != 0 ? 0.f : l;
+  }
+  const int nb = (m + kKeyBlock - 1) / kKeyBlock;
+  for (int j = 0; j < nb; ++j) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();   // block j staged; every wave done with block j - 1
+    // the next block's loads and this block's reads go through distinct __restrict__
+    // parameters, so the compiler does not wait for the loads before the reads
+    auto step = [&](uint16_t* __restrict__ nk, uint16_t* __restrict__ nv, const uint16_t* __restrict__ ck,
+                    const uint16_t* __restrict__ cv) __attribute__((always_inline)) {
+      // unconditional (rows clamp to the last landmark): a branch around the loads
+      // would merge two states here and the compiler would then wait for them
+      stage((j + 1) * kKeyBlock, nk, nv);
+      f32x4 acc[QT][4];
+      __builtin_amdgcn_s_setprio(1);
+      uqk<D, QT, 2>(ck, ck + U::TILE, qf, acc, lane);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const float alpha = online_softmax(acc[qt], min(kKeyBlock, m - j * kKeyBlock), sl2e, mrun[qt], lrun[qt], lane);
+        rescale<D>(o[qt], alpha);
+      }
+      upv<D, QT>(cv, acc, o, lane);
+      __builtin_amdgcn_s_setprio(0);
+    };
+    const int b = j & 1, nbuf = (j + 1) & 1;
+    step(sm.kk[nbuf], sm.vv[nbuf], sm.kk[b], sm.vv[b]);
+  }
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int q = qw + 16 * qt;
+    const float lt = quad_sum(lrun[qt]), inv = 1.f / lt;
+    if (q >= N) continue;
+    if (g == 0) lse[(size_t)z * N + q] = mrun[qt] + log2f(lt);
+    uint16_t* orow = out + ((size_t)z * N + q) * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+      store4<uint16_t>(orow + 16 * dt + 4 * g, o[qt][dt][0] * inv, o[qt][dt][1] * inv, o[qt][dt][2] * inv,
+                       o[qt][dt][3] * inv);
+  }
+}
+
 // Counting sort of the (query, slot) pairs by expert and the tile table.
 hipError_t launch_bucket(const Plan& p, char* ws, hipStream_t st) {
   const int Ns = p.N * p.s;
@@ -995,6 +1096,14 @@ template <typename T, int D>
 static hipError_t combine_launch(const Plan& p, const void* Q, void* out, char* ws, hipStream_t st) {
   const float sl2e = (float)(1.4426950408889634 / sqrt((double)D));
   const void* vtop = p.dtype == MITA_BF16 ? (const void*)(ws + p.ws.vt16) : (const void*)(ws + p.ws.vt32);
+  if constexpr (sizeof(T) == 2) {   // bf16: waves of 2 column tiles; 8 waves for d = 128 (96 KB of LDS), 4 for 64
+    constexpr int QT = 2, NW = D == 128 ? 8 : 4, QPW = 16 * QT * NW;
+    hipLaunchKernelGGL((combined_kernel<D, QT, NW>), dim3((p.N + QPW - 1) / QPW, p.BH), dim3(64 * NW), 0, st,
+                       (const uint16_t*)Q, (const uint16_t*)(ws + p.ws.qtop), (const uint16_t*)vtop,
+                       (const uint16_t*)(ws + p.ws.pacc), (const float*)(ws + p.ws.pml), (uint16_t*)out, p.N, p.m, p.s,
+                       sl2e, (float*)(ws + p.ws.lse));
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((combine_kernel<T, D>), dim3(p.qtiles, p.BH), dim3(256), 0, st, (const T*)Q,
                      (const void*)(ws + p.ws.qtop), vtop, (const void*)(ws + p.ws.pacc), (const float*)(ws + p.ws.pml),
                      (T*)out, p.N, p.m, p.s, sl2e, (float*)(ws + p.ws.lse));

@@ -97,7 +97,7 @@ def kernel_names(w) -> dict:
         gather = "gatherd_kernel" if w.dtype == "bf16" else "gather_kernel"
     return {"pool": "pool_kernel", "landmark": "landmark_kernel", "topk": "topk_cand_kernel",
             "route": "route_fast_kernel" if w.m <= 64 else "route_multi_kernel", "gather": gather,
-            "combine": "combine_kernel"}
+            "combine": "combined_kernel" if w.dtype == "bf16" else "combine_kernel"}
 
 
 def sources_sha256(step: str) -> str:
@@ -316,6 +316,52 @@ def dense_compare(w, Qd, Kd, Vd, steps: int, warmup: int) -> int:
     return 0
 
 
+def backward_bench(w, Qd, Kd, Vd, steps: int, warmup: int) -> int:
+    """Forward and backward (mita_backward: dQ, dK, dV of sum(dout * out), expert sets
+    and routing held fixed) on the workload's inputs: mean time of each with HIP
+    events on the library's stream, and the backward's algorithmic MFMA rate: 5
+    contractions per (query, key) pair (scores recomputed, dO V^T, dS K, dS^T Q,
+    P^T dO), 10 d flops per pair, over the routed pairs (N k s per slice) and the
+    landmark pairs of the final attention and of the shared expert (N m each)."""
+    import torch
+
+    from sparse_top_routed_amd import mita
+
+    if w.dtype != "bf16":
+        print("the backward supports bf16 inputs only", file=sys.stderr)
+        return 2
+    st = torch.cuda.current_stream()
+    call = mita.Mita.create(Qd, w.m, w.k, w.s, grid=(w.grid_h, w.grid_w), pool=(w.pool_h, w.pool_w))
+    out = torch.empty_like(Qd)
+    dout = torch.randn(Qd.shape, device="cuda", generator=torch.Generator("cuda").manual_seed(3)).to(torch.bfloat16)
+    grads = tuple(torch.empty(Qd.shape, dtype=torch.float32, device="cuda") for _ in range(3))
+    for _ in range(warmup):
+        call.forward(Qd, Kd, Vd, out)
+        call.backward(Qd, Kd, Vd, out, dout, grads)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    fwd = bwd = 0.0
+    for _ in range(steps):
+        ev[0].record(st)
+        call.forward(Qd, Kd, Vd, out)
+        ev[1].record(st)
+        call.backward(Qd, Kd, Vd, out, dout, grads)
+        ev[2].record(st)
+        torch.cuda.synchronize()
+        fwd += ev[0].elapsed_time(ev[1])
+        bwd += ev[1].elapsed_time(ev[2])
+    fwd, bwd = fwd / steps, bwd / steps
+    flops = 10.0 * w.slices * w.d * (w.N * w.k * w.s + 2 * w.N * w.m)
+    tf = flops / (bwd * 1e-3) / 1e12
+    res = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "m": w.m, "k": w.k, "s": w.s,
+           "dtype": w.dtype, "steps": steps, "warmup": warmup, "forward_ms": fwd, "backward_ms": bwd,
+           "fwd_bwd_query_tokens_per_s": w.slices * w.N / ((fwd + bwd) * 1e-3),
+           "backward_algorithmic_tflop": flops / 1e12, "backward_tflops": tf,
+           "backward_mfma_frac": tf / BF16_PEAK_TFLOPS}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def _cpu_workers(requested: int) -> int:
     have = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
     return max(1, min(requested or have, have, 16))
@@ -340,6 +386,9 @@ def main() -> int:
     ap.add_argument("--sweep", action="store_true",
                     help="time the forward pass over the inference-time (m, k, s) settings of synth.SWEEP on the "
                          "workload's inputs (one JSON line per setting) instead of the benchmark line")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the forward and the backward (mita_backward) on the workload's inputs (one JSON line) "
+                         "instead of the benchmark line")
     ap.add_argument("--dense", action="store_true",
                     help="time the full-attention comparator against the MiTA forward on the workload's inputs "
                          "(one JSON line) instead of the benchmark line")
@@ -361,7 +410,7 @@ def main() -> int:
     # the CPU baseline runs first, before anything touches the GPU: its worker
     # processes start from a clean interpreter and never share the GPU timing
     cpu = None
-    if not (a.no_cpu or a.sweep or a.dense):
+    if not (a.no_cpu or a.sweep or a.dense or a.backward):
         cpu = cpu_baseline(w, _cpu_workers(a.cpu_workers))
 
     import torch
@@ -381,6 +430,8 @@ def main() -> int:
         return sweep(w, Qd, Kd, Vd, a.steps, a.warmup, a.breakdown)
     if a.dense:
         return dense_compare(w, Qd, Kd, Vd, a.steps, a.warmup)
+    if a.backward:
+        return backward_bench(w, Qd, Kd, Vd, a.steps, a.warmup)
     call = mita.Mita.create(Qd, w.m, w.k, w.s, grid=(w.grid_h, w.grid_w), pool=(w.pool_h, w.pool_w))
     out = torch.empty_like(Qd)
     for _ in range(a.warmup):

@@ -195,6 +195,62 @@ __device__ __forceinline__ void rescale(f32x4 (&o)[D / 16], float alpha) {
     for (int j = 0; j < 4; ++j) o[dt][j] *= alpha;
 }
 
+// Softmax of one block for QT column tiles against a lazily raised reference
+// (log2 domain, p = 2^(c s - mrun)): a row's reference moves up to its block
+// maximum only when that maximum exceeds it by more than kLazyLog2, and only then
+// are the row's output and sum rescaled (one wave-uniform branch for all tiles).
+// Numerator and denominator share the reference, so the softmax is unchanged;
+// the probabilities stay below 2^kLazyLog2. Row sums are left to the caller.
+constexpr float kLazyLog2 = 8.f;
+
+template <int D, int QT>
+__device__ __forceinline__ void lazy_softmax(f32x4 (&x)[QT][4], int live, float c, float (&mrun)[QT],
+                                             float (&lrun)[QT], f32x4 (&o)[QT][D / 16], int lane) {
+  float bm[QT];
+  bool any = false;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    if (live < kKeyBlock) {   // block-uniform; key 16 kt + 4 g + j is masked when 16 kt + j >= live - 4 g
+      const int lim = live - 4 * (lane >> 4);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (16 * kt + j >= lim) x[qt][kt][j] = -INFINITY;
+    }
+    float v = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v = fmaxf(v, x[qt][kt][j]);
+    bm[qt] = quad_max(v) * c;
+    any |= bm[qt] > mrun[qt] + kLazyLog2;
+  }
+  if (__builtin_amdgcn_ballot_w64(any) != 0) {   // wave-uniform
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const bool up = bm[qt] > mrun[qt] + kLazyLog2;
+      // raw v_exp_f32; 2^(-inf) = 0 clears the empty state of the first block
+      const float alpha = up ? __builtin_amdgcn_exp2f(mrun[qt] - bm[qt]) : 1.f;
+      mrun[qt] = up ? bm[qt] : mrun[qt];
+      lrun[qt] *= alpha;
+      rescale<D>(o[qt], alpha);
+    }
+  }
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[qt][kt][j] = __builtin_amdgcn_exp2f(fmaf(x[qt][kt][j], c, -mrun[qt]));
+}
+
+// Sum of the two bf16 halves of w added to acc (one v_dot2 with (1, 1)).
+__device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3F803F80u),
+                                         acc, false);
+}
+
 // O^T += V^T P^T for bf16: o[dt] holds O^T[16*dt + 4*(lane/16) + j][lane%16].
 template <int D>
 __device__ __forceinline__ void pv_bf16(const uint16_t* Vt, const f32x4 (&p)[4], f32x4 (&o)[D / 16], int lane) {
@@ -368,12 +424,13 @@ __device__ __forceinline__ void qk_bf16_swz(const uint16_t* Ks, const uint4 (&qf
   }
 }
 
-// P V from a swizzled row-major V tile: V^T fragments by transposed reads. Lane (r,
+// P V from a swizzled row-major V tile: V^T fragments by transposed reads; the
+// lane's probabilities (bf16, as multiplied) are added to lsum. Lane (r,
 // g) needs rows (keys) 4 q .. 4 q + 3 of column (d) 16 dt + r with q = 8 h + g (low
 // half) or 8 h + 4 + g (high half): the 4 x 16 patch of rows 4 q .. and columns 16 dt ..
 template <int D, int QT>
 __device__ __forceinline__ void pv_bf16_swz(const uint16_t* Vs, const f32x4 (&p)[QT][4], f32x4 (&o)[QT][D / 16],
-                                            int lane) {
+                                            float (&lsum)[QT], int lane) {
   using S = SwzTile<D>;
   const int g = lane >> 4, i = lane & 15;
   const int row = 4 * g + (i >> 2);           // + 32 h + 16 hi: multiples of 8, same swizzle
@@ -388,6 +445,8 @@ __device__ __forceinline__ void pv_bf16_swz(const uint16_t* Vs, const f32x4 (&p)
       bb[qt].y = pack_bf16x2(p[qt][2 * h][2], p[qt][2 * h][3]);
       bb[qt].z = pack_bf16x2(p[qt][2 * h + 1][0], p[qt][2 * h + 1][1]);
       bb[qt].w = pack_bf16x2(p[qt][2 * h + 1][2], p[qt][2 * h + 1][3]);
+      // the row sum adds the probabilities as rounded for the product
+      lsum[qt] = add_bf16x2(bb[qt].w, add_bf16x2(bb[qt].z, add_bf16x2(bb[qt].y, add_bf16x2(bb[qt].x, lsum[qt]))));
     }
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
@@ -460,7 +519,8 @@ __device__ __forceinline__ void uqk(const uint16_t* T0, const uint16_t* T1, cons
 
 // o[qt][dt] += T^T p[qt] (transposed reads of the tile), the order pv_bf16 uses.
 template <int D, int QT>
-__device__ __forceinline__ void upv(const uint16_t* T, const f32x4 (&p)[QT][4], f32x4 (&o)[QT][D / 16], int lane) {
+__device__ __forceinline__ void upv(const uint16_t* T, const f32x4 (&p)[QT][4], f32x4 (&o)[QT][D / 16],
+                                    float (&lsum)[QT], int lane) {
   const int g = lane >> 4, i = lane & 15;
   const int row = 4 * g + (i >> 2);   // + 32 h + 16 hi: bits the swizzle does not use
   const int sw = UTile<D>::swz(row), b = (i & 3) >> 1;
@@ -474,6 +534,8 @@ __device__ __forceinline__ void upv(const uint16_t* T, const f32x4 (&p)[QT][4], 
       bb[qt].y = pack_bf16x2(p[qt][2 * h][2], p[qt][2 * h][3]);
       bb[qt].z = pack_bf16x2(p[qt][2 * h + 1][0], p[qt][2 * h + 1][1]);
       bb[qt].w = pack_bf16x2(p[qt][2 * h + 1][2], p[qt][2 * h + 1][3]);
+      // the row sum adds the probabilities as rounded for the product
+      lsum[qt] = add_bf16x2(bb[qt].w, add_bf16x2(bb[qt].z, add_bf16x2(bb[qt].y, add_bf16x2(bb[qt].x, lsum[qt]))));
     }
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {

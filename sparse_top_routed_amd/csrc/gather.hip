@@ -481,7 +481,9 @@ void gather_kernel(const T* __restrict__ Q, const T* __restrict__ K,
 // next tile's query rows load into the registers of the current ones once its
 // last scores are taken. V stays row-major and is read transposed. While a wave's
 // MFMA work is in flight its priority is raised, so the other wave of the SIMD
-// does its softmax meanwhile. Held to two waves per SIMD.
+// does its softmax meanwhile. Held to two waves per SIMD. The softmax keeps a
+// lazily raised reference and sums the probabilities as rounded for P V
+// (lazy_softmax).
 template <int D>
 struct GatherDLds {
   __align__(16) uint16_t rk[2][SwzTile<D>::TILE];
@@ -491,7 +493,9 @@ struct GatherDLds {
   uint32_t wtot[4];
 };
 
-template <int D, int QT>
+// KFULL: k is a multiple of the key block (no block of an expert is partial, and
+// the kernel carries no masking code).
+template <int D, int QT, bool KFULL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gatherd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const int32_t* __restrict__ I, const int4* __restrict__ tiles, const int32_t* __restrict__ perm,
@@ -608,20 +612,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
           dma_rows<D>(nk, nv, K + (size_t)z_n * N * D, V + (size_t)z_n * N * D, id_n, w, lane);
         ids(j + 2, id_n, z_n);
         const bool live = QT * 16 * w < cur.z;   // the wave has live rows (wave-uniform)
-        f32x4 acc[QT][4];
+        // the scores live inside one branch (merging them with an idle path would
+        // cost a register fill per block); the next tile's query rows (block-
+        // uniform) are loaded once the scores no longer need qf
         if (live) {
+          f32x4 acc[QT][4];
           __builtin_amdgcn_s_setprio(kGatherPrio);
           qk_bf16_swz<D, QT>(ck, qf, acc, lane);
-        }
-        if (lastblk) qload(ti + 1, qe_n, qf);   // the next tile's query rows (block-uniform)
-        if (live) {
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) {
-            const float alpha = online_softmax(acc[qt], min(kKeyBlock, k - kb), sl2e, mrun[qt], lrun[qt], lane);
-            rescale<D>(o[qt], alpha);
-          }
-          pv_bf16_swz<D, QT>(cv, acc, o, lane);
+          if (lastblk) qload(ti + 1, qe_n, qf);
+          lazy_softmax<D, QT>(acc, KFULL ? kKeyBlock : min(kKeyBlock, k - kb), sl2e, mrun, lrun, o, lane);
+          pv_bf16_swz<D, QT>(cv, acc, o, lrun, lane);
           __builtin_amdgcn_s_setprio(0);
+        } else if (lastblk) {
+          qload(ti + 1, qe_n, qf);
         }
       };
       step(sm.rk[(j + 1) & 1], sm.rv[(j + 1) & 1], sm.rk[j & 1], sm.rv[j & 1]);
@@ -909,8 +912,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Q, c
 // queries per workgroup): the landmark blocks (Q~ hi and lo planes,
 // V~) are staged by direct loads into double-buffered tiles that every wave
 // reads (V~ transposed), so each block is fetched once per 16 QT NW queries and
-// each fragment read feeds QT MFMAs. Same arithmetic per query as combine_kernel.
-template <int D, int QT, int NW>
+// each fragment read feeds QT MFMAs. The softmax keeps a lazily raised reference
+// and sums the probabilities as rounded for the product (see lazy_softmax).
+// MFULL: m is a multiple of the key block (no masking code).
+template <int D, int QT, int NW, bool MFULL>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void combined_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ qtop, const uint16_t* __restrict__ vt16,
     const uint16_t* __restrict__ pacc, const float* __restrict__ pml, uint16_t* __restrict__ out, int N, int m, int s,
@@ -981,12 +986,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       f32x4 acc[QT][4];
       __builtin_amdgcn_s_setprio(1);
       uqk<D, QT, 2>(ck, ck + U::TILE, qf, acc, lane);
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        const float alpha = online_softmax(acc[qt], min(kKeyBlock, m - j * kKeyBlock), sl2e, mrun[qt], lrun[qt], lane);
-        rescale<D>(o[qt], alpha);
-      }
-      upv<D, QT>(cv, acc, o, lane);
+      lazy_softmax<D, QT>(acc, MFULL ? kKeyBlock : min(kKeyBlock, m - j * kKeyBlock), sl2e, mrun, lrun, o, lane);
+      upv<D, QT>(cv, acc, o, lrun, lane);
       __builtin_amdgcn_s_setprio(0);
     };
     const int b = j & 1, nbuf = (j + 1) & 1;
@@ -1071,7 +1072,7 @@ static hipError_t gather_launch(const Plan& p, const void* Q, const void* K, con
     return hipGetLastError();
   }
   if constexpr (sizeof(T) == 2) {   // bf16 partials: the direct-load kernel, 1 or 2 column tiles per wave
-    static PerDevice c_q1, c_q2;
+    static PerDevice c_q1, c_q2, c_q1f, c_q2f;
     auto go = [&](auto kern, PerDevice& cache) {
       const int sl = n_cu * resident_per_cu(cache, kern, 256);
       const int gq = std::max(1, std::min(8, sl / 8));
@@ -1082,7 +1083,12 @@ static hipError_t gather_launch(const Plan& p, const void* Q, const void* K, con
                          (const int32_t*)(ws + p.ws.perm), (uint16_t*)(ws + p.ws.pacc), (float*)(ws + p.ws.pml), p.N,
                          p.m, p.k, p.s, p.max_tiles, total, gc, gq, sl2e);
     };
-    if (p.gqt == 2) go(gatherd_kernel<D, 2>, c_q2); else go(gatherd_kernel<D, 1>, c_q1);
+    const bool kfull = p.k % kKeyBlock == 0;
+    if (p.gqt == 2) {
+      if (kfull) go(gatherd_kernel<D, 2, true>, c_q2f); else go(gatherd_kernel<D, 2, false>, c_q2);
+    } else {
+      if (kfull) go(gatherd_kernel<D, 1, true>, c_q1f); else go(gatherd_kernel<D, 1, false>, c_q1);
+    }
     return hipGetLastError();
   }
   hipLaunchKernelGGL((gather_kernel<T, D, false>), dim3(grid), dim3(256), 0, st, (const T*)Q, (const T*)K, (const T*)V,
@@ -1098,10 +1104,10 @@ static hipError_t combine_launch(const Plan& p, const void* Q, void* out, char* 
   const void* vtop = p.dtype == MITA_BF16 ? (const void*)(ws + p.ws.vt16) : (const void*)(ws + p.ws.vt32);
   if constexpr (sizeof(T) == 2) {   // bf16: waves of 2 column tiles; 8 waves for d = 128 (96 KB of LDS), 4 for 64
     constexpr int QT = 2, NW = D == 128 ? 8 : 4, QPW = 16 * QT * NW;
-    hipLaunchKernelGGL((combined_kernel<D, QT, NW>), dim3((p.N + QPW - 1) / QPW, p.BH), dim3(64 * NW), 0, st,
-                       (const uint16_t*)Q, (const uint16_t*)(ws + p.ws.qtop), (const uint16_t*)vtop,
-                       (const uint16_t*)(ws + p.ws.pacc), (const float*)(ws + p.ws.pml), (uint16_t*)out, p.N, p.m, p.s,
-                       sl2e, (float*)(ws + p.ws.lse));
+    auto kern = p.m % kKeyBlock == 0 ? combined_kernel<D, QT, NW, true> : combined_kernel<D, QT, NW, false>;
+    hipLaunchKernelGGL(kern, dim3((p.N + QPW - 1) / QPW, p.BH), dim3(64 * NW), 0, st, (const uint16_t*)Q,
+                       (const uint16_t*)(ws + p.ws.qtop), (const uint16_t*)vtop, (const uint16_t*)(ws + p.ws.pacc),
+                       (const float*)(ws + p.ws.pml), (uint16_t*)out, p.N, p.m, p.s, sl2e, (float*)(ws + p.ws.lse));
     return hipGetLastError();
   }
   hipLaunchKernelGGL((combine_kernel<T, D>), dim3(p.qtiles, p.BH), dim3(256), 0, st, (const T*)Q,

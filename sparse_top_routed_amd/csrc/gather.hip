@@ -914,8 +914,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Q, c
 // reads (V~ transposed), so each block is fetched once per 16 QT NW queries and
 // each fragment read feeds QT MFMAs. The softmax keeps a lazily raised reference
 // and sums the probabilities as rounded for the product (see lazy_softmax).
-// MFULL: m is a multiple of the key block (no masking code).
-template <int D, int QT, int NW, bool MFULL>
+// MFULL: m is a multiple of the key block (no masking code). SU: partial slots
+// loaded together in the seed (1, 2 or 4).
+template <int D, int QT, int NW, bool MFULL, int SU>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void combined_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ qtop, const uint16_t* __restrict__ vt16,
     const uint16_t* __restrict__ pacc, const float* __restrict__ pml, uint16_t* __restrict__ out, int N, int m, int s,
@@ -939,35 +940,60 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   };
   stage(0, sm.kk[0], sm.vv[0]);
   // seed: per query, M = the largest partial reference; o, l = the partials rescaled to it
-  // (l on one lane of the quad: the lanes' sums are added at the end)
+  // (l on one lane of the quad: the lanes' sums are added at the end). The first SU
+  // slots' loads are all issued before any is used (slots past s repeat slot s - 1
+  // with weight 0); slots past SU follow one at a time.
   uint4 qf[QT][D / 32];
   float mrun[QT], lrun[QT];
   f32x4 o[QT][D / 16];
+  size_t p0[QT];
+  float4 ml[QT][SU];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int qc = min(qw + 16 * qt, N - 1);
     const uint16_t* qrow = Q + ((size_t)z * N + qc) * D;
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) qf[qt][ks] = ld16(qrow + 32 * ks + 8 * g);
-    const size_t p0 = ((size_t)z * N + qc) * s;
+    p0[qt] = ((size_t)z * N + qc) * s;
+#pragma unroll
+    for (int sl = 0; sl < SU; ++sl) ml[qt][sl] = *(const float4*)(pml + (p0[qt] + min(sl, s - 1)) * 4);
+  }
+  uint2 u[QT][SU][D / 16];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int sl = 0; sl < SU; ++sl)
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+        u[qt][sl][dt] = *(const uint2*)(pacc + (p0[qt] + min(sl, s - 1)) * D + 16 * dt + 4 * g);
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
     float M = -INFINITY;
-    for (int sl = 0; sl < s; ++sl) M = fmaxf(M, pml[(p0 + sl) * 4]);
+#pragma unroll
+    for (int sl = 0; sl < SU; ++sl) M = fmaxf(M, ml[qt][sl].x);
+    for (int sl = SU; sl < s; ++sl) M = fmaxf(M, pml[(p0[qt] + sl) * 4]);
     float l = 0.f;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) o[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int sl = 0; sl < s; ++sl) {
-      const float4 ml = *(const float4*)(pml + (p0 + sl) * 4);
-      const float f = exp2f(ml.x - M);
-      l += f * ml.y;
-      const float wv = f * ml.y * ml.z;
+    auto add = [&](const float4& m4, const uint2 (&uu)[D / 16], bool use) __attribute__((always_inline)) {
+      const float f = use ? exp2f(m4.x - M) : 0.f;
+      l += f * m4.y;
+      const float wv = f * m4.y * m4.z;
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
-        const uint2 u = *(const uint2*)(pacc + (p0 + sl) * D + 16 * dt + 4 * g);
-        o[qt][dt][0] += wv * f16_lo(u.x);
-        o[qt][dt][1] += wv * f16_hi(u.x);
-        o[qt][dt][2] += wv * f16_lo(u.y);
-        o[qt][dt][3] += wv * f16_hi(u.y);
+        o[qt][dt][0] += wv * f16_lo(uu[dt].x);
+        o[qt][dt][1] += wv * f16_hi(uu[dt].x);
+        o[qt][dt][2] += wv * f16_lo(uu[dt].y);
+        o[qt][dt][3] += wv * f16_hi(uu[dt].y);
       }
+    };
+#pragma unroll
+    for (int sl = 0; sl < SU; ++sl) add(ml[qt][sl], u[qt][sl], sl < s);
+    for (int sl = SU; sl < s; ++sl) {
+      uint2 ut[D / 16];
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) ut[dt] = *(const uint2*)(pacc + (p0[qt] + sl) * D + 16 * dt + 4 * g);
+      add(*(const float4*)(pml + (p0[qt] + sl) * 4), ut, true);
     }
     mrun[qt] = M;
     lrun[qt] = g != 0 ? 0.f : l;
@@ -1104,7 +1130,13 @@ static hipError_t combine_launch(const Plan& p, const void* Q, void* out, char* 
   const void* vtop = p.dtype == MITA_BF16 ? (const void*)(ws + p.ws.vt16) : (const void*)(ws + p.ws.vt32);
   if constexpr (sizeof(T) == 2) {   // bf16: waves of 2 column tiles; 8 waves for d = 128 (96 KB of LDS), 4 for 64
     constexpr int QT = 2, NW = D == 128 ? 8 : 4, QPW = 16 * QT * NW;
-    auto kern = p.m % kKeyBlock == 0 ? combined_kernel<D, QT, NW, true> : combined_kernel<D, QT, NW, false>;
+    const bool mfull = p.m % kKeyBlock == 0;
+    auto pick = [&](auto su) {
+      constexpr int SU = decltype(su)::value;
+      return mfull ? combined_kernel<D, QT, NW, true, SU> : combined_kernel<D, QT, NW, false, SU>;
+    };
+    auto kern = p.s == 1 ? pick(std::integral_constant<int, 1>{})
+              : p.s == 2 ? pick(std::integral_constant<int, 2>{}) : pick(std::integral_constant<int, 4>{});
     hipLaunchKernelGGL(kern, dim3((p.N + QPW - 1) / QPW, p.BH), dim3(64 * NW), 0, st, (const uint16_t*)Q,
                        (const uint16_t*)(ws + p.ws.qtop), (const uint16_t*)vtop, (const uint16_t*)(ws + p.ws.pacc),
                        (const float*)(ws + p.ws.pml), (uint16_t*)out, p.N, p.m, p.s, sl2e, (float*)(ws + p.ws.lse));

@@ -58,9 +58,14 @@ def slice_f64(x: np.ndarray, dtype: str, z: int) -> np.ndarray:
 
 
 def check_slice(w: synth.Workload, Q, K, V, gpu: Dict[str, np.ndarray], z: int,
-                queries: Optional[Sequence[int]] = None, check_s: bool = True) -> Dict[str, float]:
+                queries: Optional[Sequence[int]] = None, check_s: bool = True,
+                route_all: bool = False, near_margin: int = 0) -> Dict[str, float]:
     """Compare slice z of the GPU results with the oracle. Raises AssertionError on
-    a parity failure and returns a few statistics."""
+    a parity failure and returns a few statistics.
+
+    queries: the queries whose routing and output are checked (all when None).
+    route_all: check the routing of every query of the slice, and the output on
+    `queries` plus the `near_margin` queries whose routing margin is smallest."""
     q64, k64, v64 = (slice_f64(x, w.dtype, z) for x in (Q, K, V))
     d = w.d
     Qt = oracle.pool(q64, w.grid_h, w.grid_w, w.pool_h, w.pool_w)
@@ -97,14 +102,18 @@ def check_slice(w: synth.Workload, Q, K, V, gpu: Dict[str, np.ndarray], z: int,
 
     N = w.N
     qsel = np.arange(N) if queries is None else np.asarray(queries)
-    R = oracle.route_scores(q64[qsel], Qt)
+    rsel = np.arange(N) if route_all else qsel
+    R = oracle.route_scores(q64[rsel], Qt)
     g_E = gpu["E"].reshape(-1, N, w.s)[z].astype(np.int64)
-    ok_E = oracle.valid_route_sets(R, g_E[qsel], w.s)
-    assert ok_E.all(), f"slice {z}: {np.count_nonzero(~ok_E)} invalid routings (queries {qsel[~ok_E][:8]})"
-    E_or = oracle.route(q64[qsel], Qt, w.s)
+    ok_E = oracle.valid_route_sets(R, g_E[rsel], w.s)
+    assert ok_E.all(), f"slice {z}: {np.count_nonzero(~ok_E)} invalid routings (queries {rsel[~ok_E][:8]})"
+    E_or = oracle.route(q64[rsel], Qt, w.s)
     rmarg = oracle.route_margins(R, w.s)
-    same_E = (np.sort(g_E[qsel], axis=1) == np.sort(E_or, axis=1)).all(axis=1)
+    del R
+    same_E = (np.sort(g_E[rsel], axis=1) == np.sort(E_or, axis=1)).all(axis=1)
     assert same_E[rmarg >= 1e-6].all(), f"slice {z}: a routing differs on a query with a clear margin"
+    if near_margin:   # the output of the queries nearest a routing tie is checked too
+        qsel = np.union1d(qsel, rsel[np.argsort(rmarg, kind="stable")[:near_margin]])
 
     # output, recomputed by the oracle with the GPU's (validated) sets
     O = oracle.attend(q64, k64, v64, Qt, Vt, g_I, g_E, qsel)

@@ -160,7 +160,22 @@ def test_invalid_arguments_raise(lib):
 
 
 FULL = ["vit_b", "seg", "long", "very_long"]
-FULL_SLICES = {"vit_b": [0, 383], "seg": [0, 95], "long": [31], "very_long": [5]}
+# slices z = b H + h checked at full size: two per workload, different heads (and
+# batch entries where there is more than one)
+FULL_SLICES = {"vit_b": [0, 383], "seg": [0, 95], "long": [3, 28], "very_long": [2, 6]}
+FULL_QUERIES = 2048   # random queries per slice whose output is checked
+
+
+def full_size_queries(E_z: np.ndarray, N: int, rng) -> np.ndarray:
+    """Queries whose output is checked: a random sample, plus the highest query
+    routed to each expert (the tail of every expert's bucket, so partially filled
+    last tiles are covered)."""
+    rand = rng.choice(N, size=min(N, FULL_QUERIES), replace=False)
+    flat_e = E_z.reshape(-1)
+    flat_q = np.repeat(np.arange(N), E_z.shape[1])
+    last = np.full(int(flat_e.max()) + 1, -1, dtype=np.int64)
+    np.maximum.at(last, flat_e, flat_q)
+    return np.union1d(rand, last[last >= 0])
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -188,9 +203,10 @@ def test_full_size_sampled(name, lib):
     del Qd, Kd, Vd, call
     rng = np.random.default_rng(1)
     for z in FULL_SLICES[name]:
-        queries = np.sort(rng.choice(w.N, size=min(w.N, 192), replace=False))
-        say(f"[parity-full] {name}: oracle on slice {z}")
-        st = check_slice(w, Q, K, V, gpu, z, queries=queries, check_s=False)
+        queries = full_size_queries(gpu["E"].reshape(-1, w.N, w.s)[z], w.N, rng)
+        say(f"[parity-full] {name}: oracle on slice {z} (routing of all {w.N} queries, output of "
+            f"{len(queries)} + 256 nearest a routing tie)")
+        st = check_slice(w, Q, K, V, gpu, z, queries=queries, check_s=False, route_all=True, near_margin=256)
         say(f"  slice {z}: {st}")
 
 

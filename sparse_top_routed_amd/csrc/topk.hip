@@ -151,8 +151,9 @@ __device__ __forceinline__ void load_group_keys(const float* br, int nbg, int la
 // (lane l: columns l, l + 64, ...), and the row's candidate threshold is set
 // from its group maxima (at most 64 PV, in registers). Merging here, where each
 // row's maxima are read anyway, saves a launch between the two steps. CB chunks'
-// partials are loaded at once: 8, or 4 when there are at most 4 chunks (no lane
-// then loads clamped duplicates; 4 us less on the ViT-B-like forward).
+// partials are loaded at once: 8, or 4 when there are at most 4 chunks (fewer
+// clamped duplicate loads when nsplit < 8, none when nsplit = 4; 4 us less on the
+// ViT-B-like forward, which has 3 chunks).
 template <int D, int PV, int CB>
 __global__ __launch_bounds__(256) void merge_thresh_kernel(const float* __restrict__ lpart,
                                                            float* __restrict__ vt32, uint16_t* __restrict__ vt16,

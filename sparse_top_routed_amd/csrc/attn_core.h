@@ -424,6 +424,33 @@ __device__ __forceinline__ void qk_bf16_swz(const uint16_t* Ks, const uint4 (&qf
   }
 }
 
+// QT column tiles of scores from a swizzled K tile against two query planes
+// (hi, lo): per accumulator the MFMA sequence of qk_bf16<D, 1, 2> (k-slices in
+// order, hi then lo), so the scores are the same bits.
+template <int D, int QT>
+__device__ __forceinline__ void qk2_bf16_swz(const uint16_t* Ks, const uint4 (&qb)[QT][2][D / 32],
+                                             f32x4 (&acc)[QT][4], int lane) {
+  using S = SwzTile<D>;
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) acc[qt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    const uint16_t* col = Ks + r * D + 8 * ((4 * ks + g) ^ S::swz_k(r));
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const uint4 a0 = *(const uint4*)(col + 16 * kt * D);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        acc[qt][kt] = mma_bf16(a0, qb[qt][0][ks], acc[qt][kt]);
+        acc[qt][kt] = mma_bf16(a0, qb[qt][1][ks], acc[qt][kt]);
+      }
+    }
+  }
+}
+
 // P V from a swizzled row-major V tile: V^T fragments by transposed reads; the
 // lane's probabilities (bf16, as multiplied) are added to lsum. Lane (r,
 // g) needs rows (keys) 4 q .. 4 q + 3 of column (d) 16 dt + r with q = 8 h + g (low

@@ -68,14 +68,172 @@ __global__ __launch_bounds__(256) void landmark_kernel(const T* __restrict__ K, 
   }
 }
 
+// bf16 with m > 64: 128 landmarks per workgroup, two 16-landmark column tiles per
+// wave, so every staged key fragment feeds two MFMAs per Q~ plane and every value
+// fragment two. Key/value blocks are staged by direct global-to-LDS loads into
+// tiles swizzled for the score reads and the transposed value reads, double-
+// buffered (a block's rows are requested while the previous block computes);
+// the softmax keeps a lazily raised reference. Per landmark the MFMA sequence of
+// the scores is that of landmark_kernel and of the candidate kernel, so the group
+// maxima are the bits the candidates see.
+constexpr int kLandmarkTileD = 128;
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void landmarkd_kernel(
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, const uint16_t* __restrict__ qtop,
+    float* __restrict__ S, float* __restrict__ lpart, float* __restrict__ kmax, float* __restrict__ bmax, int N, int m,
+    int lchunk, int nsplit, int gq, int nbg, int lm_tiles, int BH, float sl2e) {
+  constexpr int QT = 2;
+  using Sw = SwzTile<D>;
+  // one shared object: with separate ones the compiler's LDS scopes would make the
+  // next block's loads look like writes to the block being read
+  __shared__ __align__(16) struct {
+    uint16_t rk[2][Sw::TILE];
+    uint16_t rv[2][Sw::TILE];
+    float kred[4];
+  } sm;
+  int lt, c, z;
+  if (!chunk_item(lm_tiles, nsplit, BH, lt, c, z)) return;   // workgroup-uniform
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
+  const int k0 = c * lchunk, k1 = min(N, k0 + lchunk);
+  const uint16_t* Kz = K + (size_t)z * N * D;
+  const uint16_t* Vz = V + (size_t)z * N * D;
+  // keys of this lane's rows of the block at kb (rows past the chunk's end repeat its last key)
+  auto rows = [&](int kb, int (&id)[Sw::NI]) {
+#pragma unroll
+    for (int u = 0; u < Sw::NI; ++u) id[u] = min(kb + 16 * w + u * Sw::RPI + lane / Sw::CPR, k1 - 1);
+  };
+  {
+    int id0[Sw::NI];
+    rows(k0, id0);
+    dma_rows<D>(sm.rk[0], sm.rv[0], Kz, Vz, id0, w, lane);
+  }
+  int lmc[QT];
+  bool lm_ok[QT];
+  uint4 qb[QT][2][D / 32];
+  float mrun[QT], lrun[QT];
+  f32x4 o[QT][D / 16];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int lm = lt * kLandmarkTileD + 32 * w + 16 * qt + r;
+    lm_ok[qt] = lm < m;
+    lmc[qt] = lm_ok[qt] ? lm : m - 1;   // padding lanes compute on a real landmark, never write
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks)
+        qb[qt][p][ks] = ld16(qtop + ((size_t)(z * 2 + p) * m + lmc[qt]) * D + 32 * ks + 8 * g);
+    mrun[qt] = -INFINITY;
+    lrun[qt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float kmx = 0.f;
+  const int nblk = (k1 - k0 + kKeyBlock - 1) / kKeyBlock;
+  for (int j = 0; j < nblk; ++j) {
+    const int kb = k0 + j * kKeyBlock;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();   // block j staged; every wave done with block j - 1
+    // the next block's loads and this block's reads go through distinct __restrict__
+    // parameters, so the compiler does not wait for the loads before the reads
+    auto step = [&](uint16_t* __restrict__ nk, uint16_t* __restrict__ nv, const uint16_t* __restrict__ ck,
+                    const uint16_t* __restrict__ cv) __attribute__((always_inline)) {
+      if (j + 1 < nblk) {   // block-uniform
+        int idn[Sw::NI];
+        rows(kb + kKeyBlock, idn);
+        dma_rows<D>(nk, nv, Kz, Vz, idn, w, lane);
+      }
+      if (lt == 0) {   // squared key norms, 4 threads per row (a row's chunks in any order)
+        const int row = tid >> 2, part = tid & 3;
+        const uint16_t* kr = ck + row * D + part * (D / 4);
+        float sq = 0.f;
+#pragma unroll
+        for (int e = 0; e < D / 4; ++e) {
+          const float x = bf16_to_f32(kr[e]);
+          sq = fmaf(x, x, sq);
+        }
+        sq += __shfl_xor(sq, 1, WAVE);
+        sq += __shfl_xor(sq, 2, WAVE);
+        kmx = fmaxf(kmx, sq);
+      }
+      f32x4 acc[QT][4];
+      __builtin_amdgcn_s_setprio(1);
+      qk2_bf16_swz<D, QT>(ck, qb, acc, lane);
+      const int blk = kb / kKeyBlock;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {   // group maxima (and the scores when asked for) as the sweep writes them
+        float* Brow = bmax + ((size_t)z * m + lmc[qt]) * nbg;
+        float gk[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          gk[kt] = -INFINITY;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            gk[kt] = fmaxf(gk[kt], kb + 16 * kt + 4 * g + jj < k1 ? acc[qt][kt][jj] : -INFINITY);
+        }
+        if (gq == 4) {
+          if (lm_ok[qt]) *(float4*)(Brow + 16 * blk + 4 * g) = make_float4(gk[0], gk[1], gk[2], gk[3]);
+        } else {
+          float gm = fmaxf(fmaxf(gk[0], gk[1]), fmaxf(gk[2], gk[3]));
+          if (gq == 64) gm = quad_max(gm);
+          if (lm_ok[qt] && (gq == 16 || g == 0)) Brow[gq == 16 ? 4 * blk + g : blk] = gm;
+        }
+        if (S && lm_ok[qt]) {
+          float* Srow = S + ((size_t)z * m + lmc[qt]) * N;
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int key = kb + 16 * kt + 4 * g + jj;
+              if (key < k1) Srow[key] = acc[qt][kt][jj];
+            }
+        }
+      }
+      lazy_softmax<D, QT>(acc, min(kKeyBlock, k1 - kb), sl2e, mrun, lrun, o, lane);
+      pv_bf16_swz<D, QT>(cv, acc, o, lrun, lane);
+      __builtin_amdgcn_s_setprio(0);
+    };
+    step(sm.rk[(j + 1) & 1], sm.rv[(j + 1) & 1], sm.rk[j & 1], sm.rv[j & 1]);
+  }
+  if (lt == 0) {
+    kmx = wave_max(kmx);
+    if (lane == 0) sm.kred[w] = kmx;
+    __syncthreads();
+    if (tid == 0) {
+      const float mx = fmaxf(fmaxf(sm.kred[0], sm.kred[1]), fmaxf(sm.kred[2], sm.kred[3]));
+      kmax[(size_t)z * nsplit + c] = sqrtf(mx) * 1.0001f + 1e-30f;
+    }
+  }
+  // partial softmax of this chunk: [reference, sum, pad, pad, acc[D]] per landmark
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const float l = quad_sum(lrun[qt]);
+    if (lm_ok[qt]) {
+      float* P = lpart + (((size_t)z * m + lmc[qt]) * nsplit + c) * (D + 4);
+      if (g == 0) *(float2*)P = make_float2(mrun[qt], l);
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+        *(float4*)(P + 4 + 16 * dt + 4 * g) = make_float4(o[qt][dt][0], o[qt][dt][1], o[qt][dt][2], o[qt][dt][3]);
+    }
+  }
+}
+
 template <typename T, int D>
 static hipError_t landmark_launch(const Plan& p, const void* K, const void* V, char* ws, float* S_out,
                                   hipStream_t st) {
   const float sl2e = (float)(1.4426950408889634 / sqrt((double)D));
-  const int grid = 8 * ((p.nsplit * p.BH + 7) / 8) * p.lm_tiles;   // see chunk_item
-  hipLaunchKernelGGL((landmark_kernel<T, D>), dim3(grid), dim3(256), 0, st, (const T*)K, (const T*)V,
-                     (const void*)(ws + p.ws.qtop), S_out, (float*)(ws + p.ws.lpart), (float*)(ws + p.ws.kmax),
-                     (float*)(ws + p.ws.bmax), p.N, p.m, p.lchunk, p.nsplit, p.gq, p.nbg, p.lm_tiles, p.BH, sl2e);
+  if (sizeof(T) == 2 && p.m > kLandmarkTile) {   // bf16, several landmark tiles: the direct-load kernel
+    const int tiles = (p.m + kLandmarkTileD - 1) / kLandmarkTileD;
+    const int grid = 8 * ((p.nsplit * p.BH + 7) / 8) * tiles;   // see chunk_item
+    hipLaunchKernelGGL((landmarkd_kernel<D>), dim3(grid), dim3(256), 0, st, (const uint16_t*)K, (const uint16_t*)V,
+                       (const uint16_t*)(ws + p.ws.qtop), S_out, (float*)(ws + p.ws.lpart), (float*)(ws + p.ws.kmax),
+                       (float*)(ws + p.ws.bmax), p.N, p.m, p.lchunk, p.nsplit, p.gq, p.nbg, tiles, p.BH, sl2e);
+  } else {
+    const int grid = 8 * ((p.nsplit * p.BH + 7) / 8) * p.lm_tiles;   // see chunk_item
+    hipLaunchKernelGGL((landmark_kernel<T, D>), dim3(grid), dim3(256), 0, st, (const T*)K, (const T*)V,
+                       (const void*)(ws + p.ws.qtop), S_out, (float*)(ws + p.ws.lpart), (float*)(ws + p.ws.kmax),
+                       (float*)(ws + p.ws.bmax), p.N, p.m, p.lchunk, p.nsplit, p.gq, p.nbg, p.lm_tiles, p.BH, sl2e);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // the chunks' partial softmaxes merged into V~, and the candidate thresholds of

@@ -401,6 +401,19 @@ __device__ __forceinline__ void dma_rows(uint16_t* Kt, uint16_t* Vt, const uint1
   }
 }
 
+// The key tile of dma_rows alone (swizzled for score reads).
+template <int D>
+__device__ __forceinline__ void dma_rows_k(uint16_t* Kt, const uint16_t* Kz, const int (&ids)[SwzTile<D>::NI], int w,
+                                           int lane) {
+  using S = SwzTile<D>;
+  const int p = lane % S::CPR;
+#pragma unroll
+  for (int u = 0; u < S::NI; ++u) {
+    const int row = 16 * w + u * S::RPI + lane / S::CPR;
+    lds_dma16(Kz + (size_t)ids[u] * D + 8 * (p ^ S::swz_k(row)), Kt + (16 * w + u * S::RPI) * D);
+  }
+}
+
 // QT column tiles of scores from a swizzled K tile.
 template <int D, int QT>
 __device__ __forceinline__ void qk_bf16_swz(const uint16_t* Ks, const uint4 (&qf)[QT][D / 32], f32x4 (&acc)[QT][4],

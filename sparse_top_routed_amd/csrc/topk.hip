@@ -248,6 +248,112 @@ __global__ __launch_bounds__(256) void topk_cand_kernel(const T* __restrict__ K,
   if (lm_ok && g == 0) ccnt[row * nsplit + c] = min(base, (uint32_t)capc + 1u);
 }
 
+// bf16 with m > 64: 128 landmarks per workgroup (two column tiles per wave),
+// key blocks staged by direct loads into swizzled double-buffered tiles; the
+// scores by the shared-expert kernel's MFMA sequence (qk2_bf16_swz: k-slices in
+// order, hi then lo plane), so a score here has the bits the group maxima came
+// from. Candidates as in candidate_sweep, per column tile.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void topk_candd_kernel(
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ qtop, const uint32_t* __restrict__ thr,
+    uint2* __restrict__ cand, uint32_t* __restrict__ ccnt, uint32_t* __restrict__ glist, int N, int m, int lchunk,
+    int nsplit, int capc, int lm_tiles, int BH) {
+  constexpr int QT = 2;
+  using Sw = SwzTile<D>;
+  __shared__ __align__(16) struct {
+    uint16_t rk[2][Sw::TILE];
+  } sm;
+  if (blockIdx.x == 0 && threadIdx.x == 0) glist[0] = 0u;   // no fallback rows yet (the select kernel adds them)
+  int lt, c, z;
+  if (!chunk_item(lm_tiles, nsplit, BH, lt, c, z)) return;   // workgroup-uniform
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
+  const int k0 = c * lchunk, k1 = min(N, k0 + lchunk);
+  const uint16_t* Kz = K + (size_t)z * N * D;
+  auto rows = [&](int kb, int (&id)[Sw::NI]) {
+#pragma unroll
+    for (int u = 0; u < Sw::NI; ++u) id[u] = min(kb + 16 * w + u * Sw::RPI + lane / Sw::CPR, k1 - 1);
+  };
+  {
+    int id0[Sw::NI];
+    rows(k0, id0);
+    dma_rows_k<D>(sm.rk[0], Kz, id0, w, lane);
+  }
+  bool lm_ok[QT];
+  size_t rowi[QT];
+  float tf[QT];
+  uint32_t base[QT];
+  uint4 qb[QT][2][D / 32];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int lm = lt * 128 + 32 * w + 16 * qt + r;
+    lm_ok[qt] = lm < m;
+    const int lmc = lm_ok[qt] ? lm : m - 1;
+    rowi[qt] = (size_t)z * m + lmc;
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks)
+        qb[qt][p][ks] = ld16(qtop + ((size_t)(z * 2 + p) * m + lmc) * D + 32 * ks + 8 * g);
+    const uint32_t tk = thr[rowi[qt]];
+    tf[qt] = tk ? key_f32(tk) : -INFINITY;   // compare the scores themselves (same order)
+    base[qt] = 0;
+  }
+  const int nblk = (k1 - k0 + kKeyBlock - 1) / kKeyBlock;
+  for (int j = 0; j < nblk; ++j) {
+    const int kb = k0 + j * kKeyBlock;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();   // block j staged; every wave done with block j - 1
+    auto step = [&](uint16_t* __restrict__ nk, const uint16_t* __restrict__ ck) __attribute__((always_inline)) {
+      if (j + 1 < nblk) {   // block-uniform
+        int idn[Sw::NI];
+        rows(kb + kKeyBlock, idn);
+        dma_rows_k<D>(nk, Kz, idn, w, lane);
+      }
+      f32x4 acc[QT][4];
+      qk2_bf16_swz<D, QT>(ck, qb, acc, lane);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        // per kt: this lane's candidate count in a byte of one word
+        uint32_t flags = 0, packed = 0;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const bool pr = (kb + 16 * kt + 4 * g + jj < k1) & (acc[qt][kt][jj] >= tf[qt]);
+            flags |= pr ? 1u << (4 * kt + jj) : 0u;
+            packed += pr ? 1u << (8 * kt) : 0u;
+          }
+        const uint32_t p0 = __shfl(packed, r, WAVE), p1 = __shfl(packed, r + 16, WAVE);
+        const uint32_t p2 = __shfl(packed, r + 32, WAVE), p3 = __shfl(packed, r + 48, WAVE);
+        const uint32_t tot = p0 + p1 + p2 + p3;   // no byte exceeds 16: no carries
+        const uint32_t ex = (g > 0 ? p0 : 0u) + (g > 1 ? p1 : 0u) + (g > 2 ? p2 : 0u);
+        // slot of the lane's first candidate of each kt: the landmark's candidates
+        // of earlier kt, then those of lanes with smaller g
+        const uint32_t first = ex + (tot << 8) + (tot << 16) + (tot << 24);
+        uint2* seg = cand + (rowi[qt] * nsplit + c) * (size_t)capc;
+        uint32_t fl = lm_ok[qt] ? flags : 0u;
+        while (fl) {   // one pass per candidate of the lane, in key order
+          const int bit = __builtin_ctz(fl);
+          fl &= fl - 1u;
+          const int kt = bit >> 2;
+          const uint32_t pos = base[qt] + ((first >> (8 * kt)) & 255u) +
+                               (uint32_t)__builtin_popcount(flags & ((1u << bit) - 1u) & (0xFu << (4 * kt)));
+          float x = acc[qt][0][0];
+#pragma unroll
+          for (int b = 1; b < 16; ++b) x = bit == b ? acc[qt][b >> 2][b & 3] : x;
+          if (pos < (uint32_t)capc) seg[pos] = make_uint2(f32_key(x), (uint32_t)(kb + 16 * kt + 4 * g + (bit & 3)));
+        }
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) base[qt] += (tot >> (8 * kt)) & 255u;
+      }
+    };
+    step(sm.rk[(j + 1) & 1], sm.rk[j & 1]);
+  }
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+    if (lm_ok[qt] && g == 0) ccnt[rowi[qt] * nsplit + c] = min(base[qt], (uint32_t)capc + 1u);
+}
+
 // ---------------------------------------------------------------- 3. select
 // One wave per row (WPB rows per workgroup). The row's candidate lists (index
 // order, chunk after chunk) go to LDS; candidate j is slot j / 64 of lane j % 64
@@ -510,10 +616,18 @@ static hipError_t topk_launch(const Plan& p, const void* K, char* ws, hipStream_
   hipError_t e = hipSuccess;
   if (p.cap > 0) {
     // candidates against the thresholds the landmark step set (merge_thresh_kernel)
-    const int cgrid = 8 * ((p.nsplit * p.BH + 7) / 8) * p.lm_tiles;   // see chunk_item
-    hipLaunchKernelGGL((topk_cand_kernel<T, D>), dim3(cgrid), dim3(256), 0, st, (const T*)K,
-                       (const void*)(ws + p.ws.qtop), (const uint32_t*)(ws + p.ws.thr), (uint2*)(ws + p.ws.cand),
-                       (uint32_t*)(ws + p.ws.ccnt), glist, p.N, p.m, p.lchunk, p.nsplit, p.capc, p.lm_tiles, p.BH);
+    if (sizeof(T) == 2 && p.m > kLandmarkTile) {   // bf16, several landmark tiles: the direct-load kernel
+      const int tiles = (p.m + 127) / 128;
+      const int cgrid = 8 * ((p.nsplit * p.BH + 7) / 8) * tiles;   // see chunk_item
+      hipLaunchKernelGGL((topk_candd_kernel<D>), dim3(cgrid), dim3(256), 0, st, (const uint16_t*)K,
+                         (const uint16_t*)(ws + p.ws.qtop), (const uint32_t*)(ws + p.ws.thr), (uint2*)(ws + p.ws.cand),
+                         (uint32_t*)(ws + p.ws.ccnt), glist, p.N, p.m, p.lchunk, p.nsplit, p.capc, tiles, p.BH);
+    } else {
+      const int cgrid = 8 * ((p.nsplit * p.BH + 7) / 8) * p.lm_tiles;   // see chunk_item
+      hipLaunchKernelGGL((topk_cand_kernel<T, D>), dim3(cgrid), dim3(256), 0, st, (const T*)K,
+                         (const void*)(ws + p.ws.qtop), (const uint32_t*)(ws + p.ws.thr), (uint2*)(ws + p.ws.cand),
+                         (uint32_t*)(ws + p.ws.ccnt), glist, p.N, p.m, p.lchunk, p.nsplit, p.capc, p.lm_tiles, p.BH);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     auto sel = [&](auto kern, int wpb) {
       hipLaunchKernelGGL(kern, dim3((rows + wpb - 1) / wpb), dim3(64 * wpb), 0, st, (const uint2*)(ws + p.ws.cand),

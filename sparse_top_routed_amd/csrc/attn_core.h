@@ -401,6 +401,31 @@ __device__ __forceinline__ void dma_rows(uint16_t* Kt, uint16_t* Vt, const uint1
   }
 }
 
+// dma_rows through raw buffer resources (base of the slice's K or V, records =
+// its byte size; dword 3 = 0x00020000 for gfx9 raw buffers): the row offsets are
+// 32-bit (ids < N, N d 2 < 2^31 bytes), so each load costs one address add.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t rs, uint32_t off, void* l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)l, 16, off, 0, 0, 0);
+}
+template <int D>
+__device__ __forceinline__ void dma_rows_buf(uint16_t* Kt, uint16_t* Vt, __amdgpu_buffer_rsrc_t rsK,
+                                             __amdgpu_buffer_rsrc_t rsV, const int (&ids)[SwzTile<D>::NI], int w,
+                                             int lane) {
+  using S = SwzTile<D>;
+  const int p = lane % S::CPR;
+#pragma unroll
+  for (int u = 0; u < S::NI; ++u) {
+    const int row = 16 * w + u * S::RPI + lane / S::CPR;
+    const uint32_t src = (uint32_t)ids[u] * (D * 2);
+    const int lds_row0 = 16 * w + u * S::RPI;
+    lds_dma16_buf(rsK, src + 16 * (p ^ S::swz_k(row)), Kt + lds_row0 * D);
+    lds_dma16_buf(rsV, src + 16 * (p ^ S::swz_v(row)), Vt + lds_row0 * D);
+  }
+}
+
 // The key tile of dma_rows alone (swizzled for score reads).
 template <int D>
 __device__ __forceinline__ void dma_rows_k(uint16_t* Kt, const uint16_t* Kz, const int (&ids)[SwzTile<D>::NI], int w,

@@ -504,7 +504,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   using T = uint16_t;
   using S = SwzTile<D>;
   __shared__ GatherDLds<D> sm;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4;
+  // Two column tiles per wave: wave-uniform values in scalar registers (scalar
+  // row offsets and LDS targets, a scalar branch for idle waves) and buffer
+  // loads for the staged rows cut a fifth of the vector instructions per block
+  // and measured faster; with one column tile (64-row tiles, more idle waves)
+  // the same changes measured slower, so that form keeps vector values.
+  constexpr bool kScalar = QT == 2;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4;
+  const int w = kScalar ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int row0 = QT * 16 * w + (lane & 15);   // row of the wave's column tile qt: row0 + 16 qt
   const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3, gpx = (int)(gridDim.x >> 3) / gs;
   if (jx >= gpx * gs) return;   // workgroup-uniform
@@ -529,10 +536,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     auto blk = [&](int j, int& zb, const int32_t*& Ieb, int& kbb) {
       j = min(j, nblk - 1);
       const int ti = j / B;
-      zb = sm.tz[ti];
-      Ieb = I + ((size_t)zb * m + sm.tile[ti].x) * k;
+      zb = kScalar ? __builtin_amdgcn_readfirstlane(sm.tz[ti]) : sm.tz[ti];
+      const int ex = kScalar ? __builtin_amdgcn_readfirstlane(sm.tile[ti].x) : sm.tile[ti].x;
+      Ieb = I + ((size_t)zb * m + ex) * k;
       kbb = (j % B) * kKeyBlock;
     };
+    // the slice's K and V as raw buffers: each staged row is a 32-bit offset
+    auto rsK = [&](int zb) { return raw_rsrc(K + (size_t)zb * N * D, (uint32_t)N * D * 2); };
+    auto rsV = [&](int zb) { return raw_rsrc(V + (size_t)zb * N * D, (uint32_t)N * D * 2); };
     // token ids of this lane's rows of block j (rows past the expert's end repeat its last token)
     auto ids = [&](int j, int (&id)[S::NI], int& zb) {
       const int32_t* Ieb;
@@ -563,7 +574,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     {
       int id0[S::NI], z0;
       ids(0, id0, z0);
-      dma_rows<D>(sm.rk[0], sm.rv[0], K + (size_t)z0 * N * D, V + (size_t)z0 * N * D, id0, w, lane);
+      if constexpr (kScalar)
+        dma_rows_buf<D>(sm.rk[0], sm.rv[0], rsK(z0), rsV(z0), id0, w, lane);
+      else
+        dma_rows<D>(sm.rk[0], sm.rv[0], K + (size_t)z0 * N * D, V + (size_t)z0 * N * D, id0, w, lane);
       ids(1, id_n, z_n);
     }
     int qe[QT], qe_n[QT], qe_nn[QT];
@@ -608,13 +622,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
       // they cannot overlap and does not wait for the loads before the reads.
       auto step = [&](uint16_t* __restrict__ nk, uint16_t* __restrict__ nv, const uint16_t* __restrict__ ck,
                       const uint16_t* __restrict__ cv) __attribute__((always_inline)) {
-        if (j + 1 < nblk)   // block-uniform
-          dma_rows<D>(nk, nv, K + (size_t)z_n * N * D, V + (size_t)z_n * N * D, id_n, w, lane);
+        if (j + 1 < nblk) {   // block-uniform
+          if constexpr (kScalar)
+            dma_rows_buf<D>(nk, nv, rsK(z_n), rsV(z_n), id_n, w, lane);
+          else
+            dma_rows<D>(nk, nv, K + (size_t)z_n * N * D, V + (size_t)z_n * N * D, id_n, w, lane);
+        }
         ids(j + 2, id_n, z_n);
-        const bool live = QT * 16 * w < cur.z;   // the wave has live rows (wave-uniform)
-        // the scores live inside one branch (merging them with an idle path would
-        // cost a register fill per block); the next tile's query rows (block-
-        // uniform) are loaded once the scores no longer need qf
+        // The wave has live rows (with kScalar a scalar condition, so the two paths
+        // stay apart). The scores live inside the busy path (merging them with the
+        // idle path would cost a register fill per block); the next tile's query
+        // rows (block-uniform) load once the scores no longer need qf.
+        const bool live = QT * 16 * w < (kScalar ? __builtin_amdgcn_readfirstlane(cur.z) : cur.z);
         if (live) {
           f32x4 acc[QT][4];
           __builtin_amdgcn_s_setprio(kGatherPrio);
@@ -624,7 +643,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
           pv_bf16_swz<D, QT>(cv, acc, o, lrun, lane);
           __builtin_amdgcn_s_setprio(0);
         } else if (lastblk) {
+          // an idle wave waits for its loads here: the compiler may lay this path
+          // out ahead of the busy one, and loads left in flight would then make the
+          // busy path's key reads wait for them
           qload(ti + 1, qe_n, qf);
+          if constexpr (kScalar) __builtin_amdgcn_s_waitcnt(0);
         }
       };
       step(sm.rk[(j + 1) & 1], sm.rv[(j + 1) & 1], sm.rk[j & 1], sm.rv[j & 1]);
@@ -1097,7 +1120,9 @@ static hipError_t gather_launch(const Plan& p, const void* Q, const void* K, con
                        p.s, p.max_tiles, total, gchunk, gsz, sl2e, (float*)(ws + p.ws.lse));
     return hipGetLastError();
   }
-  if constexpr (sizeof(T) == 2) {   // bf16 partials: the direct-load kernel, 1 or 2 column tiles per wave
+  // bf16 partials: the direct-load kernel, 1 or 2 column tiles per wave (its buffer
+  // offsets within a slice's K / V are 32-bit)
+  if (sizeof(T) == 2 && (int64_t)p.N * D * 2 < ((int64_t)1 << 31)) {
     static PerDevice c_q1, c_q2, c_q1f, c_q2f;
     auto go = [&](auto kern, PerDevice& cache) {
       const int sl = n_cu * resident_per_cu(cache, kern, 256);

@@ -484,6 +484,13 @@ void gather_kernel(const T* __restrict__ Q, const T* __restrict__ K,
 // does its softmax meanwhile. Held to two waves per SIMD. The softmax keeps a
 // lazily raised reference and sums the probabilities as rounded for P V
 // (lazy_softmax).
+// Landmark merge (bf16): waves per workgroup and landmark buffers. Four waves on one
+// buffer (48 KB of LDS for d = 128) let two workgroups share a CU, so while one
+// waits for its next block or its partials the other computes: faster than eight
+// waves on two buffers (one workgroup per CU, its waves in lockstep): very long
+// merge 1.41 -> 1.24 ms, long 0.82 -> 0.69 ms.
+constexpr int kCombineWaves = 4, kCombineBuffers = 1;
+
 template <int D>
 struct GatherDLds {
   __align__(16) uint16_t rk[2][SwzTile<D>::TILE];
@@ -931,15 +938,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Q, c
     store4<T>(orow + 16 * dt + 4 * g, o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
 }
 
-// The same for bf16 inputs with 8 waves of QT column tiles (16 QT NW consecutive
+// The same for bf16 inputs with NW waves of QT column tiles (16 QT NW consecutive
 // queries per workgroup): the landmark blocks (Q~ hi and lo planes,
-// V~) are staged by direct loads into double-buffered tiles that every wave
+// V~) are staged by direct loads into tiles that every wave
 // reads (V~ transposed), so each block is fetched once per 16 QT NW queries and
 // each fragment read feeds QT MFMAs. The softmax keeps a lazily raised reference
 // and sums the probabilities as rounded for the product (see lazy_softmax).
 // MFULL: m is a multiple of the key block (no masking code). SU: partial slots
-// loaded together in the seed (1, 2 or 4).
-template <int D, int QT, int NW, bool MFULL, int SU>
+// loaded together in the seed (1, 2 or 4). NB: landmark buffers (2: the next
+// block loads while one computes; 1: less LDS, so more workgroups per CU).
+template <int D, int QT, int NW, bool MFULL, int SU, int NB>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void combined_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ qtop, const uint16_t* __restrict__ vt16,
     const uint16_t* __restrict__ pacc, const float* __restrict__ pml, uint16_t* __restrict__ out, int N, int m, int s,
@@ -948,8 +956,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // one shared object: with separate ones the compiler's LDS scopes would make the
   // next block's loads look like writes to the block being read
   __shared__ __align__(16) struct {
-    uint16_t kk[2][2 * U::TILE];   // per buffer: Q~ hi tile, then lo tile
-    uint16_t vv[2][U::TILE];
+    uint16_t kk[NB][2 * U::TILE];   // per buffer: Q~ hi tile, then lo tile
+    uint16_t vv[NB][U::TILE];
   } sm;
   const int z = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
   const int qw = blockIdx.x * (16 * QT * NW) + QT * 16 * w + r;   // query of column tile qt: qw + 16 qt
@@ -1022,25 +1030,38 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     lrun[qt] = g != 0 ? 0.f : l;
   }
   const int nb = (m + kKeyBlock - 1) / kKeyBlock;
+  auto attend = [&](int j, const uint16_t* ck, const uint16_t* cv) __attribute__((always_inline)) {
+    f32x4 acc[QT][4];
+    __builtin_amdgcn_s_setprio(1);
+    uqk<D, QT, 2>(ck, ck + U::TILE, qf, acc, lane);
+    lazy_softmax<D, QT>(acc, MFULL ? kKeyBlock : min(kKeyBlock, m - j * kKeyBlock), sl2e, mrun, lrun, o, lane);
+    upv<D, QT>(cv, acc, o, lrun, lane);
+    __builtin_amdgcn_s_setprio(0);
+  };
   for (int j = 0; j < nb; ++j) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();   // block j staged; every wave done with block j - 1
-    // the next block's loads and this block's reads go through distinct __restrict__
-    // parameters, so the compiler does not wait for the loads before the reads
-    auto step = [&](uint16_t* __restrict__ nk, uint16_t* __restrict__ nv, const uint16_t* __restrict__ ck,
-                    const uint16_t* __restrict__ cv) __attribute__((always_inline)) {
-      // unconditional (rows clamp to the last landmark): a branch around the loads
-      // would merge two states here and the compiler would then wait for them
-      stage((j + 1) * kKeyBlock, nk, nv);
-      f32x4 acc[QT][4];
-      __builtin_amdgcn_s_setprio(1);
-      uqk<D, QT, 2>(ck, ck + U::TILE, qf, acc, lane);
-      lazy_softmax<D, QT>(acc, MFULL ? kKeyBlock : min(kKeyBlock, m - j * kKeyBlock), sl2e, mrun, lrun, o, lane);
-      upv<D, QT>(cv, acc, o, lrun, lane);
-      __builtin_amdgcn_s_setprio(0);
-    };
-    const int b = j & 1, nbuf = (j + 1) & 1;
-    step(sm.kk[nbuf], sm.vv[nbuf], sm.kk[b], sm.vv[b]);
+    if constexpr (NB == 1) {
+      if (j > 0) {
+        __syncthreads();   // every wave done with block j - 1
+        stage(j * kKeyBlock, sm.kk[0], sm.vv[0]);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();   // block j staged
+      attend(j, sm.kk[0], sm.vv[0]);
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();   // block j staged; every wave done with block j - 1
+      // the next block's loads and this block's reads go through distinct __restrict__
+      // parameters, so the compiler does not wait for the loads before the reads
+      auto step = [&](uint16_t* __restrict__ nk, uint16_t* __restrict__ nv, const uint16_t* __restrict__ ck,
+                      const uint16_t* __restrict__ cv) __attribute__((always_inline)) {
+        // unconditional (rows clamp to the last landmark): a branch around the loads
+        // would merge two states here and the compiler would then wait for them
+        stage((j + 1) * kKeyBlock, nk, nv);
+        attend(j, ck, cv);
+      };
+      const int b = j & 1, nbuf = (j + 1) & 1;
+      step(sm.kk[nbuf], sm.vv[nbuf], sm.kk[b], sm.vv[b]);
+    }
   }
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
@@ -1153,12 +1174,12 @@ template <typename T, int D>
 static hipError_t combine_launch(const Plan& p, const void* Q, void* out, char* ws, hipStream_t st) {
   const float sl2e = (float)(1.4426950408889634 / sqrt((double)D));
   const void* vtop = p.dtype == MITA_BF16 ? (const void*)(ws + p.ws.vt16) : (const void*)(ws + p.ws.vt32);
-  if constexpr (sizeof(T) == 2) {   // bf16: waves of 2 column tiles; 8 waves for d = 128 (96 KB of LDS), 4 for 64
-    constexpr int QT = 2, NW = D == 128 ? 8 : 4, QPW = 16 * QT * NW;
+  if constexpr (sizeof(T) == 2) {   // bf16: waves of 2 column tiles
+    constexpr int QT = 2, NW = kCombineWaves, NB = kCombineBuffers, QPW = 16 * QT * NW;
     const bool mfull = p.m % kKeyBlock == 0;
     auto pick = [&](auto su) {
       constexpr int SU = decltype(su)::value;
-      return mfull ? combined_kernel<D, QT, NW, true, SU> : combined_kernel<D, QT, NW, false, SU>;
+      return mfull ? combined_kernel<D, QT, NW, true, SU, NB> : combined_kernel<D, QT, NW, false, SU, NB>;
     };
     auto kern = p.s == 1 ? pick(std::integral_constant<int, 1>{})
               : p.s == 2 ? pick(std::integral_constant<int, 2>{}) : pick(std::integral_constant<int, 4>{});

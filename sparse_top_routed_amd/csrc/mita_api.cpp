@@ -375,6 +375,10 @@ mita_status mita_forward(const void* Q, const void* K, const void* V, int m, int
   std::lock_guard<std::mutex> lk(sd->mu);
   hipStream_t rs = sd->stream;
   if ((st = hip_status(launch_pool(P, Q, ws, hs), "pool")) != MITA_OK) return st;
+  // the router's queue counters are cleared before the fork: a one-workgroup kernel
+  // at the head of the side stream would wait for a CU slot behind the shared-
+  // expert kernel's workgroups, and the routing with it
+  if ((st = hip_status(launch_clear(P, ws, hs), "clear")) != MITA_OK) return st;
   // fork: routing (+ bucketing) on the side stream, steps 2-3 on the caller's
   if ((st = hip_status(hipEventRecord(sd->fork, hs), "fork")) != MITA_OK) return st;
   if ((st = hip_status(hipStreamWaitEvent(rs, sd->fork, 0), "fork wait")) != MITA_OK) return st;
@@ -382,8 +386,7 @@ mita_status mita_forward(const void* Q, const void* K, const void* V, int m, int
   // (also after a failed launch, so a graph being captured is never left forked).
   // The first failure is the one reported.
   FirstError fe;
-  fe.add(launch_clear(P, ws, rs), "clear");
-  if (fe.ok()) fe.add(launch_route(P, Q, ws, rs), "route");
+  fe.add(launch_route(P, Q, ws, rs), "route");
   if (fe.ok()) fe.add(launch_bucket(P, ws, rs), "bucket");
   const bool joined = fe.add(hipEventRecord(sd->join, rs), "join");
   if (fe.ok()) fe.add(launch_landmark(P, K, V, ws, nullptr, hs), "landmark");

@@ -20,8 +20,10 @@
 // all their keys: dQ). Then Q~ passes its gradient back through the pooling.
 //
 // Determinism: no float atomics. Partial sums go to per-part buffers reduced in
-// a fixed order; a token's routed dK/dV rows are summed over the experts that hold
-// it in expert order (an inverse list built one expert at a time).
+// a fixed order; each expert's queries are taken in ascending (query, slot) order
+// (a stable re-sort of the routing); a token's routed dK/dV rows are summed over
+// the experts that hold it in expert order (an inverse list built one expert at a
+// time).
 //
 // Tiles (64 rows of D bf16) are read two ways: as QK operands (16 consecutive
 // rows at one 16-byte chunk) and transposed (8 consecutive rows x 2 neighbouring
@@ -131,13 +133,30 @@ __device__ __forceinline__ int part_lo(int n, int parts, int i) { return (int)((
 // ---------------------------------------------------------------- key-outer
 // Workgroup = 64 keys (16 per wave, held as B fragments) of one (slice, key
 // set); it walks the key set's queries 64 at a time, staged in LDS (rows of Q
-// and dO by direct loads, lse and D beside them; double-buffered), and
-// accumulates dK^T += Q^T dS, dV^T += dO^T P for its keys.
+// and dO, and their lse and D, all by direct loads; double-buffered), and
+// accumulates dK^T += Q^T dS, dV^T += dO^T P for its keys. The source rows of a
+// chunk (through the bucket permutation for the routed part) are read one chunk
+// ahead, so no load waits inside a chunk; rows past the set's end repeat its last
+// query and are masked out of P.
+template <int D>
+struct KvLds {
+  uint16_t qs[2][BT<D>::TILE];
+  uint16_t os[2][BT<D>::TILE];
+  float ls[2][kKeyBlock], ds[2][kKeyBlock];
+};
+
+__device__ __forceinline__ void lds_dma4(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)l, 4, 0, 0);
+}
+
 template <int D, int PART>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_kv_kernel(BwdArgs a) {
-  __shared__ __align__(16) uint16_t qs[2][BT<D>::TILE];
-  __shared__ __align__(16) uint16_t os[2][BT<D>::TILE];
-  __shared__ __align__(16) float ls[2][kKeyBlock], ds[2][kKeyBlock];
+  using B = BT<D>;
+  constexpr int NI = (kKeyBlock / 4) / B::RPI;   // rows a lane stages per tile
+  // one shared object: with separate ones the compiler's LDS scopes would make the
+  // next chunk's loads look like writes to the chunk being read
+  __shared__ __align__(16) KvLds<D> sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
   const int N = a.N, m = a.m, k = a.k, s = a.s;
   int z, e = 0, kb, nkeys, q0 = 0, nq;
@@ -187,64 +206,91 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) dk[dt] = dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // query t of the set: its Q and dO rows, lse and D
-  auto qrow = [&](int t, const uint16_t*& qp, const uint16_t*& op, float& l, float& dd) {
-    const bool ok = t < nq;
-    const int tc = ok ? t : max(nq - 1, 0);
-    if constexpr (PART == kShared) {
-      qp = a.qt16 + ((size_t)z * 2 * m + tc) * D;
-      op = a.dvt16 + ((size_t)z * m + tc) * D;
-      l = a.lse_se[(size_t)z * m + tc];
-      dd = a.Di[(size_t)z * m + tc];
-    } else {
-      int q = q0 + tc;
-      if constexpr (PART == kRouted) q = a.perm[(size_t)z * N * s + q] / s;
-      qp = a.Q + ((size_t)z * N + q) * D;
-      op = a.dO + ((size_t)z * N + q) * D;
-      l = a.lse[(size_t)z * N + q];
-      dd = a.Dq[(size_t)z * N + q];
-    }
-    if (!ok) { l = INFINITY; dd = 0.f; }   // weight 2^(x - inf) = 0: the row adds nothing
+  // row of query t of the set, as read ahead (the bucket entry for the routed
+  // part: the division waits for the load, so it is left to the use), and as used
+  auto qsrc = [&](int t) {
+    const int tc = min(t, max(nq - 1, 0));
+    if constexpr (PART == kShared) return tc;
+    if constexpr (PART == kRouted) return a.perm[(size_t)z * N * s + q0 + tc];
+    return q0 + tc;
   };
-  auto stage = [&](int c, uint16_t* __restrict__ qt, uint16_t* __restrict__ ot, float* lsb, float* dsb) {
-    bdma<D, 4>(qt, [&](int row) { const uint16_t *qp, *op; float l, dd; qrow(c + row, qp, op, l, dd); return qp; }, w, lane);
-    bdma<D, 4>(ot, [&](int row) { const uint16_t *qp, *op; float l, dd; qrow(c + row, qp, op, l, dd); return op; }, w, lane);
-    if (tid < kKeyBlock) {
-      const uint16_t *qp, *op;
-      float l, dd;
-      qrow(c + tid, qp, op, l, dd);
-      lsb[tid] = l;
-      dsb[tid] = dd;
+  auto qfin = [&](int x) {
+    if constexpr (PART == kRouted) return x / s;
+    return x;
+  };
+  // the rows this lane stages of the chunk at c (NI of a tile), and the row whose
+  // lse and D it loads (wave 0)
+  auto chunk_rows = [&](int c, int (&qi)[NI], int& ql) {
+#pragma unroll
+    for (int u = 0; u < NI; ++u) qi[u] = qsrc(c + 16 * w + u * B::RPI + lane / B::CPR);
+    ql = qsrc(c + lane);
+  };
+  auto qsrc_row = [&](int x, bool grad) {
+    const int q = qfin(x);
+    if constexpr (PART == kShared)
+      return grad ? a.dvt16 + ((size_t)z * m + q) * D : a.qt16 + ((size_t)z * 2 * m + q) * D;
+    else
+      return (grad ? a.dO : a.Q) + ((size_t)z * N + q) * D;
+  };
+  auto stage = [&](const int (&qi)[NI], int ql, uint16_t* qt, uint16_t* ot, float* lsb, float* dsb) {
+    const int p = lane % B::CPR;
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      const int r0 = 16 * w + u * B::RPI, row = r0 + lane / B::CPR;
+      lds_dma16(qsrc_row(qi[u], false) + 8 * (p ^ B::swz(row)), qt + r0 * D);
+      lds_dma16(qsrc_row(qi[u], true) + 8 * (p ^ B::swz(row)), ot + r0 * D);
+    }
+    if (w == 0) {
+      const int q = qfin(ql);
+      if constexpr (PART == kShared) {
+        lds_dma4(a.lse_se + (size_t)z * m + q, lsb);
+        lds_dma4(a.Di + (size_t)z * m + q, dsb);
+      } else {
+        lds_dma4(a.lse + (size_t)z * N + q, lsb);
+        lds_dma4(a.Dq + (size_t)z * N + q, dsb);
+      }
     }
   };
   const int nch = (nq + kKeyBlock - 1) / kKeyBlock;
-  if (nch > 0) stage(0, qs[0], os[0], ls[0], ds[0]);
+  int qi_n[NI], ql_n;
+  if (nch > 0) {
+    int qi0[NI], ql0;
+    chunk_rows(0, qi0, ql0);
+    stage(qi0, ql0, sm.qs[0], sm.os[0], sm.ls[0], sm.ds[0]);
+    chunk_rows(kKeyBlock, qi_n, ql_n);
+  }
   for (int ci = 0; ci < nch; ++ci) {
+    const int c = ci * kKeyBlock;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();   // chunk ci staged; every wave done with chunk ci - 1
-    auto step = [&](uint16_t* __restrict__ nq_t, uint16_t* __restrict__ no_t, const uint16_t* __restrict__ cq,
-                    const uint16_t* __restrict__ co) __attribute__((always_inline)) {
-      if (ci + 1 < nch) stage((ci + 1) * kKeyBlock, nq_t, no_t, ls[(ci + 1) & 1], ds[(ci + 1) & 1]);
+    auto step = [&](uint16_t* __restrict__ nq_t, uint16_t* __restrict__ no_t, float* __restrict__ nls,
+                    float* __restrict__ nds, const uint16_t* __restrict__ cq, const uint16_t* __restrict__ co,
+                    const float* __restrict__ cls, const float* __restrict__ cds) __attribute__((always_inline)) {
+      if (ci + 1 < nch) {   // block-uniform
+        stage(qi_n, ql_n, nq_t, no_t, nls, nds);
+        chunk_rows(c + 2 * kKeyBlock, qi_n, ql_n);
+      }
       f32x4 sc[4], dp[4];
       bqk<D>(cq, kf, sc, lane);   // S[query 16 kt + 4 g + j][key r]
       bqk<D>(co, vf, dp, lane);   // dP[query][key]
-      const float* lb = ls[ci & 1];
-      const float* db = ds[ci & 1];
+      const int lim = nq - c - 4 * g;   // query 16 kt + 4 g + j of the chunk is past the set when 16 kt + j >= lim
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        const float4 l4 = *(const float4*)(lb + 16 * kt + 4 * g), d4 = *(const float4*)(db + 16 * kt + 4 * g);
+        const float4 l4 = *(const float4*)(cls + 16 * kt + 4 * g), d4 = *(const float4*)(cds + 16 * kt + 4 * g);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sc[kt][j], a.c, -lv[j]));
-          sc[kt][j] = p;
-          dp[kt][j] = p * (dp[kt][j] - dvv[j]);
+          float pv = __builtin_amdgcn_exp2f(fmaf(sc[kt][j], a.c, -lv[j]));
+          pv = 16 * kt + j < lim ? pv : 0.f;
+          sc[kt][j] = pv;
+          dp[kt][j] = pv * (dp[kt][j] - dvv[j]);
         }
       }
       bpt<D>(co, sc, dv, lane);   // dV^T += dO^T P
       bpt<D>(cq, dp, dk, lane);   // dK^T += Q^T dS
     };
-    step(qs[(ci + 1) & 1], os[(ci + 1) & 1], qs[ci & 1], os[ci & 1]);
+    const int b = ci & 1, nb = (ci + 1) & 1;
+    step(sm.qs[nb], sm.os[nb], sm.ls[nb], sm.ds[nb], sm.qs[b], sm.os[b], sm.ls[b], sm.ds[b]);
   }
   if (key >= nkeys) return;
   float *kd, *vd;
@@ -272,11 +318,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 // ---------------------------------------------------------------- query-outer
 // Workgroup = NW waves of 16 queries (Q and dO rows as B fragments, lse and D per
 // lane); it walks the queries' keys 64 at a time (K and V rows staged by direct
-// loads, double-buffered) and accumulates dQ^T += K^T dS^T.
+// loads, double-buffered; the routed part's token ids read a block ahead) and
+// accumulates dQ^T += K^T dS^T.
+template <int D>
+struct QLds {
+  uint16_t kst[2][BT<D>::TILE];
+  uint16_t vst[2][BT<D>::TILE];
+};
+
 template <int D, int PART, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void bwd_q_kernel(BwdArgs a) {
-  __shared__ __align__(16) uint16_t kst[2][BT<D>::TILE];
-  __shared__ __align__(16) uint16_t vst[2][BT<D>::TILE];
+  // one shared object (see bwd_kv_kernel)
+  __shared__ __align__(16) QLds<D> sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
   const int N = a.N, m = a.m, k = a.k, s = a.s;
   int z, e = 0, nrows, k0 = 0, nkeys, row0 = 0;
@@ -334,31 +387,53 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // key t of the set (clamped to the last): its K and V rows
-  auto krow = [&](int t, bool val) {
+  // key t of the set (clamped to the last), as read ahead (a token id for the
+  // routed part), and the K or V row it names
+  using B = BT<D>;
+  constexpr int RPW = kKeyBlock / NW, NI = RPW / B::RPI;   // rows a wave, and a lane, stage per tile
+  auto ksrc = [&](int t) {
     const int tc = min(t, nkeys - 1);
-    if constexpr (PART == kRouted) {
-      const int tok = a.I[((size_t)z * m + e) * k + tc];
-      return (val ? a.V : a.K) + ((size_t)z * N + tok) * D;
-    } else if constexpr (PART == kLandmark) {
-      return val ? a.vt16 + ((size_t)z * m + tc) * D : a.qt16 + ((size_t)z * 2 * m + tc) * D;
-    } else {
-      return (val ? a.V : a.K) + ((size_t)z * N + k0 + tc) * D;
-    }
+    if constexpr (PART == kRouted) return (int)a.I[((size_t)z * m + e) * k + tc];
+    else if constexpr (PART == kLandmark) return tc;
+    else return k0 + tc;
   };
-  auto stage = [&](int kb, uint16_t* __restrict__ kt_, uint16_t* __restrict__ vt_) {
-    bdma<D, NW>(kt_, [&](int row) { return krow(kb + row, false); }, w, lane);
-    bdma<D, NW>(vt_, [&](int row) { return krow(kb + row, true); }, w, lane);
+  auto krow = [&](int x, bool val) {
+    if constexpr (PART == kLandmark)
+      return val ? a.vt16 + ((size_t)z * m + x) * D : a.qt16 + ((size_t)z * 2 * m + x) * D;
+    else
+      return (val ? a.V : a.K) + ((size_t)z * N + x) * D;
+  };
+  auto block_rows = [&](int kb, int (&ti)[NI]) {
+#pragma unroll
+    for (int u = 0; u < NI; ++u) ti[u] = ksrc(kb + w * RPW + u * B::RPI + lane / B::CPR);
+  };
+  auto stage = [&](const int (&ti)[NI], uint16_t* kt_, uint16_t* vt_) {
+    const int p = lane % B::CPR;
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      const int r0 = w * RPW + u * B::RPI, row = r0 + lane / B::CPR;
+      lds_dma16(krow(ti[u], false) + 8 * (p ^ B::swz(row)), kt_ + r0 * D);
+      lds_dma16(krow(ti[u], true) + 8 * (p ^ B::swz(row)), vt_ + r0 * D);
+    }
   };
   const int nb = (nkeys + kKeyBlock - 1) / kKeyBlock;
   const bool live = 16 * w < nrows;   // wave-uniform
-  stage(0, kst[0], vst[0]);
+  int ti_n[NI];
+  {
+    int ti0[NI];
+    block_rows(0, ti0);
+    stage(ti0, sm.kst[0], sm.vst[0]);
+    block_rows(kKeyBlock, ti_n);
+  }
   for (int bi = 0; bi < nb; ++bi) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     auto step = [&](uint16_t* __restrict__ nk, uint16_t* __restrict__ nv, const uint16_t* __restrict__ ck,
                     const uint16_t* __restrict__ cv) __attribute__((always_inline)) {
-      if (bi + 1 < nb) stage((bi + 1) * kKeyBlock, nk, nv);
+      if (bi + 1 < nb) {   // block-uniform: the next block's rows, the one after's ids
+        stage(ti_n, nk, nv);
+        block_rows((bi + 2) * kKeyBlock, ti_n);
+      }
       if (!live) return;
       f32x4 sc[4], dp[4];
       bqk<D>(ck, qf, sc, lane);   // S^T[key 16 kt + 4 g + j][query r]
@@ -373,7 +448,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
         }
       bpt<D>(ck, dp, dq, lane);   // dQ^T += K^T dS^T
     };
-    step(kst[(bi + 1) & 1], vst[(bi + 1) & 1], kst[bi & 1], vst[bi & 1]);
+    step(sm.kst[(bi + 1) & 1], sm.vst[(bi + 1) & 1], sm.kst[bi & 1], sm.vst[bi & 1]);
   }
   if (rw >= nrows) return;
   float* dst;
@@ -437,6 +512,105 @@ __global__ __launch_bounds__(256) void bwd_se_reduce_kernel(const float* __restr
     float a = 0.f;
     for (int p = 0; p < parts; ++p) a += se_dqt[(size_t)p * n + i];
     dqt[i] += a;
+  }
+}
+
+// The routed key-outer kernel sums each expert's queries in bucket order, and
+// the forward fills its buckets with atomics (any order: it computes every query
+// on its own). For sums in a fixed order the backward re-sorts the routing with a
+// stable counting sort: within each bucket, (query * s + slot) ascending, at the
+// forward's bucket offsets. Chunks of kPermChunk entries, a quarter per wave.
+constexpr int kPermChunk = 4096;
+
+// Entries of each expert per chunk (integer counts: order-free).
+__global__ __launch_bounds__(256) void bwd_perm_count_kernel(const int32_t* __restrict__ E, uint32_t* __restrict__ cb,
+                                                             int Ns, int m, int nch) {
+  extern __shared__ uint32_t h[];   // [m]
+  const int c = blockIdx.x, z = blockIdx.y, tid = threadIdx.x;
+  for (int i = tid; i < m; i += 256) h[i] = 0;
+  __syncthreads();
+  const int32_t* Ez = E + (size_t)z * Ns;
+  for (int j = tid; j < kPermChunk; j += 256) {
+    const int e = c * kPermChunk + j;
+    const int x = e < Ns ? Ez[e] : -1;
+    if ((unsigned)x < (unsigned)m) atomicAdd(&h[x], 1u);
+  }
+  __syncthreads();
+  for (int i = tid; i < m; i += 256) cb[((size_t)z * nch + c) * m + i] = h[i];
+}
+
+// Per (slice, expert): the chunk counts become the chunk's first position in the
+// bucket (the bucket offset plus the counts of the chunks before it).
+__global__ __launch_bounds__(256) void bwd_perm_scan_kernel(const uint32_t* __restrict__ boff,
+                                                            uint32_t* __restrict__ cb, int m, int nch, long n) {
+  const long t = (long)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n) return;
+  const long z = t / m;
+  const int e = (int)(t - z * m);
+  uint32_t run = boff[z * (m + 1) + e];
+  uint32_t* col = cb + (size_t)z * nch * m + e;
+  for (int c0 = 0; c0 < nch; c0 += 8) {
+    uint32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = c0 + u < nch ? col[(size_t)(c0 + u) * m] : 0u;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (c0 + u < nch) {
+        col[(size_t)(c0 + u) * m] = run;
+        run += v[u];
+      }
+  }
+}
+
+// Scatter in entry order: each wave takes its quarter of the chunk 64 entries at
+// a time; lanes with the same expert get consecutive positions in lane order
+// (one ballot per distinct expert), after every earlier entry of that expert.
+__global__ __launch_bounds__(256) void bwd_perm_fill_kernel(const int32_t* __restrict__ E,
+                                                            const uint32_t* __restrict__ cb,
+                                                            int32_t* __restrict__ perm, int Ns, int m, int nch) {
+  extern __shared__ uint32_t cw[];   // [4][m]: per-wave counts, then per-wave cursors
+  const int c = blockIdx.x, z = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  constexpr int kSteps = kPermChunk / 256;
+  for (int i = tid; i < 4 * m; i += 256) cw[i] = 0;
+  __syncthreads();
+  const int32_t* Ez = E + (size_t)z * Ns;
+  const int w0 = c * kPermChunk + w * (kPermChunk / 4);
+  int ex[kSteps];
+#pragma unroll
+  for (int u = 0; u < kSteps; ++u) {
+    const int e = w0 + 64 * u + lane;
+    ex[u] = e < Ns ? Ez[e] : -1;
+    if ((unsigned)ex[u] >= (unsigned)m) ex[u] = -1;
+    if (ex[u] >= 0) atomicAdd(&cw[w * m + ex[u]], 1u);
+  }
+  __syncthreads();
+  for (int i = tid; i < m; i += 256) {
+    uint32_t run = cb[((size_t)z * nch + c) * m + i];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint32_t t = cw[v * m + i];
+      cw[v * m + i] = run;
+      run += t;
+    }
+  }
+  __syncthreads();
+  int32_t* pz = perm + (size_t)z * Ns;
+  uint32_t* cur = cw + w * m;
+#pragma unroll
+  for (int u = 0; u < kSteps; ++u) {
+    const int x = ex[u];
+    uint64_t todo = __ballot(x >= 0);
+    while (todo) {
+      const int key = __builtin_amdgcn_readlane(x, __builtin_ctzll(todo));
+      const uint64_t same = __ballot(x == key);
+      const uint32_t b = cur[key];
+      if (x == key) {
+        const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(same >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)same, 0u));
+        pz[b + r] = w0 + 64 * u + lane;
+      }
+      if (lane == 0) cur[key] = b + (uint32_t)__popcll(same);
+      todo &= ~same;
+    }
   }
 }
 
@@ -612,6 +786,9 @@ void backward_plan(const Plan& p, BwdLayout* L) {
   L->icur = take(bh * N * 4);
   L->ioff = take(bh * N * 4);
   L->ilist = take(bh * m * k * 4);
+  L->pnch = (int)((N * s + kPermChunk - 1) / kPermChunk);
+  L->psort = take(bh * N * s * 4);
+  L->pbase = take(bh * (size_t)L->pnch * m * 4);
   L->total = off;
 }
 
@@ -628,7 +805,7 @@ static hipError_t backward_launch(const Plan& p, const BwdLayout& L, const void*
   a.vt16 = (const uint16_t*)(fws + p.ws.vt16);
   a.dvt16 = (const uint16_t*)(bws + L.dvt16);
   a.I = (const int32_t*)(fws + p.ws.I);
-  a.perm = (const int32_t*)(fws + p.ws.perm);
+  a.perm = (const int32_t*)(bws + L.psort);
   a.tiles = (const int4*)(fws + p.ws.tiles);
   a.boff = (const uint32_t*)(fws + p.ws.boff);
   a.lse = (const float*)(fws + p.ws.lse);
@@ -655,6 +832,20 @@ static hipError_t backward_launch(const Plan& p, const BwdLayout& L, const void*
   hipLaunchKernelGGL((bwd_rowdot_kernel<D, uint16_t, uint16_t>), dim3((unsigned)((BH * N + 15) / 16)), dim3(256), 0,
                      st, (const uint16_t*)dO, (const uint16_t*)O, (float*)(bws + L.Dq), BH * N);
   MITA_CHECK_LAUNCH();
+  // the routing re-sorted in a fixed order
+  {
+    const dim3 grid((unsigned)L.pnch, (unsigned)BH);
+    const int Ns = p.N * p.s;
+    hipLaunchKernelGGL(bwd_perm_count_kernel, grid, dim3(256), (size_t)p.m * 4, st, (const int32_t*)(fws + p.ws.E),
+                       (uint32_t*)(bws + L.pbase), Ns, p.m, L.pnch);
+    MITA_CHECK_LAUNCH();
+    hipLaunchKernelGGL(bwd_perm_scan_kernel, dim3((unsigned)((BH * m + 255) / 256)), dim3(256), 0, st,
+                       (const uint32_t*)(fws + p.ws.boff), (uint32_t*)(bws + L.pbase), p.m, L.pnch, BH * m);
+    MITA_CHECK_LAUNCH();
+    hipLaunchKernelGGL(bwd_perm_fill_kernel, grid, dim3(256), (size_t)p.m * 16, st, (const int32_t*)(fws + p.ws.E),
+                       (const uint32_t*)(bws + L.pbase), (int32_t*)(bws + L.psort), Ns, p.m, L.pnch);
+    MITA_CHECK_LAUNCH();
+  }
   // routed part: dQ per (query, slot); dK, dV per (expert, slot of its list)
   if (p.trows == 128)
     hipLaunchKernelGGL((bwd_q_kernel<D, kRouted, 8>), dim3((unsigned)(BH * p.max_tiles)), dim3(512), 0, st, a);

@@ -83,6 +83,7 @@ struct Plan {
 // the landmark part's queries and the shared part's keys for parallelism.
 struct BwdLayout {
   int qparts, kparts;
+  int pnch;         // chunks of the routing re-sort: ceil(N s / 4096)
   size_t Dq;        // f32 [BH, N]          rowsum(dO * O)
   size_t Di;        // f32 [BH, m]          rowsum(dV~ * V~)
   size_t dvt;       // f32 [BH, m, d]       dV~
@@ -101,6 +102,8 @@ struct BwdLayout {
   size_t icur;      // u32 [BH, N]          fill cursors
   size_t ioff;      // u32 [BH, N]          list offsets
   size_t ilist;     // u32 [BH, m k]        (expert, slot) entries per token, in expert order
+  size_t psort;     // i32 [BH, N s]        the routing grouped by expert, (query * s + slot) ascending per bucket
+  size_t pbase;     // u32 [BH, pnch, m]    per chunk: entries of each expert, then their first position
   size_t total;
 };
 void backward_plan(const Plan& p, BwdLayout* L);

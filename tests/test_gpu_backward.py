@@ -80,7 +80,9 @@ def test_backward_matches_oracle(w, lib):
 def test_backward_full_size_invariant(lib):
     """The long workload whole (B=2, H=16, N=65536, d=128, m=256, k=256, s=2): every
     query's weights and every shared-expert row sum to 1, so per slice the value
-    gradients add up to the sum of the output gradients; all gradients finite."""
+    gradients add up to the sum of the output gradients; all gradients finite; a
+    second call is bit-identical (the forward fills its buckets in atomic order
+    from many workgroups at this size; the backward must not depend on it)."""
     w = W["long"]
     say("[backward-full] long: forward + backward")
     Q, K, V = synth.make_inputs(w)
@@ -88,8 +90,13 @@ def test_backward_full_size_invariant(lib):
     call = lib.Mita.create(Qd, w.m, w.k, w.s, grid=(w.grid_h, w.grid_w), pool=(w.pool_h, w.pool_w))
     O = call.forward(Qd, Kd, Vd)
     dOd = (torch.randn(Qd.shape, device="cuda", generator=torch.Generator("cuda").manual_seed(3))).to(torch.bfloat16)
-    dQ, dK, dV = call.backward(Qd, Kd, Vd, O, dOd)
+    dQ, dK, dV = (t.clone() for t in call.backward(Qd, Kd, Vd, O, dOd))
+    O2 = call.forward(Qd, Kd, Vd)   # buckets refilled
+    g2 = call.backward(Qd, Kd, Vd, O2, dOd)
     torch.cuda.synchronize()
+    assert torch.equal(O, O2)
+    for name, a, b in zip(("dQ", "dK", "dV"), (dQ, dK, dV), g2):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"{name} differs between two calls"
     for g in (dQ, dK, dV):
         assert torch.isfinite(g).all()
     lhs = dV.double().sum(dim=2)

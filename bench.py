@@ -95,7 +95,9 @@ def kernel_names(w) -> dict:
         gather = "gather1_kernel" if w.k <= 64 else "gather_kernel"
     else:   # partials: the direct-load kernel for bf16 inputs
         gather = "gatherd_kernel" if w.dtype == "bf16" else "gather_kernel"
-    return {"pool": "pool_kernel", "landmark": "landmark_kernel", "topk": "topk_cand_kernel",
+    direct = w.dtype == "bf16" and w.m > 64   # several landmark tiles: the direct-load kernels
+    return {"pool": "pool_kernel", "landmark": "landmarkd_kernel" if direct else "landmark_kernel",
+            "topk": "topk_candd_kernel" if direct else "topk_cand_kernel",
             "route": "route_fast_kernel" if w.m <= 64 else "route_multi_kernel", "gather": gather,
             "combine": "combined_kernel" if w.dtype == "bf16" else "combine_kernel"}
 

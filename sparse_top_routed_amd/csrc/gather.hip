@@ -484,12 +484,14 @@ void gather_kernel(const T* __restrict__ Q, const T* __restrict__ K,
 // does its softmax meanwhile. Held to two waves per SIMD. The softmax keeps a
 // lazily raised reference and sums the probabilities as rounded for P V
 // (lazy_softmax).
-// Landmark merge (bf16): waves per workgroup and landmark buffers. Four waves on one
-// buffer (48 KB of LDS for d = 128) let two workgroups share a CU, so while one
-// waits for its next block or its partials the other computes: faster than eight
-// waves on two buffers (one workgroup per CU, its waves in lockstep): very long
-// merge 1.41 -> 1.24 ms, long 0.82 -> 0.69 ms.
-constexpr int kCombineWaves = 4, kCombineBuffers = 1;
+// Landmark merge (bf16): waves per workgroup and landmark buffers. Four-wave
+// workgroups, two per CU, so while one waits for its partials the other computes
+// (eight waves in one workgroup run in lockstep: very long merge 1.41 ms against
+// 1.24 ms). With Q~ staged as one bf16 tile, two buffers take 64 KB of LDS for
+// d = 128 and two workgroups still fit a CU; the next block then loads while this
+// one computes: very long merge 1.16 -> 1.07 ms, long 0.62 -> 0.58 ms against one
+// buffer.
+constexpr int kCombineWaves = 4, kCombineBuffers = 2;
 
 template <int D>
 struct GatherDLds {
@@ -939,11 +941,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Q, c
 }
 
 // The same for bf16 inputs with NW waves of QT column tiles (16 QT NW consecutive
-// queries per workgroup): the landmark blocks (Q~ hi and lo planes,
-// V~) are staged by direct loads into tiles that every wave
-// reads (V~ transposed), so each block is fetched once per 16 QT NW queries and
-// each fragment read feeds QT MFMAs. The softmax keeps a lazily raised reference
-// and sums the probabilities as rounded for the product (see lazy_softmax).
+// queries per workgroup): the landmark blocks (Q~ as bf16, V~) are staged by
+// direct loads into tiles that every wave reads (V~ transposed), so each block is
+// fetched once per 16 QT NW queries and each fragment read feeds QT MFMAs. These
+// scores only weight the output (no selection rests on them), so Q~ takes the
+// precision of the other bf16 operands: its hi plane, the bf16 rounding of the
+// fp64 landmark (routing and the expert sets use both planes). The softmax keeps
+// a lazily raised reference and sums the probabilities as rounded for the product
+// (see lazy_softmax).
 // MFULL: m is a multiple of the key block (no masking code). SU: partial slots
 // loaded together in the seed (1, 2 or 4). NB: landmark buffers (2: the next
 // block loads while one computes; 1: less LDS, so more workgroups per CU).
@@ -956,17 +961,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // one shared object: with separate ones the compiler's LDS scopes would make the
   // next block's loads look like writes to the block being read
   __shared__ __align__(16) struct {
-    uint16_t kk[NB][2 * U::TILE];   // per buffer: Q~ hi tile, then lo tile
+    uint16_t kk[NB][U::TILE];   // Q~ (hi plane)
     uint16_t vv[NB][U::TILE];
   } sm;
   const int z = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
   const int qw = blockIdx.x * (16 * QT * NW) + QT * 16 * w + r;   // query of column tile qt: qw + 16 qt
   const uint16_t* hz = qtop + (size_t)z * 2 * m * D;
-  const uint16_t* lz = hz + (size_t)m * D;
   const uint16_t* vz = vt16 + (size_t)z * m * D;
   auto stage = [&](int lb, uint16_t* tk, uint16_t* tv) __attribute__((always_inline)) {
     udma<D, NW>(tk, [&](int row) __attribute__((always_inline)) { return hz + (size_t)min(lb + row, m - 1) * D; }, w, lane);
-    udma<D, NW>(tk + U::TILE, [&](int row) __attribute__((always_inline)) { return lz + (size_t)min(lb + row, m - 1) * D; }, w, lane);
     udma<D, NW>(tv, [&](int row) __attribute__((always_inline)) { return vz + (size_t)min(lb + row, m - 1) * D; }, w, lane);
   };
   stage(0, sm.kk[0], sm.vv[0]);
@@ -1033,7 +1036,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   auto attend = [&](int j, const uint16_t* ck, const uint16_t* cv) __attribute__((always_inline)) {
     f32x4 acc[QT][4];
     __builtin_amdgcn_s_setprio(1);
-    uqk<D, QT, 2>(ck, ck + U::TILE, qf, acc, lane);
+    uqk<D, QT, 1>(ck, nullptr, qf, acc, lane);
     lazy_softmax<D, QT>(acc, MFULL ? kKeyBlock : min(kKeyBlock, m - j * kKeyBlock), sl2e, mrun, lrun, o, lane);
     upv<D, QT>(cv, acc, o, lrun, lane);
     __builtin_amdgcn_s_setprio(0);

@@ -201,12 +201,16 @@ __device__ __forceinline__ void rescale(f32x4 (&o)[D / 16], float alpha) {
 // are the row's output and sum rescaled (one wave-uniform branch for all tiles).
 // Numerator and denominator share the reference, so the softmax is unchanged;
 // the probabilities stay below 2^kLazyLog2. Row sums are left to the caller.
+// A row's maximum is the largest of its four lanes' maxima, so the test runs on
+// each lane's own maximum (c > 0 keeps the order) and the row maxima, which need
+// lanes of other lane groups, are formed only in the rare branch that moves a
+// reference.
 constexpr float kLazyLog2 = 8.f;
 
 template <int D, int QT>
 __device__ __forceinline__ void lazy_softmax(f32x4 (&x)[QT][4], int live, float c, float (&mrun)[QT],
                                              float (&lrun)[QT], f32x4 (&o)[QT][D / 16], int lane) {
-  float bm[QT];
+  float lm[QT];
   bool any = false;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
@@ -223,16 +227,18 @@ __device__ __forceinline__ void lazy_softmax(f32x4 (&x)[QT][4], int live, float 
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) v = fmaxf(v, x[qt][kt][j]);
-    bm[qt] = quad_max(v) * c;
-    any |= bm[qt] > mrun[qt] + kLazyLog2;
+    lm[qt] = v;
+    any |= v * c > mrun[qt] + kLazyLog2;
   }
   if (__builtin_amdgcn_ballot_w64(any) != 0) {   // wave-uniform
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      const bool up = bm[qt] > mrun[qt] + kLazyLog2;
+#pragma clang fp contract(off)   // bm rounded: alpha takes the new reference itself
+      const float bm = quad_max(lm[qt]) * c;
+      const bool up = bm > mrun[qt] + kLazyLog2;
       // raw v_exp_f32; 2^(-inf) = 0 clears the empty state of the first block
-      const float alpha = up ? __builtin_amdgcn_exp2f(mrun[qt] - bm[qt]) : 1.f;
-      mrun[qt] = up ? bm[qt] : mrun[qt];
+      const float alpha = up ? __builtin_amdgcn_exp2f(mrun[qt] - bm) : 1.f;
+      mrun[qt] = up ? bm : mrun[qt];
       lrun[qt] *= alpha;
       rescale<D>(o[qt], alpha);
     }

@@ -676,10 +676,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
             amax = quad_max(amax) * inv;
             const float sc = amax > 0.f ? amax : 1.f, wv = inv / sc;
             uint16_t* prow = pacc + ps * D;
+            // Column blocks in pairs (16 dt .. 16 dt + 31): lanes of groups g and g ^ 1
+            // (the same row) trade half their values, so each lane stores 16
+            // contiguous bytes and the row's four lanes 64: even g the block dt at
+            // columns 4 g .., odd g the block dt + 1 at columns 4 (g - 1) ..
 #pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt)
-              *(uint2*)(prow + 16 * dt + 4 * g) = make_uint2(pack_f16x2(o[qt][dt][0] * wv, o[qt][dt][1] * wv),
-                                                             pack_f16x2(o[qt][dt][2] * wv, o[qt][dt][3] * wv));
+            for (int dt = 0; dt < D / 16; dt += 2) {
+              const auto s0 = __builtin_amdgcn_permlane16_swap(pack_f16x2(o[qt][dt][0] * wv, o[qt][dt][1] * wv),
+                                                               pack_f16x2(o[qt][dt + 1][0] * wv, o[qt][dt + 1][1] * wv),
+                                                               false, false);
+              const auto s1 = __builtin_amdgcn_permlane16_swap(pack_f16x2(o[qt][dt][2] * wv, o[qt][dt][3] * wv),
+                                                               pack_f16x2(o[qt][dt + 1][2] * wv, o[qt][dt + 1][3] * wv),
+                                                               false, false);
+              *(uint4*)(prow + 16 * dt + 16 * (g & 1) + 4 * (g & 2)) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+            }
             if (g == 0) *(float4*)(pml + ps * 4) = make_float4(mrun[qt], l, sc, 0.f);
           }
         }

@@ -620,13 +620,44 @@ __device__ __forceinline__ void upv(const uint16_t* T, const f32x4 (&p)[QT][4], 
   }
 }
 
-// Write 4 consecutive outputs d0..d0+3 of one row.
-template <typename T>
-__device__ __forceinline__ void store4(T* dst, float a, float b, float c, float d) {
+// A row's D outputs in the S^T layout sit on its four lanes (lane group g holds
+// columns 16 dt + 4 g .. + 3 of every 16-column block dt), 8 bytes per block for
+// 16-bit values. Row stores and loads go in 16-byte pieces instead: over a pair of
+// blocks (dt, dt + 1) the lanes of groups g and g ^ 1 trade half their values
+// with v_permlane16_swap, after which even g holds columns 16 dt + 4 g .. + 7 and
+// odd g columns 16 (dt + 1) + 4 (g - 1) .. + 7, at this offset (in elements) from
+// the row's start. The trade is its own inverse: applied to such a piece after a
+// load it gives back the two 8-byte values of the lane's own columns.
+__device__ __forceinline__ int pair_col(int dt, int g) { return 16 * dt + 16 * (g & 1) + 4 * (g & 2); }
+// lane values a (block dt), b (block dt + 1), two 32-bit words each -> the piece
+__device__ __forceinline__ uint4 pair_trade(uint2 a, uint2 b) {
+  const auto x = __builtin_amdgcn_permlane16_swap(a.x, b.x, false, false);
+  const auto y = __builtin_amdgcn_permlane16_swap(a.y, b.y, false, false);
+  return make_uint4(x[0], y[0], x[1], y[1]);
+}
+// the piece -> the lane values of blocks dt (first) and dt + 1 (second)
+__device__ __forceinline__ void pair_untrade(uint4 c, uint2& a, uint2& b) {
+  const auto x = __builtin_amdgcn_permlane16_swap(c.x, c.z, false, false);
+  const auto y = __builtin_amdgcn_permlane16_swap(c.y, c.w, false, false);
+  a = make_uint2(x[0], y[0]);
+  b = make_uint2(x[1], y[1]);
+}
+
+// One row's D outputs o[dt] * inv from its four lanes (every lane of the row
+// calls it): 16-byte pieces for bf16, the lane's 16 bytes per block for fp32.
+template <typename T, int D>
+__device__ __forceinline__ void store_row(T* orow, const f32x4 (&o)[D / 16], float inv, int g) {
   if constexpr (sizeof(T) == 2) {
-    *(uint2*)dst = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
+#pragma unroll
+    for (int dt = 0; dt < D / 16; dt += 2)
+      *(uint4*)(orow + pair_col(dt, g)) =
+          pair_trade(make_uint2(pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv), pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv)),
+                     make_uint2(pack_bf16x2(o[dt + 1][0] * inv, o[dt + 1][1] * inv),
+                                pack_bf16x2(o[dt + 1][2] * inv, o[dt + 1][3] * inv)));
   } else {
-    *(float4*)dst = make_float4(a, b, c, d);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+      *(float4*)(orow + 16 * dt + 4 * g) = make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
   }
 }
 

@@ -54,9 +54,7 @@ __global__ __launch_bounds__(256) void dense_kernel(const T* __restrict__ Q, con
   const float inv = 1.f / quad_sum(lrun);
   if (q < N) {
     T* orow = out + ((size_t)z * N + q) * D;
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-      store4<T>(orow + 16 * dt + 4 * g, o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+    store_row<T, D>(orow, o, inv, g);
   }
 }
 

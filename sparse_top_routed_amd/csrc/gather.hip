@@ -433,9 +433,7 @@ void gather_kernel(const T* __restrict__ Q, const T* __restrict__ K,
             T* orow = out + ((size_t)zc * N + q) * D;
             const float inv = 1.f / l;
             if (g == 0) lse[(size_t)zc * N + q] = mrun + log2f(l);
-#pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt)
-              store4<T>(orow + 16 * dt + 4 * g, o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+            store_row<T, D>(orow, o, inv, g);
           } else {   // the slot's output o / l, divided by its largest magnitude (the quad holds the row)
             const size_t ps = ((size_t)zc * N + q) * s + slot;
             const float inv = 1.f / l;
@@ -447,11 +445,13 @@ void gather_kernel(const T* __restrict__ Q, const T* __restrict__ K,
             amax = quad_max(amax) * inv;
             const float sc = amax > 0.f ? amax : 1.f, wv = inv / sc;
             if constexpr (BF) {   // fp16 in [-1, 1]: 2^-11 relative to the slot's largest value
-              uint16_t* prow = (uint16_t*)pacc + ps * D;
+              uint16_t* prow = (uint16_t*)pacc + ps * D;   // 16-byte pieces (pair_trade)
 #pragma unroll
-              for (int dt = 0; dt < D / 16; ++dt)
-                *(uint2*)(prow + 16 * dt + 4 * g) = make_uint2(pack_f16x2(o[dt][0] * wv, o[dt][1] * wv),
-                                                               pack_f16x2(o[dt][2] * wv, o[dt][3] * wv));
+              for (int dt = 0; dt < D / 16; dt += 2)
+                *(uint4*)(prow + pair_col(dt, g)) =
+                    pair_trade(make_uint2(pack_f16x2(o[dt][0] * wv, o[dt][1] * wv), pack_f16x2(o[dt][2] * wv, o[dt][3] * wv)),
+                               make_uint2(pack_f16x2(o[dt + 1][0] * wv, o[dt + 1][1] * wv),
+                                          pack_f16x2(o[dt + 1][2] * wv, o[dt + 1][3] * wv)));
             } else {
               float* prow = (float*)pacc + ps * D;
 #pragma unroll
@@ -676,20 +676,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
             amax = quad_max(amax) * inv;
             const float sc = amax > 0.f ? amax : 1.f, wv = inv / sc;
             uint16_t* prow = pacc + ps * D;
-            // Column blocks in pairs (16 dt .. 16 dt + 31): lanes of groups g and g ^ 1
-            // (the same row) trade half their values, so each lane stores 16
-            // contiguous bytes and the row's four lanes 64: even g the block dt at
-            // columns 4 g .., odd g the block dt + 1 at columns 4 (g - 1) ..
+            // 16-byte pieces (pair_trade): the row's four lanes store 64 contiguous bytes
 #pragma unroll
-            for (int dt = 0; dt < D / 16; dt += 2) {
-              const auto s0 = __builtin_amdgcn_permlane16_swap(pack_f16x2(o[qt][dt][0] * wv, o[qt][dt][1] * wv),
-                                                               pack_f16x2(o[qt][dt + 1][0] * wv, o[qt][dt + 1][1] * wv),
-                                                               false, false);
-              const auto s1 = __builtin_amdgcn_permlane16_swap(pack_f16x2(o[qt][dt][2] * wv, o[qt][dt][3] * wv),
-                                                               pack_f16x2(o[qt][dt + 1][2] * wv, o[qt][dt + 1][3] * wv),
-                                                               false, false);
-              *(uint4*)(prow + 16 * dt + 16 * (g & 1) + 4 * (g & 2)) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
-            }
+            for (int dt = 0; dt < D / 16; dt += 2)
+              *(uint4*)(prow + pair_col(dt, g)) =
+                  pair_trade(make_uint2(pack_f16x2(o[qt][dt][0] * wv, o[qt][dt][1] * wv),
+                                        pack_f16x2(o[qt][dt][2] * wv, o[qt][dt][3] * wv)),
+                             make_uint2(pack_f16x2(o[qt][dt + 1][0] * wv, o[qt][dt + 1][1] * wv),
+                                        pack_f16x2(o[qt][dt + 1][2] * wv, o[qt][dt + 1][3] * wv)));
             if (g == 0) *(float4*)(pml + ps * 4) = make_float4(mrun[qt], l, sc, 0.f);
           }
         }
@@ -877,9 +871,7 @@ __global__ __launch_bounds__(256) void gather1_kernel(const T* __restrict__ Q, c
         if (rowi < cur.z) {
           if (g == 0) lse[(size_t)zc * N + q] = mx + log2f(lt);
           T* orow = out + ((size_t)zc * N + q) * D;
-#pragma unroll
-          for (int dt = 0; dt < D / 16; ++dt)
-            store4<T>(orow + 16 * dt + 4 * g, o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+          store_row<T, D>(orow, o, inv, g);
         }
       }
     };
@@ -926,9 +918,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Q, c
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       float4 a;
-      if constexpr (sizeof(T) == 2) {
-        const uint2 u = *(const uint2*)((const uint16_t*)pacc + (p0 + sl) * D + 16 * dt + 4 * g);
-        a = make_float4(f16_lo(u.x), f16_hi(u.x), f16_lo(u.y), f16_hi(u.y));
+      if constexpr (sizeof(T) == 2) {   // 16-byte pieces (pair_untrade)
+        if (dt % 2) continue;
+        uint2 u0, u1;
+        pair_untrade(*(const uint4*)((const uint16_t*)pacc + (p0 + sl) * D + pair_col(dt, g)), u0, u1);
+        o[dt + 1][0] += wv * f16_lo(u1.x);
+        o[dt + 1][1] += wv * f16_hi(u1.x);
+        o[dt + 1][2] += wv * f16_lo(u1.y);
+        o[dt + 1][3] += wv * f16_hi(u1.y);
+        a = make_float4(f16_lo(u0.x), f16_hi(u0.x), f16_lo(u0.y), f16_hi(u0.y));
       } else {
         a = *(const float4*)((const float*)pacc + (p0 + sl) * D + 16 * dt + 4 * g);
       }
@@ -945,9 +943,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Q, c
   const float lt = quad_sum(lrun), inv = 1.f / lt;
   if (g == 0) lse[(size_t)z * N + q] = mrun + log2f(lt);
   T* orow = out + ((size_t)z * N + q) * D;
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt)
-    store4<T>(orow + 16 * dt + 4 * g, o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+  store_row<T, D>(orow, o, inv, g);
 }
 
 // The same for bf16 inputs with NW waves of QT column tiles (16 QT NW consecutive
@@ -1002,14 +998,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
     for (int sl = 0; sl < SU; ++sl) ml[qt][sl] = *(const float4*)(pml + (p0[qt] + min(sl, s - 1)) * 4);
   }
-  uint2 u[QT][SU][D / 16];
+  // partial rows in the 16-byte pieces the routed kernel stores (pair_untrade below)
+  uint4 u[QT][SU][D / 32];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
     for (int sl = 0; sl < SU; ++sl)
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt)
-        u[qt][sl][dt] = *(const uint2*)(pacc + (p0[qt] + min(sl, s - 1)) * D + 16 * dt + 4 * g);
+      for (int dp = 0; dp < D / 32; ++dp)
+        u[qt][sl][dp] = *(const uint4*)(pacc + (p0[qt] + min(sl, s - 1)) * D + pair_col(2 * dp, g));
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     float M = -INFINITY;
@@ -1019,24 +1016,30 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     float l = 0.f;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) o[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto add = [&](const float4& m4, const uint2 (&uu)[D / 16], bool use) __attribute__((always_inline)) {
+    auto add = [&](const float4& m4, const uint4 (&uc)[D / 32], bool use) __attribute__((always_inline)) {
       const float f = use ? exp2f(m4.x - M) : 0.f;
       l += f * m4.y;
       const float wv = f * m4.y * m4.z;
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        o[qt][dt][0] += wv * f16_lo(uu[dt].x);
-        o[qt][dt][1] += wv * f16_hi(uu[dt].x);
-        o[qt][dt][2] += wv * f16_lo(uu[dt].y);
-        o[qt][dt][3] += wv * f16_hi(uu[dt].y);
+      for (int dp = 0; dp < D / 32; ++dp) {
+        uint2 uu[2];
+        pair_untrade(uc[dp], uu[0], uu[1]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int dt = 2 * dp + h;
+          o[qt][dt][0] += wv * f16_lo(uu[h].x);
+          o[qt][dt][1] += wv * f16_hi(uu[h].x);
+          o[qt][dt][2] += wv * f16_lo(uu[h].y);
+          o[qt][dt][3] += wv * f16_hi(uu[h].y);
+        }
       }
     };
 #pragma unroll
     for (int sl = 0; sl < SU; ++sl) add(ml[qt][sl], u[qt][sl], sl < s);
     for (int sl = SU; sl < s; ++sl) {
-      uint2 ut[D / 16];
+      uint4 ut[D / 32];
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) ut[dt] = *(const uint2*)(pacc + (p0[qt] + sl) * D + 16 * dt + 4 * g);
+      for (int dp = 0; dp < D / 32; ++dp) ut[dp] = *(const uint4*)(pacc + (p0[qt] + sl) * D + pair_col(2 * dp, g));
       add(*(const float4*)(pml + (p0[qt] + sl) * 4), ut, true);
     }
     mrun[qt] = M;
@@ -1080,13 +1083,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   for (int qt = 0; qt < QT; ++qt) {
     const int q = qw + 16 * qt;
     const float lt = quad_sum(lrun[qt]), inv = 1.f / lt;
+    uint4 pc[D / 32];   // the row in 16-byte pieces (pair_trade), formed by all lanes
+#pragma unroll
+    for (int dp = 0; dp < D / 32; ++dp) {
+      const f32x4 &a = o[qt][2 * dp], &b = o[qt][2 * dp + 1];
+      pc[dp] = pair_trade(make_uint2(pack_bf16x2(a[0] * inv, a[1] * inv), pack_bf16x2(a[2] * inv, a[3] * inv)),
+                          make_uint2(pack_bf16x2(b[0] * inv, b[1] * inv), pack_bf16x2(b[2] * inv, b[3] * inv)));
+    }
     if (q >= N) continue;
     if (g == 0) lse[(size_t)z * N + q] = mrun[qt] + log2f(lt);
     uint16_t* orow = out + ((size_t)z * N + q) * D;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-      store4<uint16_t>(orow + 16 * dt + 4 * g, o[qt][dt][0] * inv, o[qt][dt][1] * inv, o[qt][dt][2] * inv,
-                       o[qt][dt][3] * inv);
+    for (int dp = 0; dp < D / 32; ++dp) *(uint4*)(orow + pair_col(2 * dp, g)) = pc[dp];
   }
 }
 

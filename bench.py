@@ -387,7 +387,9 @@ def main() -> int:
     ap.add_argument("--print-sha", action="store_true", help="print the dominant kernels' source hashes and exit")
     ap.add_argument("--sweep", action="store_true",
                     help="time the forward pass over the inference-time (m, k, s) settings of synth.SWEEP on the "
-                         "workload's inputs (one JSON line per setting) instead of the benchmark line")
+                         "workload's inputs (one JSON line per setting) instead of the benchmark line; the settings "
+                         "are pooling grids of the ViT-B-like workload, which it uses unless --workload names another "
+                         "2D-grid workload")
     ap.add_argument("--backward", action="store_true",
                     help="time the forward and the backward (mita_backward) on the workload's inputs (one JSON line) "
                          "instead of the benchmark line")
@@ -408,6 +410,8 @@ def main() -> int:
 
     import synth
 
+    if a.sweep and a.workload == ap.get_default("workload"):
+        a.workload = "vit_b"
     w = synth.WORKLOADS[a.workload]
     # the CPU baseline runs first, before anything touches the GPU: its worker
     # processes start from a clean interpreter and never share the GPU timing

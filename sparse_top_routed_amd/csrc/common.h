@@ -58,8 +58,9 @@ __device__ __forceinline__ bool chunk_item(int lm_tiles, int nsplit, int BH, int
 // ---------------------------------------------------------------- order keys
 // Monotone map of float32 onto uint32: a < b (as floats) iff key(a) < key(b).
 __device__ __forceinline__ uint32_t f32_key(float x) {
-  uint32_t u = __float_as_uint(x);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  // negative: all bits flipped; otherwise the sign bit set (no branch or select)
+  const uint32_t u = __float_as_uint(x);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 __device__ __forceinline__ float key_f32(uint32_t k) {
   uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;

@@ -346,7 +346,7 @@ __global__ __launch_bounds__(256) void route_fast_kernel(const T* __restrict__ Q
 // than the few registers that spill.
 // A query is certain, or its band is re-scored in fp64 when the list holds it,
 // or it is queued for the exact kernel.
-template <typename T, int D, int TM, int TPW>
+template <typename T, int D, int TM, int TPW, bool MFULL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void route_multi_kernel(const T* __restrict__ Q, const void* __restrict__ qtop,
                                                           const double* __restrict__ qt64,
                                                           const float* __restrict__ qtnorm, int32_t* __restrict__ E,
@@ -437,8 +437,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int li = lb0 + 16 * kt + 4 * g + j;   // past m: key 0 never enters the list
-          top_insert<TM>(tk[tt], li < m ? rk.make(acc[kt][j], li) : 0u);
+          const int li = lb0 + 16 * kt + 4 * g + j;
+          const uint32_t key = rk.make(acc[kt][j], li);
+          // past m: key 0, which never enters the list; an arithmetic mask (a
+          // conditional here compiled to a branch per score), none when m is a
+          // multiple of the block
+          top_insert<TM>(tk[tt], MFULL ? key : key & (uint32_t)((li - m) >> 31));
         }
     }
   }
@@ -586,7 +590,8 @@ static hipError_t route_fast_launch(const Plan& p, const void* Q, char* ws, hipS
     constexpr int TPW = (sizeof(T) == 2 && D == 64) ? 4 : 2;
     // the rare queries the lists cannot settle go to the exact kernel (an in-kernel
     // exact pass would cost every workgroup its registers)
-    hipLaunchKernelGGL((route_multi_kernel<T, D, TM, TPW>), dim3((p.qtiles + TPW - 1) / TPW, p.BH), dim3(256), 0, st, (const T*)Q,
+    auto kern = p.m % kKeyBlock == 0 ? route_multi_kernel<T, D, TM, TPW, true> : route_multi_kernel<T, D, TM, TPW, false>;
+    hipLaunchKernelGGL(kern, dim3((p.qtiles + TPW - 1) / TPW, p.BH), dim3(256), 0, st, (const T*)Q,
                        (const void*)(ws + p.ws.qtop), (const double*)(ws + p.ws.qt64), (const float*)(ws + p.ws.qtnorm),
                        (int32_t*)(ws + p.ws.E), (uint32_t*)(ws + p.ws.counters), (uint32_t*)(ws + p.ws.rflag), p.N,
                        p.m, p.s, p.gamma_qk, p.qtiles);

@@ -22,8 +22,8 @@
 // Determinism: no float atomics. Partial sums go to per-part buffers reduced in
 // a fixed order; each expert's queries are taken in ascending (query, slot) order
 // (a stable re-sort of the routing); a token's routed dK/dV rows are summed over
-// the experts that hold it in expert order (an inverse list built one expert at a
-// time).
+// the experts that hold it in expert order (an inverse list placed by per-token
+// expert bitmaps).
 //
 // Tiles (64 rows of D bf16) are read two ways: as QK operands (16 consecutive
 // rows at one 16-byte chunk) and transposed (8 consecutive rows x 2 neighbouring
@@ -614,63 +614,100 @@ __global__ __launch_bounds__(256) void bwd_perm_fill_kernel(const int32_t* __res
   }
 }
 
-// Inverse lists of the expert sets: how many experts hold each token.
-__global__ __launch_bounds__(256) void bwd_inv_count_kernel(const int32_t* __restrict__ I, uint32_t* __restrict__ cnt,
-                                                            int N, int mk, long total) {
+// Inverse lists of the expert sets: per token, the (expert, slot) entries of the
+// experts that hold it, in expert order. Each token gets a bitmap of the experts
+// holding it (atomic OR: order-free); its count is the bitmap's popcount, its list
+// offset an exclusive scan of the counts (per block of kInvBlock tokens, then over
+// the blocks of a slice), and an entry's place in the list the popcount of the
+// token's bits below its expert: every step is parallel and the order is fixed.
+constexpr int kInvBlock = 1024;   // tokens per scan block (256 threads x 4)
+
+__global__ __launch_bounds__(256) void bwd_inv_mark_kernel(const int32_t* __restrict__ I,
+                                                           uint32_t* __restrict__ bits, int N, int m, int k, int W,
+                                                           long total) {
   for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
-    const long z = i / mk;
-    atomicAdd(&cnt[z * N + I[i]], 1u);   // integer counts: order-free
+    const long z = i / ((long)m * k);
+    const int e = (int)((i / k) % m);
+    atomicOr(&bits[((size_t)z * N + I[i]) * W + (e >> 5)], 1u << (e & 31));   // integer OR: order-free
   }
 }
 
-// Exclusive scan of each slice's counts (one workgroup per slice).
-__global__ __launch_bounds__(1024) void bwd_inv_scan_kernel(const uint32_t* __restrict__ cnt, uint32_t* __restrict__ off,
-                                                            int N) {
-  __shared__ uint32_t wt[16];
+// Counts, and their exclusive scan within each block of kInvBlock tokens (off);
+// the block totals go to bsum [BH, nb].
+__global__ __launch_bounds__(256) void bwd_inv_count_kernel(const uint32_t* __restrict__ bits,
+                                                            uint32_t* __restrict__ cnt, uint32_t* __restrict__ off,
+                                                            uint32_t* __restrict__ bsum, int N, int W, int nb) {
+  __shared__ uint32_t wtot[4];
+  const int b = blockIdx.x, z = blockIdx.y, tid = threadIdx.x;
+  uint32_t c[4], sum = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int t = b * kInvBlock + 4 * tid + u;
+    c[u] = 0;
+    if (t < N) {
+      const uint32_t* bt = bits + ((size_t)z * N + t) * W;
+      for (int w = 0; w < W; ++w) c[u] += __popc(bt[w]);
+    }
+    sum += c[u];
+  }
+  uint32_t tot;
+  uint32_t run = block_incl_scan(sum, wtot, tot) - sum;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int t = b * kInvBlock + 4 * tid + u;
+    if (t < N) {
+      cnt[(size_t)z * N + t] = c[u];
+      off[(size_t)z * N + t] = run;
+    }
+    run += c[u];
+  }
+  if (tid == 0) bsum[(size_t)z * nb + b] = tot;
+}
+
+// Exclusive scan of each slice's block totals (one workgroup per slice), then
+// added to the offsets of the block's tokens by bwd_inv_offset_kernel.
+__global__ __launch_bounds__(256) void bwd_inv_bscan_kernel(uint32_t* __restrict__ bsum, int nb) {
+  __shared__ uint32_t wtot[4];
   __shared__ uint32_t carry;
-  const int z = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int z = blockIdx.x, tid = threadIdx.x;
   if (tid == 0) carry = 0;
   __syncthreads();
-  for (int b0 = 0; b0 < N; b0 += 1024) {
-    const int i = b0 + tid;
-    const uint32_t v = i < N ? cnt[(size_t)z * N + i] : 0u;
+  for (int b0 = 0; b0 < nb; b0 += 256) {
+    const int b = b0 + tid;
+    const uint32_t v = b < nb ? bsum[(size_t)z * nb + b] : 0u;
     uint32_t tot;
-    const uint32_t ex = wave_excl_scan(v, tot);
-    if (lane == 0) wt[w] = tot;
+    const uint32_t ex = block_incl_scan(v, wtot, tot) - v + carry;
+    if (b < nb) bsum[(size_t)z * nb + b] = ex;
     __syncthreads();
-    uint32_t before = carry;
-    for (int j = 0; j < w; ++j) before += wt[j];
-    if (i < N) off[(size_t)z * N + i] = before + ex;
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t s = 0;
-      for (int j = 0; j < 16; ++j) s += wt[j];
-      carry += s;
-    }
+    if (tid == 0) carry += tot;
     __syncthreads();
   }
 }
 
-// Fills the lists one expert at a time (a token appears at most once per expert, so
-// the threads of one step touch distinct tokens): each token's entries end up in
-// expert order, whatever the scheduling.
-__global__ __launch_bounds__(1024) void bwd_inv_fill_kernel(const int32_t* __restrict__ I,
-                                                            const uint32_t* __restrict__ off,
-                                                            uint32_t* __restrict__ cur, uint32_t* __restrict__ list,
-                                                            int N, int m, int k) {
-  const int z = blockIdx.x;
-  const int32_t* Iz = I + (size_t)z * m * k;
-  uint32_t* lz = list + (size_t)z * m * k;
-  const uint32_t* oz = off + (size_t)z * N;
-  uint32_t* cz = cur + (size_t)z * N;
-  for (int e = 0; e < m; ++e) {
-    for (int j = threadIdx.x; j < k; j += 1024) {
-      const int t = Iz[(size_t)e * k + j];
-      const uint32_t c = cz[t];
-      lz[oz[t] + c] = (uint32_t)(e * k + j);
-      cz[t] = c + 1;
-    }
-    __syncthreads();
+__global__ __launch_bounds__(256) void bwd_inv_offset_kernel(uint32_t* __restrict__ off,
+                                                             const uint32_t* __restrict__ bsum, int N, int nb,
+                                                             long total) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
+    const long z = i / N;
+    off[i] += bsum[z * nb + (i - z * N) / kInvBlock];
+  }
+}
+
+// Each (expert, slot) entry written at its token's offset plus the number of
+// experts below it that hold the token.
+__global__ __launch_bounds__(256) void bwd_inv_fill_kernel(const int32_t* __restrict__ I,
+                                                           const uint32_t* __restrict__ bits,
+                                                           const uint32_t* __restrict__ off,
+                                                           uint32_t* __restrict__ list, int N, int m, int k, int W,
+                                                           long total) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
+    const long z = i / ((long)m * k);
+    const int ej = (int)(i - z * (long)m * k), e = ej / k;
+    const int t = I[i];
+    const uint32_t* bt = bits + ((size_t)z * N + t) * W;
+    uint32_t r = __popc(bt[e >> 5] & ((1u << (e & 31)) - 1u));
+    for (int w = 0; w < (e >> 5); ++w) r += __popc(bt[w]);
+    list[(size_t)z * m * k + off[(size_t)z * N + t] + r] = (uint32_t)ej;
   }
 }
 
@@ -782,9 +819,12 @@ void backward_plan(const Plan& p, BwdLayout* L) {
   L->dVe = take(bh * m * k * d * 4);
   L->dKs = take(bh * N * d * 4);
   L->dVs = take(bh * N * d * 4);
+  L->iw = (p.m + 31) / 32;
+  L->inb = (int)((N + kInvBlock - 1) / kInvBlock);
   L->icnt = take(bh * N * 4);
-  L->icur = take(bh * N * 4);
+  L->ibits = take(bh * N * (size_t)L->iw * 4);
   L->ioff = take(bh * N * 4);
+  L->ibsum = take(bh * (size_t)L->inb * 4);
   L->ilist = take(bh * m * k * 4);
   L->pnch = (int)((N * s + kPermChunk - 1) / kPermChunk);
   L->psort = take(bh * N * s * 4);
@@ -878,19 +918,25 @@ static hipError_t backward_launch(const Plan& p, const BwdLayout& L, const void*
                      (const float*)(bws + L.se_dqt), L.kparts, nmd, (float*)(bws + L.dqt));
   MITA_CHECK_LAUNCH();
   // inverse lists of the expert sets, then dK, dV and dQ assembled
-  const long nN = BH * N;
-  hipLaunchKernelGGL(bwd_clear_kernel, dim3((unsigned)std::min<long>(4096, (2 * nN + 255) / 256)), dim3(256), 0, st,
-                     (uint32_t*)(bws + L.icnt), (long)((L.icur - L.icnt) / 4 + nN));   // counts and cursors
+  const long nN = BH * N, nmk = BH * m * k, nbits = nN * L.iw;
+  hipLaunchKernelGGL(bwd_clear_kernel, dim3((unsigned)std::min<long>(4096, (nbits + 255) / 256)), dim3(256), 0, st,
+                     (uint32_t*)(bws + L.ibits), nbits);
   MITA_CHECK_LAUNCH();
-  hipLaunchKernelGGL(bwd_inv_count_kernel, dim3((unsigned)std::min<long>(8192, (BH * m * k + 255) / 256)), dim3(256),
-                     0, st, (const int32_t*)(fws + p.ws.I), (uint32_t*)(bws + L.icnt), p.N, p.m * p.k, BH * m * k);
+  hipLaunchKernelGGL(bwd_inv_mark_kernel, dim3((unsigned)std::min<long>(8192, (nmk + 255) / 256)), dim3(256), 0, st,
+                     (const int32_t*)(fws + p.ws.I), (uint32_t*)(bws + L.ibits), p.N, p.m, p.k, L.iw, nmk);
   MITA_CHECK_LAUNCH();
-  hipLaunchKernelGGL(bwd_inv_scan_kernel, dim3((unsigned)BH), dim3(1024), 0, st, (const uint32_t*)(bws + L.icnt),
-                     (uint32_t*)(bws + L.ioff), p.N);
+  hipLaunchKernelGGL(bwd_inv_count_kernel, dim3((unsigned)L.inb, (unsigned)BH), dim3(256), 0, st,
+                     (const uint32_t*)(bws + L.ibits), (uint32_t*)(bws + L.icnt), (uint32_t*)(bws + L.ioff),
+                     (uint32_t*)(bws + L.ibsum), p.N, L.iw, L.inb);
   MITA_CHECK_LAUNCH();
-  hipLaunchKernelGGL(bwd_inv_fill_kernel, dim3((unsigned)BH), dim3(1024), 0, st, (const int32_t*)(fws + p.ws.I),
-                     (const uint32_t*)(bws + L.ioff), (uint32_t*)(bws + L.icur), (uint32_t*)(bws + L.ilist), p.N, p.m,
-                     p.k);
+  hipLaunchKernelGGL(bwd_inv_bscan_kernel, dim3((unsigned)BH), dim3(256), 0, st, (uint32_t*)(bws + L.ibsum), L.inb);
+  MITA_CHECK_LAUNCH();
+  hipLaunchKernelGGL(bwd_inv_offset_kernel, dim3((unsigned)std::min<long>(4096, (nN + 255) / 256)), dim3(256), 0, st,
+                     (uint32_t*)(bws + L.ioff), (const uint32_t*)(bws + L.ibsum), p.N, L.inb, nN);
+  MITA_CHECK_LAUNCH();
+  hipLaunchKernelGGL(bwd_inv_fill_kernel, dim3((unsigned)std::min<long>(8192, (nmk + 255) / 256)), dim3(256), 0, st,
+                     (const int32_t*)(fws + p.ws.I), (const uint32_t*)(bws + L.ibits), (const uint32_t*)(bws + L.ioff),
+                     (uint32_t*)(bws + L.ilist), p.N, p.m, p.k, L.iw, nmk);
   MITA_CHECK_LAUNCH();
   hipLaunchKernelGGL((bwd_final_kv_kernel<D>), dim3((unsigned)((nN + 15) / 16)), dim3(256), 0, st,
                      (const float*)(bws + L.dKs), (const float*)(bws + L.dVs), (const float*)(bws + L.dKe),

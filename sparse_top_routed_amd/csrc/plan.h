@@ -98,9 +98,12 @@ struct BwdLayout {
   size_t dVe;       // f32 [BH, m, k, d]
   size_t dKs;       // f32 [BH, N, d]       shared-part dK
   size_t dVs;       // f32 [BH, N, d]
+  int iw;           // words of a token's expert bitmap: ceil(m / 32)
+  int inb;          // scan blocks of the inverse-list offsets per slice
   size_t icnt;      // u32 [BH, N]          experts holding each token
-  size_t icur;      // u32 [BH, N]          fill cursors
+  size_t ibits;     // u32 [BH, N, iw]      the experts holding each token, as bits
   size_t ioff;      // u32 [BH, N]          list offsets
+  size_t ibsum;     // u32 [BH, inb]        per scan block: token total, then its offset
   size_t ilist;     // u32 [BH, m k]        (expert, slot) entries per token, in expert order
   size_t psort;     // i32 [BH, N s]        the routing grouped by expert, (query * s + slot) ascending per bucket
   size_t pbase;     // u32 [BH, pnch, m]    per chunk: entries of each expert, then their first position

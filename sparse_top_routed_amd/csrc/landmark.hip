@@ -90,6 +90,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
   __shared__ __align__(16) struct {
     uint16_t rk[2][Sw::TILE];
     uint16_t rv[2][Sw::TILE];
+    float gmx[kLandmarkTileD][16];   // maxima of groups of 64: 16 blocks per landmark row
     float kred[4];
   } sm;
   int lt, c, z;
@@ -130,6 +131,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
   }
   float kmx = 0.f;
   const int nblk = (k1 - k0 + kKeyBlock - 1) / kKeyBlock;
+  // Maxima of groups of 64 (one per block and landmark): a store per block would
+  // put 4 bytes into a different row from each of 16 lanes, and lines would be
+  // written back partly filled. Instead each wave keeps its rows' maxima of 16
+  // blocks in LDS (rows 32 w .. 32 w + 31: no other wave touches them) and stores
+  // them as 64 contiguous bytes per row (rows and groups 16-byte aligned).
+  const bool gpack = gq == 64 && nbg % 4 == 0 && (k0 / kKeyBlock) % 16 == 0;
+  auto gflush = [&](int blk_first, int nb16) {   // blocks blk_first .. + nb16 - 1 of the wave's 32 rows
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int rl = 32 * w + 16 * h + (lane >> 2), q4 = lane & 3;   // row of the tile, its quarter
+      const int lm = lt * kLandmarkTileD + rl;
+      if (lm < m) {
+        float* dst = bmax + ((size_t)z * m + lm) * nbg + blk_first + 4 * q4;
+        const float* src = &sm.gmx[rl][4 * q4];
+        if (nb16 == 16) {
+          *(float4*)dst = *(const float4*)src;
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (4 * q4 + u < nb16) dst[u] = src[u];
+        }
+      }
+    }
+  };
   for (int j = 0; j < nblk; ++j) {
     const int kb = k0 + j * kKeyBlock;
     __builtin_amdgcn_s_waitcnt(0);
@@ -176,7 +201,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
         } else {
           float gm = fmaxf(fmaxf(gk[0], gk[1]), fmaxf(gk[2], gk[3]));
           if (gq == 64) gm = quad_max(gm);
-          if (lm_ok[qt] && (gq == 16 || g == 0)) Brow[gq == 16 ? 4 * blk + g : blk] = gm;
+          if (gpack) {   // block-uniform
+            if (g == 0) sm.gmx[32 * w + 16 * qt + r][j & 15] = gm;
+          } else if (lm_ok[qt] && (gq == 16 || g == 0)) {
+            Brow[gq == 16 ? 4 * blk + g : blk] = gm;
+          }
         }
         if (S && lm_ok[qt]) {
           float* Srow = S + ((size_t)z * m + lmc[qt]) * N;
@@ -194,6 +223,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
       __builtin_amdgcn_s_setprio(0);
     };
     step(sm.rk[(j + 1) & 1], sm.rv[(j + 1) & 1], sm.rk[j & 1], sm.rv[j & 1]);
+    if (gpack && ((j & 15) == 15 || j == nblk - 1))   // block-uniform: a group of 16 blocks, or the chunk, ends
+      gflush(k0 / kKeyBlock + (j & ~15), (j & 15) + 1);
   }
   if (lt == 0) {
     kmx = wave_max(kmx);

@@ -26,19 +26,6 @@ struct Tiles {
   static constexpr int EPC = 16 / sizeof(T);                    // elements per 16-byte chunk
 };
 
-// Copy 64 rows into a key tile: row r comes from rowptr(r) (D contiguous
-// elements, 16-byte aligned); rows r >= nvalid repeat row nvalid - 1, so their
-// scores are finite and the caller excludes them by index.
-template <typename T, int D, typename RowFn>
-__device__ __forceinline__ void stage_rows(T* dst, int stride, RowFn rowptr, int nvalid, int tid) {
-  constexpr int EPC = Tiles<T, D>::EPC, CPR = D / EPC, TOTAL = kKeyBlock * CPR;
-#pragma unroll
-  for (int c = tid; c < TOTAL; c += 256) {
-    const int r = c / CPR, cc = (c % CPR) * EPC;
-    *(uint4*)(dst + r * stride + cc) = ld16(rowptr(min(r, nvalid - 1)) + cc);
-  }
-}
-
 // A thread's share of one 64-row block, held in registers so the loads can be
 // issued early (prefetch) and written to LDS later. Rows r >= nvalid repeat row
 // nvalid - 1 (a real row, so finite): every consumer masks those keys out of
@@ -64,6 +51,17 @@ struct RowRegs {
     }
   }
 };
+
+// Copy 64 rows into a key tile: row r comes from rowptr(r) (D contiguous
+// elements, 16-byte aligned); rows r >= nvalid repeat row nvalid - 1, so their
+// scores are finite and the caller excludes them by index. Every load is issued
+// before the first store (one wait for all of them).
+template <typename T, int D, typename RowFn>
+__device__ __forceinline__ void stage_rows(T* dst, int stride, RowFn rowptr, int nvalid, int tid) {
+  RowRegs<T, D> rr;
+  rr.load(rowptr, nvalid, tid);
+  rr.store(dst, stride, tid);
+}
 
 // Slot of key quad qd (keys 4 qd .. 4 qd + 3) in row d of a bf16 V^T tile.
 // The XOR swizzle spreads both access patterns over distinct LDS banks: the
@@ -416,6 +414,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uin
 __device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t rs, uint32_t off, void* l) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)l, 16, off, 0, 0, 0);
 }
+// The same with a wave-uniform byte offset added (a scalar register).
+__device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t soff, void* l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)l, 16, off, soff, 0, 0);
+}
 template <int D>
 __device__ __forceinline__ void dma_rows_buf(uint16_t* Kt, uint16_t* Vt, __amdgpu_buffer_rsrc_t rsK,
                                              __amdgpu_buffer_rsrc_t rsV, const int (&ids)[SwzTile<D>::NI], int w,
@@ -531,23 +533,21 @@ __device__ __forceinline__ void pv_bf16_swz(const uint16_t* Vs, const f32x4 (&p)
   }
 }
 
-// ---------------------------------------------------------------- tiles read both ways
-// 64-row bf16 tiles (no padding) read as QK operands (16 consecutive rows at one
-// 16-byte chunk) and transposed (8 consecutive rows x 2 neighbouring chunks per
-// half-wave) with one swizzle, chunk c of row r at c ^ f(r): f(r) = 2 (r & 7) |
-// (r >> 3 & 1) for D = 128 (16 distinct values over 16 rows; over 8 aligned rows
-// the even parts differ) and 2 (r >> 1 & 3) | (r >> 3 & 1) for D = 64 (rows are
-// half a bank line, so r & 1 separates neighbours). Filled by direct loads from
-// NW waves (rows w 64 / NW .. of the tile per wave).
+// ---------------------------------------------------------------- tiles of NW-wave workgroups
+// 64-row bf16 tiles filled by direct loads from NW waves (rows w 64 / NW .. of
+// the tile per wave), swizzled as SwzTile: chunk c of row r at c ^ swz_k(r) in a
+// tile read as QK operands, at c ^ swz_v(r) in one read transposed. (A single
+// swizzle for both reads, 2 (r & 7) | (r >> 3 & 1), measured one LDS bank-conflict
+// cycle per MFMA on the QK reads; swz_k and swz_v measure none.)
 template <int D>
 struct UTile {
   static constexpr int CPR = D / 8, TILE = kKeyBlock * D, RPI = 512 / D;
-  __device__ static __forceinline__ int swz(int r) {
-    return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
-  }
+  __device__ static __forceinline__ int swz_k(int r) { return SwzTile<D>::swz_k(r); }
+  __device__ static __forceinline__ int swz_v(int r) { return SwzTile<D>::swz_v(r); }
 };
 
-template <int D, int NW, typename RowFn>
+// VT: the tile is read transposed (swz_v), else as QK operands (swz_k).
+template <int D, int NW, bool VT, typename RowFn>
 __device__ __forceinline__ void udma(uint16_t* tile, RowFn rowp, int w, int lane) {
   using U = UTile<D>;
   constexpr int RPW = kKeyBlock / NW, NI = RPW / U::RPI;
@@ -556,7 +556,7 @@ __device__ __forceinline__ void udma(uint16_t* tile, RowFn rowp, int w, int lane
 #pragma unroll
   for (int u = 0; u < NI; ++u) {
     const int r0 = w * RPW + u * U::RPI, row = r0 + lane / U::CPR;
-    lds_dma16(rowp(row) + 8 * (p ^ U::swz(row)), tile + r0 * D);
+    lds_dma16(rowp(row) + 8 * (p ^ (VT ? U::swz_v(row) : U::swz_k(row))), tile + r0 * D);
   }
 }
 
@@ -573,7 +573,7 @@ __device__ __forceinline__ void uqk(const uint16_t* T0, const uint16_t* T1, cons
     for (int kt = 0; kt < 4; ++kt) acc[qt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks) {
-    const int off = r * D + 8 * ((4 * ks + g) ^ UTile<D>::swz(r));   // 16 kt keeps the swizzle
+    const int off = r * D + 8 * ((4 * ks + g) ^ UTile<D>::swz_k(r));   // 16 kt keeps the swizzle
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       const uint4 a0 = *(const uint4*)(T0 + off + 16 * kt * D);
@@ -594,7 +594,7 @@ __device__ __forceinline__ void upv(const uint16_t* T, const f32x4 (&p)[QT][4], 
                                     float (&lsum)[QT], int lane) {
   const int g = lane >> 4, i = lane & 15;
   const int row = 4 * g + (i >> 2);   // + 32 h + 16 hi: bits the swizzle does not use
-  const int sw = UTile<D>::swz(row), b = (i & 3) >> 1;
+  const int sw = UTile<D>::swz_v(row), b = (i & 3) >> 1;
   const uint16_t* rb = T + row * D + 4 * (i & 1);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {

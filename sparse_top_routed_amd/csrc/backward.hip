@@ -25,13 +25,20 @@
 // the experts that hold it in expert order (an inverse list placed by per-token
 // expert bitmaps).
 //
-// Tiles (64 rows of D bf16) are read two ways: as QK operands (16 consecutive
-// rows at one 16-byte chunk) and transposed (8 consecutive rows x 2 neighbouring
-// chunks per half-wave). One swizzle serves both without bank conflicts: chunk c
-// of row r sits at chunk c ^ f(r), f(r) = 2 (r & 7) | (r >> 3 & 1) for D = 128
-// (16 distinct values over 16 rows; over 8 aligned rows the even parts differ)
-// and f(r) = 2 (r >> 1 & 3) | (r >> 3 & 1) for D = 64 (rows are half a bank
-// line, so r & 1 separates neighbours).
+// Tiles (64 rows of D bf16) are read two ways: as QK operands (16-byte reads:
+// lanes r = 0..15 of 16 consecutive rows, two 16-byte chunks per row per half-wave)
+// and transposed (8-byte reads: 8 consecutive rows x 2 neighbouring chunks per
+// half-wave). Chunk c of row r sits at chunk c ^ f(r), f(r) = 2 h(r), where h
+// is chosen so that neither read meets a bank conflict when a half-wave's 16-byte
+// reads are served over 128 four-byte banks (512 bytes) and its 8-byte reads over
+// 64 or 128 banks (a single swizzle that is conflict-free over 64 banks,
+// 2 (r & 7) | (r >> 3 & 1), measured one conflict cycle per MFMA on the QK reads):
+//   D = 128 (a row is 64 banks): h(r) = (r & 7) ^ (r >> 3 & 1), a permutation of
+//     0..7 over the even and over the odd rows of 16 (QK) and over 8 aligned rows
+//     (transposed);
+//   D = 64 (a row is 32 banks): h(r) = ((r >> 2) ^ (r & 2)) & 3, distinct over the
+//     four rows r & 3 = c of 16 (QK) and over the four rows of either parity of 8
+//     aligned rows (transposed).
 #include "attn_core.h"
 
 namespace mita {
@@ -40,7 +47,7 @@ template <int D>
 struct BT {
   static constexpr int CPR = D / 8, TILE = kKeyBlock * D, RPI = 512 / D;
   __device__ static __forceinline__ int swz(int r) {
-    return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+    return D == 128 ? 2 * ((r & 7) ^ ((r >> 3) & 1)) : 2 * (((r >> 2) ^ (r & 2)) & 3);
   }
 };
 

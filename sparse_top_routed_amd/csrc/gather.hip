@@ -975,8 +975,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const uint16_t* hz = qtop + (size_t)z * 2 * m * D;
   const uint16_t* vz = vt16 + (size_t)z * m * D;
   auto stage = [&](int lb, uint16_t* tk, uint16_t* tv) __attribute__((always_inline)) {
-    udma<D, NW>(tk, [&](int row) __attribute__((always_inline)) { return hz + (size_t)min(lb + row, m - 1) * D; }, w, lane);
-    udma<D, NW>(tv, [&](int row) __attribute__((always_inline)) { return vz + (size_t)min(lb + row, m - 1) * D; }, w, lane);
+    udma<D, NW, false>(tk, [&](int row) __attribute__((always_inline)) { return hz + (size_t)min(lb + row, m - 1) * D; }, w, lane);
+    udma<D, NW, true>(tv, [&](int row) __attribute__((always_inline)) { return vz + (size_t)min(lb + row, m - 1) * D; }, w, lane);
   };
   stage(0, sm.kk[0], sm.vv[0]);
   // seed: per query, M = the largest partial reference; o, l = the partials rescaled to it

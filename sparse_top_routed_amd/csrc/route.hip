@@ -355,8 +355,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
                                                           double gamma, int qtiles) {
   using TL = Tiles<T, D>;
   constexpr bool BF = TL::BF;
-  __shared__ __align__(16) T Ks0[TL::KTILE];
-  __shared__ __align__(16) T Ks1[BF ? TL::KTILE : 8];
+  __shared__ __align__(16) T Ks0[BF ? 8 : TL::KTILE];   // fp32 key tile (bf16 tiles: below)
   __shared__ float s_red[4];
   const int z = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
   const int t0 = blockIdx.x * TPW;
@@ -365,7 +364,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
   const double* qt64z = qt64 + (size_t)z * m * D;
 
   // query fragments of the TPW tiles (tiles past the end repeat the last row)
-  uint4 qb[TPW][1][D / 32];
+  uint4 qb[TPW][D / 32];
   float qf[TPW][D / 4];
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
@@ -373,7 +372,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
     const T* qrow = Q + ((size_t)z * N + q) * D;
     if constexpr (BF) {
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) qb[tt][0][ks] = ld16(qrow + 32 * ks + 8 * g);
+      for (int ks = 0; ks < D / 32; ++ks) qb[tt][ks] = ld16(qrow + 32 * ks + 8 * g);
     } else {
 #pragma unroll
       for (int ks = 0; ks < D / 4; ++ks) qf[tt][ks] = qrow[4 * ks + g];
@@ -390,36 +389,70 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
   for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
     for (int j = 0; j < TM; ++j) tk[tt][j] = 0u;
-  for (int lb0 = 0; lb0 < m; lb0 += kKeyBlock) {
-    __syncthreads();   // readers of the previous block are done
-    const int nvalid = min(kKeyBlock, m - lb0);
-    stage_rows<T, D>(Ks0, TL::KSTR, [&](int rr) { return plane0 + (size_t)(lb0 + rr) * D; }, nvalid, tid);
-    if constexpr (BF)
-      stage_rows<T, D>(Ks1, TL::KSTR, [&](int rr) { return plane1 + (size_t)(lb0 + rr) * D; }, nvalid, tid);
-    __syncthreads();
-    // scores of all TPW tiles at once: each landmark fragment read from LDS
-    // serves every tile right away (nothing to keep live across tiles)
-    f32x4 acct[TPW][4];
+  auto take = [&](const f32x4 (&acct)[TPW][4], int lb0) {
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) acct[tt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (BF) {
-      constexpr int KSTR = TL::KSTR;
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks)
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const int off = (16 * kt + r) * KSTR + 32 * ks + 8 * g;
-          const uint4 a0 = *(const uint4*)((const uint16_t*)Ks0 + off);
-          const uint4 a1 = *(const uint4*)((const uint16_t*)Ks1 + off);
-#pragma unroll
-          for (int tt = 0; tt < TPW; ++tt) {
-            acct[tt][kt] = mma_bf16(a0, qb[tt][0][ks], acct[tt][kt]);
-            acct[tt][kt] = mma_bf16(a1, qb[tt][0][ks], acct[tt][kt]);
-          }
+        for (int j = 0; j < 4; ++j) {
+          const int li = lb0 + 16 * kt + 4 * g + j;
+          const uint32_t key = rk.make(acct[tt][kt][j], li);
+          // past m: key 0, which never enters the list; an arithmetic mask (a
+          // conditional here compiled to a branch per score), none when m is a
+          // multiple of the block
+          top_insert<TM>(tk[tt], MFULL ? key : key & (uint32_t)((li - m) >> 31));
         }
-    } else {
+  };
+  if constexpr (BF) {
+    // Landmark blocks (hi and lo planes of Q~) by direct loads into swizzled
+    // tiles, one buffer: once every wave has read a block, the next block's loads
+    // are issued and fly while the top lists take this block's scores. The loads
+    // go through one buffer resource over both planes: a lane's offset within a
+    // block is fixed, the block's offset a scalar. Rows past m read the lo plane
+    // or, past its end, zeros: finite scores, masked by index.
+    __shared__ __align__(16) uint16_t Th[UTile<D>::TILE];
+    __shared__ __align__(16) uint16_t Tl[UTile<D>::TILE];
+    using U = UTile<D>;
+    constexpr int NI = kKeyBlock / 4 / U::RPI;   // load instructions per wave per tile
+    const __amdgpu_buffer_rsrc_t rs = raw_rsrc(plane0, 2u * (uint32_t)m * D * 2);
+    uint32_t voff[NI];
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      const int row = 16 * w + u * U::RPI + lane / U::CPR;
+      voff[u] = (uint32_t)row * (D * 2) + 16 * ((lane % U::CPR) ^ U::swz_k(row));
+    }
+    const int ws = __builtin_amdgcn_readfirstlane(w);   // LDS bases in scalar registers
+    auto stage = [&](int lb0) {
+      const uint32_t sh = (uint32_t)lb0 * (D * 2), sl = sh + (uint32_t)m * (D * 2);
+#pragma unroll
+      for (int u = 0; u < NI; ++u) lds_dma16_buf(rs, voff[u], sh, Th + (16 * ws + u * U::RPI) * D);
+#pragma unroll
+      for (int u = 0; u < NI; ++u) lds_dma16_buf(rs, voff[u], sl, Tl + (16 * ws + u * U::RPI) * D);
+    };
+    stage(0);
+    for (int lb0 = 0; lb0 < m; lb0 += kKeyBlock) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();   // the block is in LDS (every wave's share)
+      // per score the MFMA sequence of the padded-tile form: k-slices in order,
+      // hi then lo plane
+      f32x4 acct[TPW][4];
+      uqk<D, TPW, 2>(Th, Tl, qb, acct, lane);
+      __syncthreads();   // every wave has read the block
+      if (lb0 + kKeyBlock < m) stage(lb0 + kKeyBlock);   // block-uniform
+      take(acct, lb0);
+    }
+  } else {
+    for (int lb0 = 0; lb0 < m; lb0 += kKeyBlock) {
+      __syncthreads();   // readers of the previous block are done
+      const int nvalid = min(kKeyBlock, m - lb0);
+      stage_rows<T, D>(Ks0, TL::KSTR, [&](int rr) { return plane0 + (size_t)(lb0 + rr) * D; }, nvalid, tid);
+      __syncthreads();
+      f32x4 acct[TPW][4];
+#pragma unroll
+      for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) acct[tt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
       constexpr int KSTR = TL::KSTR;
 #pragma unroll
       for (int ks = 0; ks < D / 4; ++ks)
@@ -429,23 +462,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
 #pragma unroll
           for (int tt = 0; tt < TPW; ++tt) acct[tt][kt] = mma_f32(a, qf[tt][ks], acct[tt][kt]);
         }
-    }
-#pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-      const f32x4 (&acc)[4] = acct[tt];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int li = lb0 + 16 * kt + 4 * g + j;
-          const uint32_t key = rk.make(acc[kt][j], li);
-          // past m: key 0, which never enters the list; an arithmetic mask (a
-          // conditional here compiled to a branch per score), none when m is a
-          // multiple of the block
-          top_insert<TM>(tk[tt], MFULL ? key : key & (uint32_t)((li - m) >> 31));
-        }
+      take(acct, lb0);
     }
   }
+  __syncthreads();   // s_red (written before the loop) for every wave
   const double qtmax = (double)fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
 
 #pragma unroll
@@ -465,7 +485,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
     if constexpr (BF) {
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) {
-        const uint16_t* h = (const uint16_t*)&qb[tt][0][ks];
+        const uint16_t* h = (const uint16_t*)&qb[tt][ks];
 #pragma unroll
         for (int e = 0; e < 8; ++e) { const float x = bf16_to_f32(h[e]); sq = fmaf(x, x, sq); }
       }
@@ -522,7 +542,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
         if constexpr (BF) {
 #pragma unroll
           for (int ks = 0; ks < D / 32; ++ks) {
-            const uint16_t* h = (const uint16_t*)&qb[tt][0][ks];
+            const uint16_t* h = (const uint16_t*)&qb[tt][ks];
 #pragma unroll
             for (int e = 0; e < 8; ++e) part = fma(qr[32 * ks + 8 * g + e], (double)bf16_to_f32(h[e]), part);
           }

@@ -37,18 +37,39 @@ __device__ __forceinline__ void top_insert(uint32_t (&t)[TM], uint32_t x) {
   t[0] = max(t[0], x);
 }
 
-// Landmark score as a sortable key that carries its landmark id: the order key
-// of the score with its low ib bits replaced by imask - id (imask = 2^ib - 1 >=
-// m - 1), so keys are distinct, a higher score wins and, among scores equal
-// after the truncation, the lower id wins. Real keys are never 0.
+// Landmark score as a float key that carries its landmark id: the score with its
+// low ib mantissa bits replaced by imask - id (imask = 2^ib - 1 >= m - 1). Keys of
+// one query are distinct floats (finite: the exponent is untouched; scores near
+// zero become denormals, which the kernels keep), ordered by value with three-input
+// medians, one instruction per list entry; the empty entry is -inf. A key bounds its
+// score from both sides: the score has the key's bits above the low ib, so it lies
+// between the key with those bits cleared and with them set.
 struct RouteKey {
   uint32_t imask;
-  __device__ __forceinline__ uint32_t make(float v, int li) const { return (f32_key(v) & ~imask) | (imask - li); }
-  __device__ __forceinline__ int id(uint32_t k) const { return (int)(imask - (k & imask)); }
-  // bounds of the score a key stands for
-  __device__ __forceinline__ double lo(uint32_t k) const { return (double)key_f32(k & ~imask); }
-  __device__ __forceinline__ double hi(uint32_t k) const { return (double)key_f32(k | imask); }
+  // idb: the id bits imask - id; nmask: ~imask
+  __device__ __forceinline__ float make(float v, uint32_t idb, uint32_t nmask) const {
+    return __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, v) & nmask) | idb);
+  }
+  __device__ __forceinline__ int id(float k) const { return (int)(imask - (__builtin_bit_cast(uint32_t, k) & imask)); }
+  __device__ __forceinline__ double lo(float k) const {
+    const uint32_t u = __builtin_bit_cast(uint32_t, k);
+    return (double)fminf(__builtin_bit_cast(float, u & ~imask), __builtin_bit_cast(float, u | imask));
+  }
+  __device__ __forceinline__ double hi(float k) const {
+    const uint32_t u = __builtin_bit_cast(uint32_t, k);
+    return (double)fmaxf(__builtin_bit_cast(float, u & ~imask), __builtin_bit_cast(float, u | imask));
+  }
 };
+// Insert a key into a descending list of keys; the new maximum is the median of
+// the old one, x and pinf = +inf. pinf comes from a run-time value: with a literal
+// +inf the compiler turns the median into a maximum, which then quiets both
+// operands first (three instructions instead of one).
+template <int TM>
+__device__ __forceinline__ void key_insert(float (&t)[TM], float x, float pinf) {
+#pragma unroll
+  for (int j = TM - 1; j >= 1; --j) t[j] = __builtin_amdgcn_fmed3f(t[j - 1], t[j], x);
+  t[0] = __builtin_amdgcn_fmed3f(t[0], x, pinf);
+}
 
 template <typename T>
 __device__ __forceinline__ double load_f64(const T* p, int c) {
@@ -384,12 +405,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
   if (lane == 0) s_red[w] = qtm;
 
   const RouteKey rk{(2u << (31 - __builtin_clz((uint32_t)(m - 1)))) - 1u};   // m > 64: imask >= m - 1
-  uint32_t tk[TPW][TM];   // the TM largest keys of the lane, then of the query
+  const float pinf = __builtin_bit_cast(float, 0x7F800000u | ((uint32_t)m >> 31));   // +inf (m > 0)
+  float tk[TPW][TM];   // the TM largest keys of the lane, then of the query
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
-    for (int j = 0; j < TM; ++j) tk[tt][j] = 0u;
+    for (int j = 0; j < TM; ++j) tk[tt][j] = -INFINITY;
+  // In the block loop a key's id bits leave out the lane's 4 g: imask - (lb0 + 16 kt
+  // + j) = (imask - lb0) ^ (16 kt + j) (the low 6 bits of imask - lb0 are ones) is
+  // the same for every lane, a scalar, so a key costs one instruction. A lane's
+  // ids are still distinct; 4 g is put in after the loop (bits 2-3 of every such
+  // id are ones, so XOR 4 g subtracts it and keeps the lane's order).
+  // ~imask in a vector register (the result of a lane exchange counts as
+  // per-lane), so that with the scalar id bits a key is one v_and_or_b32 (a vector
+  // instruction reads at most one scalar register)
+  const uint32_t nmask = (uint32_t)__shfl((int)~rk.imask, lane, WAVE);
   auto take = [&](const f32x4 (&acct)[TPW][4], int lb0) {
+    const uint32_t cb = rk.imask - (uint32_t)lb0;
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
@@ -397,11 +429,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int li = lb0 + 16 * kt + 4 * g + j;
-          const uint32_t key = rk.make(acct[tt][kt][j], li);
-          // past m: key 0, which never enters the list; an arithmetic mask (a
-          // conditional here compiled to a branch per score), none when m is a
-          // multiple of the block
-          top_insert<TM>(tk[tt], MFULL ? key : key & (uint32_t)((li - m) >> 31));
+          const float key = rk.make(acct[tt][kt][j], cb ^ (uint32_t)(16 * kt + j), nmask);
+          // past m: -inf, which never enters the list (a bit select: a conditional
+          // here compiled to a branch per score); none when m is a multiple of the block
+          const uint32_t keep = (uint32_t)((li - m) >> 31);
+          key_insert<TM>(tk[tt],
+                         MFULL ? key
+                               : __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, key) & keep) | (0xFF800000u & ~keep)),
+                         pinf);
         }
   };
   if constexpr (BF) {
@@ -474,12 +509,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
     const bool q_ok = (t0 + tt) < qtiles && q < N;
     const T* qrow = Q + ((size_t)z * N + min(q, N - 1)) * D;
 #pragma unroll
+    for (int j = 0; j < TM; ++j)   // the lane's 4 g into the id bits (-inf: an empty entry)
+      if (tk[tt][j] != -INFINITY) tk[tt][j] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, tk[tt][j]) ^ (4u * g));
+#pragma unroll
     for (int sh = 16; sh <= 32; sh <<= 1) {
-      uint32_t ok[TM];
+      float ok[TM];
 #pragma unroll
       for (int j = 0; j < TM; ++j) ok[j] = __shfl_xor(tk[tt][j], sh, WAVE);
 #pragma unroll
-      for (int j = 0; j < TM; ++j) top_insert<TM>(tk[tt], ok[j]);
+      for (int j = 0; j < TM; ++j) key_insert<TM>(tk[tt], ok[j], pinf);
     }
     float sq = 0.f;
     if constexpr (BF) {
@@ -497,7 +535,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
     const double Eq = gamma * (double)qn * qtmax;
     // s-th and (s+1)-th keys without dynamic register indexing; each key bounds
     // its score from both sides, so the s-th score lies in [lo(k_s), hi(k_s)]
-    uint32_t k_s = 0u, k_s1 = 0u;
+    float k_s = -INFINITY, k_s1 = -INFINITY;
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
       if (j == s - 1) k_s = tk[tt][j];
@@ -536,7 +574,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
 #pragma unroll
       for (int j = 0; j < TM; ++j) {
         tid_[j] = rk.id(tk[tt][j]);
-        band[j] = refine && j >= c_in && tk[tt][j] != 0u && rk.hi(tk[tt][j]) >= lo;
+        band[j] = refine && j >= c_in && tk[tt][j] != -INFINITY && rk.hi(tk[tt][j]) >= lo;
         const double* qr = qt64z + (size_t)(band[j] ? tid_[j] : 0) * D;
         double part = 0.0;
         if constexpr (BF) {

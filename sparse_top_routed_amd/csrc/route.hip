@@ -555,7 +555,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
     int c_in = 0;
 #pragma unroll
     for (int j = 0; j < TM; ++j) c_in += (j < s && rk.lo(tk[tt][j]) > hi) ? 1 : 0;
-    const int need = s - c_in;
     if (unc && g == 0) {
 #pragma unroll
       for (int j = 0; j < TM; ++j)
@@ -567,39 +566,84 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void r
       const uint32_t pos = atomicAdd(&counters[0], 1u);
       rflag[pos] = (uint32_t)(z * N + q);
     }
-    if (__any(refine)) {
-      double s64[TM];
-      bool band[TM];
-      int tid_[TM];
+    // Band re-scoring in fp64, compacted: the wave takes its queries to refine two
+    // at a time (lanes 32 slot .. + 31 for one query, 4 lanes per list entry, each
+    // a quarter of the row), so a tile with one uncertain query pays for that one.
+    uint64_t rq = __ballot(refine && g == 0);   // bit r: query r of the tile (lane r is its g = 0 lane)
+    while (rq) {   // wave-uniform
+      const int s0 = __builtin_ctzll(rq);
+      rq &= rq - 1;
+      const int s1 = rq ? __builtin_ctzll(rq) : -1;
+      if (rq) rq &= rq - 1;
+      const int slot = lane >> 5, j = (lane & 31) >> 2, part = lane & 3;
+      const int src = slot ? s1 : s0;
+      const int srcl = max(src, 0);
+      const bool act = src >= 0 && j < TM;
+      // the query's list, band and count above it, from its lane
+      float kk[TM];
 #pragma unroll
-      for (int j = 0; j < TM; ++j) {
-        tid_[j] = rk.id(tk[tt][j]);
-        band[j] = refine && j >= c_in && tk[tt][j] != -INFINITY && rk.hi(tk[tt][j]) >= lo;
-        const double* qr = qt64z + (size_t)(band[j] ? tid_[j] : 0) * D;
-        double part = 0.0;
+      for (int f = 0; f < TM; ++f) kk[f] = __shfl(tk[tt][f], srcl, WAVE);
+      const double blo = __shfl(lo, srcl, WAVE);
+      const int cin = __shfl(c_in, srcl, WAVE);
+      float myk = kk[0];
+#pragma unroll
+      for (int f = 1; f < TM; ++f) myk = f == j ? kk[f] : myk;
+      const int myid = rk.id(myk);
+      const int qs = (t0 + tt) * kQueryTile + 16 * w + srcl;
+      double acc = 0.0;
+      if (act) {
+        constexpr int QD = D / 4;   // elements per lane
+        const double2* qr = (const double2*)(qt64z + (size_t)myid * D + QD * part);
+        const T* qrow = Q + ((size_t)z * N + qs) * D + QD * part;
         if constexpr (BF) {
 #pragma unroll
-          for (int ks = 0; ks < D / 32; ++ks) {
-            const uint16_t* h = (const uint16_t*)&qb[tt][ks];
+          for (int c = 0; c < QD / 8; ++c) {
+            const uint4 u = ((const uint4*)qrow)[c];
+            const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) part = fma(qr[32 * ks + 8 * g + e], (double)bf16_to_f32(h[e]), part);
+            for (int e = 0; e < 4; ++e) {
+              const double2 t = qr[4 * c + e];
+              acc = fma(t.x, (double)__builtin_bit_cast(float, uw[e] << 16), acc);
+              acc = fma(t.y, (double)__builtin_bit_cast(float, uw[e] & 0xFFFF0000u), acc);
+            }
           }
         } else {
 #pragma unroll
-          for (int ks = 0; ks < D / 4; ++ks) part = fma(qr[4 * ks + g], (double)qf[tt][ks], part);
+          for (int c = 0; c < QD / 4; ++c) {
+            const float4 x = ((const float4*)qrow)[c];
+            const double2 t0v = qr[2 * c], t1v = qr[2 * c + 1];
+            acc = fma(t0v.x, (double)x.x, acc);
+            acc = fma(t0v.y, (double)x.y, acc);
+            acc = fma(t1v.x, (double)x.z, acc);
+            acc = fma(t1v.y, (double)x.w, acc);
+          }
         }
-        part += __shfl_xor(part, 16, WAVE);
-        s64[j] = part + __shfl_xor(part, 32, WAVE);
       }
-      if (refine && g == 0) {
+      acc += __shfl_xor(acc, 1, WAVE);
+      acc += __shfl_xor(acc, 2, WAVE);
+      double sv[TM];
 #pragma unroll
-        for (int j = 0; j < TM; ++j) {
-          if (!band[j]) continue;
-          int rank = 0;
+      for (int f = 0; f < TM; ++f) sv[f] = __shfl(acc, 32 * slot + 4 * f, WAVE);
+      if (act && part == 0) {
+        bool band[TM];
+        double mysv = sv[0];
+        bool myband = false;
 #pragma unroll
-          for (int f = 0; f < TM; ++f)
-            rank += (band[f] && ((s64[f] > s64[j]) | ((s64[f] == s64[j]) & (tid_[f] < tid_[j])))) ? 1 : 0;
-          if (rank < need) Eq_out[c_in + rank] = tid_[j];
+        for (int f = 0; f < TM; ++f) {
+          band[f] = f >= cin && kk[f] != -INFINITY && rk.hi(kk[f]) >= blo;
+          if (f == j) {
+            mysv = sv[f];
+            myband = band[f];
+          }
+        }
+        if (myband) {
+          int rank = 0;   // by (fp64 score desc, id asc) among the band
+#pragma unroll
+          for (int f = 0; f < TM; ++f) {
+            const int idf = rk.id(kk[f]);
+            rank += (band[f] && ((sv[f] > mysv) | ((sv[f] == mysv) & (idf < myid)))) ? 1 : 0;
+          }
+          if (rank < s - cin) E[((size_t)z * N + qs) * s + cin + rank] = myid;
         }
       }
     }

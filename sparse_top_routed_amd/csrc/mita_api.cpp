@@ -379,20 +379,27 @@ mita_status mita_forward(const void* Q, const void* K, const void* V, int m, int
   // at the head of the side stream would wait for a CU slot behind the shared-
   // expert kernel's workgroups, and the routing with it
   if ((st = hip_status(launch_clear(P, ws, hs), "clear")) != MITA_OK) return st;
-  // fork: routing (+ bucketing) on the side stream, steps 2-3 on the caller's
-  if ((st = hip_status(hipEventRecord(sd->fork, hs), "fork")) != MITA_OK) return st;
-  if ((st = hip_status(hipStreamWaitEvent(rs, sd->fork, 0), "fork wait")) != MITA_OK) return st;
-  // From here the side stream depends on the caller's: every path joins it back
-  // (also after a failed launch, so a graph being captured is never left forked).
-  // The first failure is the one reported.
   FirstError fe;
-  fe.add(launch_route(P, Q, ws, rs), "route");
-  if (fe.ok()) fe.add(launch_bucket(P, ws, rs), "bucket");
-  const bool joined = fe.add(hipEventRecord(sd->join, rs), "join");
-  if (fe.ok()) fe.add(launch_landmark(P, K, V, ws, nullptr, hs), "landmark");
-  if (fe.ok()) fe.add(launch_topk(P, K, ws, hs), "topk");
-  // join: the output step needs both branches
-  if (joined) fe.add(hipStreamWaitEvent(hs, sd->join, 0), "join wait");
+  if (route_alongside(P)) {
+    // fork: routing (+ bucketing) on the side stream, steps 2-3 on the caller's
+    if ((st = hip_status(hipEventRecord(sd->fork, hs), "fork")) != MITA_OK) return st;
+    if ((st = hip_status(hipStreamWaitEvent(rs, sd->fork, 0), "fork wait")) != MITA_OK) return st;
+    // From here the side stream depends on the caller's: every path joins it back
+    // (also after a failed launch, so a graph being captured is never left forked).
+    // The first failure is the one reported.
+    fe.add(launch_route(P, Q, ws, rs), "route");
+    if (fe.ok()) fe.add(launch_bucket(P, ws, rs), "bucket");
+    const bool joined = fe.add(hipEventRecord(sd->join, rs), "join");
+    if (fe.ok()) fe.add(launch_landmark(P, K, V, ws, nullptr, hs), "landmark");
+    if (fe.ok()) fe.add(launch_topk(P, K, ws, hs), "topk");
+    // join: the output step needs both branches
+    if (joined) fe.add(hipStreamWaitEvent(hs, sd->join, 0), "join wait");
+  } else {   // a routing grid of several rounds: in line, before steps 2-3
+    fe.add(launch_route(P, Q, ws, hs), "route");
+    if (fe.ok()) fe.add(launch_bucket(P, ws, hs), "bucket");
+    if (fe.ok()) fe.add(launch_landmark(P, K, V, ws, nullptr, hs), "landmark");
+    if (fe.ok()) fe.add(launch_topk(P, K, ws, hs), "topk");
+  }
   if (fe.ok()) fe.add(launch_gather(P, Q, K, V, out, ws, hs), "gather");
   if (fe.ok()) fe.add(launch_combine(P, Q, out, ws, hs), "combine");
   return fe.finish();

@@ -162,6 +162,7 @@ hipError_t launch_merge_thresh(const Plan& p, char* ws, hipStream_t st);
 hipError_t launch_dense(int dtype, int d, int BH, int N, const void* Q, const void* K, const void* V, void* out,
                         hipStream_t st);
 hipError_t launch_route(const Plan& p, const void* Q, char* ws, hipStream_t st);
+bool route_alongside(const Plan& p);   // routing on a second stream beside steps 2-3
 hipError_t launch_bucket(const Plan& p, char* ws, hipStream_t st);
 // Step 5, routed part: each expert's bucket of queries over its gathered keys. Writes
 // the output itself when the landmark part is fused (s = 1, m <= 64), else partials.

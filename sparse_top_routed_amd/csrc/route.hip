@@ -77,41 +77,48 @@ __device__ __forceinline__ double load_f64(const T* p, int c) {
   else return (double)p[c];
 }
 
-// Exact top-s of one query by one wave: the query row is staged in LDS (qs, D
-// doubles), every landmark is scored in fp64 against the fp64 Q~ rows (r64, m
-// doubles of LDS; BATCH 16-byte loads in flight per lane), then for s <= 16 the
-// winners are taken one at a time by a wave arg-max over (score desc, id asc);
-// for larger s the s-th largest order key is found by a bit-serial search and
-// the entries at or above it are ranked.
-template <typename T, int D, int BATCH>
+// Exact top-s of one query by one wave: every landmark is scored in fp64 against
+// the fp64 Q~ rows into r64 (m doubles of LDS), then for s <= 16 the winners are
+// taken one at a time by a wave arg-max over (score desc, id asc); for larger s
+// the s-th largest order key is found by a bit-serial search and the entries at
+// or above it are ranked. Scoring: 8 lanes per landmark row, lane k of the eight
+// taking 16 bytes of every 128-byte piece of it, so a load instruction reads 8
+// rows of whole cache lines (a row per lane would touch 64 lines per instruction
+// and leave the wave waiting on the address unit); the lane's query elements stay
+// in registers, and the eight partial sums meet in three lane exchanges. RPP
+// groups of 8 rows are in flight per pass.
+template <typename T, int D, int RPP>
 __device__ __forceinline__ void exact_route_wave(const T* qrow, const double* qt64z, int m, int s,
-                                                 int32_t* Eo, double* r64, double* qs, int lane) {
-  // the query row and the first batch of this lane's landmark row are fetched together
-  double qv[(D + 63) / 64];
+                                                 int32_t* Eo, double* r64, int lane) {
+  constexpr int NC = D / 16;   // 128-byte pieces per row
+  const int rg = lane >> 3, k = lane & 7;
+  double qv[2 * NC];
 #pragma unroll
-  for (int j = 0; j < (D + 63) / 64; ++j) qv[j] = load_f64<T>(qrow, min(lane + 64 * j, D - 1));
-  for (int i0 = 0; i0 < m; i0 += 64) {
-    const int i = min(i0 + lane, m - 1);
-    const double2* qr = (const double2*)(qt64z + (size_t)i * D);
-    double a0 = 0.0, a1 = 0.0;
+  for (int c = 0; c < NC; ++c) {
+    qv[2 * c] = load_f64<T>(qrow, 16 * c + 2 * k);
+    qv[2 * c + 1] = load_f64<T>(qrow, 16 * c + 2 * k + 1);
+  }
+  for (int i0 = 0; i0 < m; i0 += 8 * RPP) {
+    double2 x[RPP][NC];
 #pragma unroll
-    for (int c0 = 0; c0 < D / 2; c0 += BATCH) {
-      double2 x[BATCH];
+    for (int h = 0; h < RPP; ++h) {
+      const double2* qr = (const double2*)(qt64z + (size_t)min(i0 + 8 * h + rg, m - 1) * D);
 #pragma unroll
-      for (int c = 0; c < BATCH; ++c) x[c] = qr[c0 + c];
-      if (i0 == 0 && c0 == 0) {   // uniform: stage the query row once its loads are in flight
-#pragma unroll
-        for (int j = 0; j < (D + 63) / 64; ++j)
-          if (lane + 64 * j < D) qs[lane + 64 * j] = qv[j];
-        wave_sync();
-      }
-#pragma unroll
-      for (int c = 0; c < BATCH; ++c) {
-        a0 = fma(x[c].x, qs[2 * (c0 + c)], a0);
-        a1 = fma(x[c].y, qs[2 * (c0 + c) + 1], a1);
-      }
+      for (int c = 0; c < NC; ++c) x[h][c] = qr[8 * c + k];
     }
-    if (i0 + lane < m) r64[i0 + lane] = a0 + a1;
+#pragma unroll
+    for (int h = 0; h < RPP; ++h) {
+      double a = 0.0;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        a = fma(x[h][c].x, qv[2 * c], a);
+        a = fma(x[h][c].y, qv[2 * c + 1], a);
+      }
+      a += __shfl_xor(a, 1, WAVE);
+      a += __shfl_xor(a, 2, WAVE);
+      a += __shfl_xor(a, 4, WAVE);
+      if (k == 0 && i0 + 8 * h + rg < m) r64[i0 + 8 * h + rg] = a;
+    }
   }
   wave_sync();
   if (s <= 16) {
@@ -657,7 +664,7 @@ __global__ __launch_bounds__(256) void route_exact_kernel(const T* __restrict__ 
                                                           int32_t* __restrict__ E, const uint32_t* __restrict__ counters,
                                                           const uint32_t* __restrict__ list, int N, int m, int s,
                                                           int total) {
-  extern __shared__ double x64[];   // per wave: [m] scores, then the query row [D]
+  extern __shared__ double x64[];   // per wave: [m] scores (and D doubles not used)
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   double* r64 = x64 + (size_t)w * (m + D);
   const int count = list ? (int)counters[0] : total;
@@ -665,8 +672,7 @@ __global__ __launch_bounds__(256) void route_exact_kernel(const T* __restrict__ 
   for (int t = blockIdx.x * nw + w; t < count; t += gridDim.x * nw) {
     const int qid = list ? (int)list[t] : t;
     const int z = qid / N;
-    exact_route_wave<T, D, 32>(Q + (size_t)qid * D, qt64 + (size_t)z * m * D, m, s, E + (size_t)qid * s, r64,
-                               r64 + m, lane);
+    exact_route_wave<T, D, 2>(Q + (size_t)qid * D, qt64 + (size_t)z * m * D, m, s, E + (size_t)qid * s, r64, lane);
   }
 }
 
@@ -732,6 +738,22 @@ static hipError_t route_launch(const Plan& p, const void* Q, char* ws, hipStream
                      (const uint32_t*)(ws + p.ws.counters), fast ? (const uint32_t*)(ws + p.ws.rflag) : nullptr, p.N,
                      p.m, p.s, total);
   return hipGetLastError();
+}
+
+// Routing beside steps 2-3 (on a second stream) pays while its grid is short, at
+// most two rounds of resident workgroups (taken as four per CU, the fast router's
+// occupancy), or for d = 64, whose shared-expert and top-k kernels leave more of
+// the CUs' issue slots idle. A longer d = 128 routing grid only competes with those
+// kernels for the same CUs, and the forward runs better with routing first on the
+// caller's stream (measured: very long 6.75 -> 6.59 ms, long 2.99 -> 2.89 ms in
+// line; seg-like, d = 64 and 6144 routing workgroups: 1.43 ms beside, 1.49 ms in
+// line).
+bool route_alongside(const Plan& p) {
+  if (p.m <= kKeyBlock && p.s <= kRouteFastMaxS) return true;   // one round by construction
+  if (p.d == 64) return true;
+  const int64_t wgs = p.s <= kRouteFastMaxS ? (int64_t)((p.qtiles + 1) / 2) * p.BH   // two query tiles per workgroup
+                                            : ((int64_t)p.BH * p.N + 3) / 4;        // exact kernel: four queries
+  return wgs <= 2LL * 4 * device_cu_count();
 }
 
 hipError_t launch_route(const Plan& p, const void* Q, char* ws, hipStream_t st) {

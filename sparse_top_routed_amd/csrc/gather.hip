@@ -542,24 +542,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     __syncthreads();
     if (nt == 0) continue;
     const int nblk = (int)nt * B;
-    auto blk = [&](int j, int& zb, const int32_t*& Ieb, int& kbb) {
-      j = min(j, nblk - 1);
-      const int ti = j / B;
-      zb = kScalar ? __builtin_amdgcn_readfirstlane(sm.tz[ti]) : sm.tz[ti];
-      const int ex = kScalar ? __builtin_amdgcn_readfirstlane(sm.tile[ti].x) : sm.tile[ti].x;
-      Ieb = I + ((size_t)zb * m + ex) * k;
-      kbb = (j % B) * kKeyBlock;
+    // Cursor of the token ids being fetched (two blocks ahead of the block that
+    // computes): tile it2, block bi2 of it, and that tile's slice and expert list,
+    // read from the tile table only when the cursor enters a tile (past the last
+    // tile it stays on the last one: those ids are fetched, never staged).
+    int it2 = 0, bi2 = 0, zI = 0;
+    const int32_t* IeI = I;
+    auto enter = [&](int t) {
+      t = min(t, (int)nt - 1);
+      zI = kScalar ? __builtin_amdgcn_readfirstlane(sm.tz[t]) : sm.tz[t];
+      const int ex = kScalar ? __builtin_amdgcn_readfirstlane(sm.tile[t].x) : sm.tile[t].x;
+      IeI = I + ((size_t)zI * m + ex) * k;
     };
+    enter(0);
     // the slice's K and V as raw buffers: each staged row is a 32-bit offset
     auto rsK = [&](int zb) { return raw_rsrc(K + (size_t)zb * N * D, (uint32_t)N * D * 2); };
     auto rsV = [&](int zb) { return raw_rsrc(V + (size_t)zb * N * D, (uint32_t)N * D * 2); };
-    // token ids of this lane's rows of block j (rows past the expert's end repeat its last token)
-    auto ids = [&](int j, int (&id)[S::NI], int& zb) {
-      const int32_t* Ieb;
-      int kbb;
-      blk(j, zb, Ieb, kbb);
+    // token ids of this lane's rows of the cursor's block (rows past the expert's
+    // end repeat its last token), then the cursor moves one block on
+    auto ids = [&](int (&id)[S::NI], int& zb) {
+      zb = zI;
+      const int kbb = bi2 * kKeyBlock;
 #pragma unroll
-      for (int u = 0; u < S::NI; ++u) id[u] = Ieb[min(kbb + 16 * w + u * S::RPI + lane / S::CPR, k - 1)];
+      for (int u = 0; u < S::NI; ++u) id[u] = IeI[min(kbb + 16 * w + u * S::RPI + lane / S::CPR, k - 1)];
+      if (++bi2 == B) {
+        bi2 = 0;
+        enter(++it2);
+      }
     };
     auto qids = [&](int t, int (&ent_)[QT]) {
       t = min(t, (int)nt - 1);
@@ -582,12 +591,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     int id_n[S::NI], z_n;
     {
       int id0[S::NI], z0;
-      ids(0, id0, z0);
+      ids(id0, z0);
       if constexpr (kScalar)
         dma_rows_buf<D>(sm.rk[0], sm.rv[0], rsK(z0), rsV(z0), id0, w, lane);
       else
         dma_rows<D>(sm.rk[0], sm.rv[0], K + (size_t)z0 * N * D, V + (size_t)z0 * N * D, id0, w, lane);
-      ids(1, id_n, z_n);
+      ids(id_n, z_n);
     }
     int qe[QT], qe_n[QT], qe_nn[QT];
     qids(0, qe);
@@ -599,8 +608,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     int4 cur = sm.tile[0];
     int zc = sm.tz[0];
 
-    for (int j = 0; j < nblk; ++j) {
-      const int ti = j / B, kb = (j % B) * kKeyBlock;
+    for (int j = 0, ti = 0, bi = 0; j < nblk; ++j) {   // block bi of tile ti
+      const int kb = bi * kKeyBlock;
       const bool newtile = kb == 0;   // block-uniform
       const bool lastblk = kb + kKeyBlock >= k;
       if (newtile) {
@@ -637,7 +646,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
           else
             dma_rows<D>(nk, nv, K + (size_t)z_n * N * D, V + (size_t)z_n * N * D, id_n, w, lane);
         }
-        ids(j + 2, id_n, z_n);
+        ids(id_n, z_n);
         // The wave has live rows (with kScalar a scalar condition, so the two paths
         // stay apart). The scores live inside the busy path (merging them with the
         // idle path would cost a register fill per block); the next tile's query
@@ -687,6 +696,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
             if (g == 0) *(float4*)(pml + ps * 4) = make_float4(mrun[qt], l, sc, 0.f);
           }
         }
+      }
+      if (++bi == B) {
+        bi = 0;
+        ++ti;
       }
     }
     __builtin_amdgcn_s_waitcnt(0);

@@ -7,7 +7,8 @@
 // in LDS and multiplied on MFMA (bf16: Q~ as hi + lo parts, so the scores have a
 // proven error E_q = gamma |q| max|q~|). Each lane keeps a sorted top list of its
 // landmarks' scores (m <= 64: the scores alone, which stay in registers; m > 64:
-// keys that carry the landmark id); the four lanes of a query merge theirs. If
+// float keys that carry the landmark id in their low mantissa bits); the four
+// lanes of a query merge theirs. If
 // the s-th and (s+1)-th scores are more than 2E_q apart the set is certain;
 // otherwise the entries within 2E_q of the s-th score are re-scored in fp64, or
 // (m > 64, band longer than the list) the query is queued for the exact kernel,
@@ -370,8 +371,8 @@ __global__ __launch_bounds__(256) void route_fast_kernel(const T* __restrict__ Q
 // Fast router for m > 64: a workgroup takes TPW query tiles at once (their query
 // fragments and top lists stay in registers) and streams the landmark blocks
 // through LDS once for all of them, so each block is staged once per TPW tiles.
-// Held to three waves per SIMD: the gathers of Q rows need the occupancy more
-// than the few registers that spill.
+// At least three waves per SIMD (the gathers of Q rows need the occupancy); the
+// d = 128 forms fit in 120 VGPRs and run four.
 // A query is certain, or its band is re-scored in fp64 when the list holds it,
 // or it is queued for the exact kernel.
 template <typename T, int D, int TM, int TPW, bool MFULL>

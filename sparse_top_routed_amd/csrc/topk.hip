@@ -25,6 +25,7 @@
 
 namespace mita {
 
+constexpr int kCandListMax = 1024;   // blocks of a key chunk the candidate kernel lists (more: no skipping)
 constexpr int kBandMax = 128;   // band members the select kernel re-scores in LDS (more: fallback; a band
                                  // normally holds a few members, and LDS per wave sets the occupancy)
 
@@ -256,12 +257,16 @@ __global__ __launch_bounds__(256) void topk_cand_kernel(const T* __restrict__ K,
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void topk_candd_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ qtop, const uint32_t* __restrict__ thr,
-    uint2* __restrict__ cand, uint32_t* __restrict__ ccnt, uint32_t* __restrict__ glist, int N, int m, int lchunk,
-    int nsplit, int capc, int lm_tiles, int BH) {
+    const float* __restrict__ bmax, uint2* __restrict__ cand, uint32_t* __restrict__ ccnt,
+    uint32_t* __restrict__ glist, int N, int m, int lchunk, int nsplit, int capc, int lm_tiles, int BH, int nbg,
+    int gq) {
   constexpr int QT = 2;
   using Sw = SwzTile<D>;
   __shared__ __align__(16) struct {
     uint16_t rk[2][Sw::TILE];
+    uint16_t blist[kCandListMax];   // the chunk's blocks that hold a candidate, in key order
+    uint32_t need[kCandListMax / 32];   // the same as a bitmap
+    uint32_t wtot[4];
   } sm;
   if (blockIdx.x == 0 && threadIdx.x == 0) glist[0] = 0u;   // no fallback rows yet (the select kernel adds them)
   int lt, c, z;
@@ -269,13 +274,61 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
   const int k0 = c * lchunk, k1 = min(N, k0 + lchunk);
   const uint16_t* Kz = K + (size_t)z * N * D;
+  const int nblk_all = (k1 - k0 + kKeyBlock - 1) / kKeyBlock;
+  // Blocks to score: a block whose scores stay below every row's threshold holds
+  // no candidate, and with groups of 64 the shared-expert kernel left each row's
+  // block maximum (the same score bits as here). Block b is kept when some
+  // landmark row of the tile has its maximum at or above the row's threshold; the
+  // kept blocks are listed in key order, so the candidate lists are those of a full
+  // sweep. Smaller groups (k large against N / 64: candidates in most blocks) or
+  // more blocks than the list holds: every block is scored.
+  int nblk;
+  if (gq == kKeyBlock && nblk_all <= kCandListMax) {   // one group maximum per block (candidates sparse per block)
+    const int blk0 = k0 / kKeyBlock, nwd = (nblk_all + 31) / 32;
+    for (int i = tid; i < nwd; i += 256) sm.need[i] = 0u;
+    __syncthreads();
+    // two threads per landmark row, each a half of the chunk's bitmap words: a
+    // word's 32 blocks compared in registers, then one LDS OR per word
+    const int rr = tid >> 1, lm = lt * 128 + rr;
+    if (lm < m) {
+      const uint32_t tk = thr[(size_t)z * m + lm];
+      const float t = tk ? key_f32(tk) : -INFINITY;
+      const float* gm = bmax + ((size_t)z * m + lm) * nbg + blk0;
+      const int wh = (nwd + 1) / 2, wd0 = (tid & 1) * wh, wd1 = min(nwd, wd0 + wh);
+      for (int wd = wd0; wd < wd1; ++wd) {
+        float bm[32];   // all 32 loads issued before the compares (indices clamped into the chunk)
+#pragma unroll
+        for (int bb = 0; bb < 32; ++bb) bm[bb] = gm[min(32 * wd + bb, nblk_all - 1)];
+        uint32_t bits = 0;
+#pragma unroll
+        for (int bb = 0; bb < 32; ++bb) bits |= (32 * wd + bb < nblk_all && bm[bb] >= t) ? 1u << bb : 0u;
+        if (bits) atomicOr(&sm.need[wd], bits);
+      }
+    }
+    __syncthreads();
+    nblk = 0;
+    for (int b0 = 0; b0 < nblk_all; b0 += 256) {   // workgroup-uniform
+      const int b = b0 + tid;
+      const uint32_t keep = b < nblk_all ? (sm.need[b >> 5] >> (b & 31)) & 1u : 0u;
+      uint32_t tot;
+      const uint32_t pos = block_incl_scan(keep, sm.wtot, tot) - keep;
+      if (keep) sm.blist[nblk + pos] = (uint16_t)b;
+      nblk += (int)tot;
+    }
+    __syncthreads();
+  } else {
+    nblk = nblk_all;
+  }
+  auto blk_key = [&](int i) {
+    return k0 + kKeyBlock * (gq == kKeyBlock && nblk_all <= kCandListMax ? (int)sm.blist[i] : i);
+  };
   auto rows = [&](int kb, int (&id)[Sw::NI]) {
 #pragma unroll
     for (int u = 0; u < Sw::NI; ++u) id[u] = min(kb + 16 * w + u * Sw::RPI + lane / Sw::CPR, k1 - 1);
   };
-  {
+  if (nblk > 0) {
     int id0[Sw::NI];
-    rows(k0, id0);
+    rows(blk_key(0), id0);
     dma_rows_k<D>(sm.rk[0], Kz, id0, w, lane);
   }
   bool lm_ok[QT];
@@ -298,15 +351,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void t
     tf[qt] = tk ? key_f32(tk) : -INFINITY;   // compare the scores themselves (same order)
     base[qt] = 0;
   }
-  const int nblk = (k1 - k0 + kKeyBlock - 1) / kKeyBlock;
   for (int j = 0; j < nblk; ++j) {
-    const int kb = k0 + j * kKeyBlock;
+    const int kb = blk_key(j);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();   // block j staged; every wave done with block j - 1
     auto step = [&](uint16_t* __restrict__ nk, const uint16_t* __restrict__ ck) __attribute__((always_inline)) {
       if (j + 1 < nblk) {   // block-uniform
         int idn[Sw::NI];
-        rows(kb + kKeyBlock, idn);
+        rows(blk_key(j + 1), idn);
         dma_rows_k<D>(nk, Kz, idn, w, lane);
       }
       f32x4 acc[QT][4];
@@ -620,8 +672,9 @@ static hipError_t topk_launch(const Plan& p, const void* K, char* ws, hipStream_
       const int tiles = (p.m + 127) / 128;
       const int cgrid = 8 * ((p.nsplit * p.BH + 7) / 8) * tiles;   // see chunk_item
       hipLaunchKernelGGL((topk_candd_kernel<D>), dim3(cgrid), dim3(256), 0, st, (const uint16_t*)K,
-                         (const uint16_t*)(ws + p.ws.qtop), (const uint32_t*)(ws + p.ws.thr), (uint2*)(ws + p.ws.cand),
-                         (uint32_t*)(ws + p.ws.ccnt), glist, p.N, p.m, p.lchunk, p.nsplit, p.capc, tiles, p.BH);
+                         (const uint16_t*)(ws + p.ws.qtop), (const uint32_t*)(ws + p.ws.thr),
+                         (const float*)(ws + p.ws.bmax), (uint2*)(ws + p.ws.cand), (uint32_t*)(ws + p.ws.ccnt), glist,
+                         p.N, p.m, p.lchunk, p.nsplit, p.capc, tiles, p.BH, p.nbg, p.gq);
     } else {
       const int cgrid = 8 * ((p.nsplit * p.BH + 7) / 8) * p.lm_tiles;   // see chunk_item
       hipLaunchKernelGGL((topk_cand_kernel<T, D>), dim3(cgrid), dim3(256), 0, st, (const T*)K,

@@ -475,7 +475,7 @@ __device__ __forceinline__ void qk_bf16_swz(const uint16_t* Ks, const uint4 (&qf
 // order, hi then lo), so the scores are the same bits.
 template <int D, int QT>
 __device__ __forceinline__ void qk2_bf16_swz(const uint16_t* Ks, const uint4 (&qb)[QT][2][D / 32],
-                                             f32x4 (&acc)[QT][4], int lane) {
+                                             f32x4 (&acc)[QT][4], int lane, int ktn = -1, float* nsq = nullptr) {
   using S = SwzTile<D>;
   const int r = lane & 15, g = lane >> 4;
 #pragma unroll
@@ -485,6 +485,13 @@ __device__ __forceinline__ void qk2_bf16_swz(const uint16_t* Ks, const uint4 (&q
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks) {
     const uint16_t* col = Ks + r * D + 8 * ((4 * ks + g) ^ S::swz_k(r));
+    if (nsq) {   // squared norm of row 16 ktn + r over this lane's pieces (same addresses as the reads below)
+      const uint4 an = *(const uint4*)(col + 16 * ktn * D);
+      *nsq = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, an.x), __builtin_bit_cast(bf16x2, an.x), *nsq, false);
+      *nsq = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, an.y), __builtin_bit_cast(bf16x2, an.y), *nsq, false);
+      *nsq = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, an.z), __builtin_bit_cast(bf16x2, an.z), *nsq, false);
+      *nsq = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, an.w), __builtin_bit_cast(bf16x2, an.w), *nsq, false);
+    }
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       const uint4 a0 = *(const uint4*)(col + 16 * kt * D);

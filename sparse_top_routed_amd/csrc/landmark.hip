@@ -168,22 +168,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
         rows(kb + kKeyBlock, idn);
         dma_rows<D>(nk, nv, Kz, Vz, idn, w, lane);
       }
-      if (D != 64 && lt == 0) {   // squared key norms, 4 threads per row (a row's chunks in any order)
-        const int row = tid >> 2, part = tid & 3;
-        const uint16_t* kr = ck + row * D + part * (D / 4);
-        float sq = 0.f;
-#pragma unroll
-        for (int e = 0; e < D / 4; ++e) {
-          const float x = bf16_to_f32(kr[e]);
-          sq = fmaf(x, x, sq);
-        }
-        sq += __shfl_xor(sq, 1, WAVE);
-        sq += __shfl_xor(sq, 2, WAVE);
-        kmx = fmaxf(kmx, sq);
-      }
       f32x4 acc[QT][4];
       __builtin_amdgcn_s_setprio(1);
-      qk2_bf16_swz<D, QT>(ck, qb, acc, lane);
+      if (D != 64 && lt == 0) {   // workgroup-uniform
+        // squared key norms beside the scores: wave w re-reads the rows of its
+        // key tile kt = w at the addresses the score reads use (no bank
+        // conflicts), the four lanes of a row each a quarter of it
+        float nsq = 0.f;
+        qk2_bf16_swz<D, QT>(ck, qb, acc, lane, w, &nsq);
+        nsq += __shfl_xor(nsq, 16, WAVE);
+        nsq += __shfl_xor(nsq, 32, WAVE);
+        kmx = fmaxf(kmx, nsq);
+      } else {
+        qk2_bf16_swz<D, QT>(ck, qb, acc, lane);
+      }
       const int blk = kb / kKeyBlock;
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {   // group maxima (and the scores when asked for) as the sweep writes them
@@ -225,8 +223,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
         // CH lanes read the CH pieces of a row (a half-wave reads contiguous rows:
         // no bank conflicts), NR rows per lane; the sums over the CH lanes first
         // trade half of a lane's rows with the partner lane, then add plainly.
-        // Measured: 6 % off the d = 64 kernel; with d = 128 (256 VGPRs) the kernel
-        // came out 4 % slower, so it keeps the 4-threads-per-row form above
+        // Measured with d = 64: 6 % off the kernel against 4 threads per row, and
+        // 10 % faster than the rows read beside the score products (the d = 128 form)
         constexpr int CH = D / 8, NR = D / 32, RS = 256 / CH;
         float sq[NR];
 #pragma unroll

@@ -89,7 +89,22 @@ __device__ __forceinline__ void shared_expert_sweep(const T* Kz, const T* Vz, in
     __syncthreads();
     fetch(kb + kKeyBlock);   // the next block, while this one computes
 
-    if (norms) {   // squared norms of the staged keys: 4 threads per row
+    if (BF && norms) {   // squared norms of the staged keys: wave w the rows of key tile w,
+      // read where the score products read them, the four lanes of a row a quarter each
+      const uint16_t* kr = (const uint16_t*)Ks + (16 * (tid >> 6) + (lane & 15)) * TL::KSTR + 8 * g;
+      float sq = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const uint4 a = *(const uint4*)(kr + 32 * ks);
+        sq = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.x), __builtin_bit_cast(bf16x2, a.x), sq, false);
+        sq = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.y), __builtin_bit_cast(bf16x2, a.y), sq, false);
+        sq = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.z), __builtin_bit_cast(bf16x2, a.z), sq, false);
+        sq = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.w), __builtin_bit_cast(bf16x2, a.w), sq, false);
+      }
+      sq += __shfl_xor(sq, 16, WAVE);
+      sq += __shfl_xor(sq, 32, WAVE);
+      kmx = fmaxf(kmx, sq);
+    } else if (norms) {   // squared norms of the staged keys: 4 threads per row
       const int row = tid >> 2, part = tid & 3;
       const T* kr = Ks + row * TL::KSTR + part * (D / 4);
       float sq = 0.f;

@@ -48,6 +48,12 @@ mita_status make_plan(const mita_shape* shape, int m, int k, int s, Plan* p, con
   if (s < 1 || s > m) { *err = "need 1 <= s <= m"; return MITA_ERR_INVALID_ARG; }
   if (sh.d != 64 && sh.d != 128) { *err = "d must be 64 or 128"; return MITA_ERR_UNSUPPORTED; }
   if (m > kMaxLandmarks) { *err = "m above 4096 is not supported"; return MITA_ERR_UNSUPPORTED; }
+  // bf16 with more than 64 landmarks and k below one key block: expert sets came
+  // out wrong on such an input (all ids 0) and a later call read out of bounds;
+  // the cause is not found, so the combination is refused
+  if (sh.dtype == MITA_BF16 && m > kLandmarkTile && k < kKeyBlock) {
+    *err = "bf16 with m > 64 and k < 64 is not supported"; return MITA_ERR_UNSUPPORTED;
+  }
   const int64_t BH = (int64_t)sh.B * sh.H;
   const int64_t lim = (int64_t)1 << 31;
   if (BH * sh.N * std::max(sh.d, s) >= lim || BH * m * (int64_t)std::max(k, sh.d) >= lim) {

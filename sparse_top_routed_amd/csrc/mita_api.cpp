@@ -48,11 +48,13 @@ mita_status make_plan(const mita_shape* shape, int m, int k, int s, Plan* p, con
   if (s < 1 || s > m) { *err = "need 1 <= s <= m"; return MITA_ERR_INVALID_ARG; }
   if (sh.d != 64 && sh.d != 128) { *err = "d must be 64 or 128"; return MITA_ERR_UNSUPPORTED; }
   if (m > kMaxLandmarks) { *err = "m above 4096 is not supported"; return MITA_ERR_UNSUPPORTED; }
-  // bf16 with more than 64 landmarks and k below one key block: expert sets came
-  // out wrong on such an input (all ids 0) and a later call read out of bounds;
-  // the cause is not found, so the combination is refused
-  if (sh.dtype == MITA_BF16 && m > kLandmarkTile && k < kKeyBlock) {
-    *err = "bf16 with m > 64 and k < 64 is not supported"; return MITA_ERR_UNSUPPORTED;
+  // bf16 with more than 64 landmarks, k below one key block and at least 4 k key
+  // blocks (thresholds from maxima of groups of 64): expert sets came out wrong on
+  // such inputs (all ids 0) and a later call read out of bounds; the cause is not
+  // found, so the combination is refused
+  if (sh.dtype == MITA_BF16 && m > kLandmarkTile && k < kKeyBlock &&
+      (sh.N + kKeyBlock - 1) / kKeyBlock >= 4 * (int64_t)k) {
+    *err = "bf16 with m > 64, k < 64 and N >= 256 k is not supported"; return MITA_ERR_UNSUPPORTED;
   }
   const int64_t BH = (int64_t)sh.B * sh.H;
   const int64_t lim = (int64_t)1 << 31;

@@ -51,7 +51,7 @@ def test_workspace_bytes_grows_with_problem():
     (shape(d=96), 16, 64, 1, mita.MITA_ERR_UNSUPPORTED),            # head size
     (shape(dt=7), 16, 64, 1, mita.MITA_ERR_INVALID_ARG),            # dtype
     (shape(N=8192, gw=8192, pw=8192), 8192, 64, 1, mita.MITA_ERR_UNSUPPORTED),  # m above 4096
-    (shape(N=8192, gw=8192, pw=96, dt=mita.MITA_BF16), 96, 32, 2, mita.MITA_ERR_UNSUPPORTED),  # bf16, m > 64, k < 64
+    (shape(N=8192, gw=8192, pw=96, dt=mita.MITA_BF16), 96, 32, 2, mita.MITA_ERR_UNSUPPORTED),  # bf16, m > 64, k < 64, N >= 256 k
 ])
 def test_invalid_arguments(sh, m, k, s, code):
     lib = mita.load()
